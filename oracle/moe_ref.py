@@ -1,0 +1,402 @@
+"""CPU oracle for the weight-only-quantized fused MoE layer.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The product path (the HIP library
+and its Python binding) never calls it, and this module imports nothing from
+the product package.
+
+Everything here is a plain, slow, obviously correct restatement of what the
+pages define:
+
+* experts_int8 page (vllm ... quantization.experts_int8):
+  ``quantize_in_place_and_get_scales`` (per-row symmetric int8),
+  ``ExpertsInt8MoEMethod.create_weights`` (w13 [E, 2I, H] int8 with the gate
+  rows first and the up rows second, w2 [E, H, I] int8, fp32 scales [E, 2I]
+  and [E, H]), ``quantizing_weight_loader`` (gate -> w13 rows 0..I-1,
+  up -> rows I..2I-1, per output channel scales) and ``apply`` (softmax top-k
+  routing through ``select_experts``, then ``fused_experts`` with
+  activation "silu", ``apply_router_weight_on_input=False``).
+* moe_wna16 page (vllm ... quantization.moe_wna16): ``MoeWNA16Method.create_weights``
+  (packed 4-bit weights along K, group scales [E, N, K/g], packed zeros along N)
+  and the weight loader's zero convention (the stored zero is the true zero).
+
+Floating point: fp64, except where a float decides an integer code (the
+quantizers); there the arithmetic is fp32 with IEEE division and round half to
+even, as the page's in-place ops on an fp32 tensor compute it.
+
+Readings where the pages are silent (the router body, the align step, the
+W4 quantizer) are stated at each function.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# 16-bit activation decoding
+# ---------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of an fp32)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def fp16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE half bit patterns (uint16) -> float64, exactly."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def act_bits_to_f64(bits: np.ndarray, act: str) -> np.ndarray:
+    if act == "bf16":
+        return bf16_bits_to_f64(bits)
+    if act == "fp16":
+        return fp16_bits_to_f64(bits)
+    raise ValueError(act)
+
+
+# ---------------------------------------------------------------------------
+# a1: per-output-channel symmetric int8 quantizer
+# ---------------------------------------------------------------------------
+
+
+def quantize_int8_rows(w: np.ndarray):
+    """Per-row symmetric int8 quantization of an fp32 matrix (rows = output channels).
+
+    experts_int8 page, ``quantize_in_place_and_get_scales``: the scale of a row is
+    its largest magnitude divided by the int8 maximum (127); the row is divided
+    by that scale, rounded (half to even) and clamped to [-127, 127].  All of
+    it runs in the tensor's own dtype, fp32 here.
+
+    Reading for an all-zero row (the page would divide 0 by 0): scale 0, codes 0.
+
+    Returns (q int8 [..., N, K], s float32 [..., N]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    vmax = np.float32(127.0)
+    m = np.max(np.abs(w), axis=-1, keepdims=True)            # fp32, exact
+    s = (m / vmax).astype(np.float32)                         # fp32 IEEE divide
+    zero = s == 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = (w / np.where(zero, np.float32(1.0), s)).astype(np.float32)   # fp32 IEEE divide
+    r = np.rint(r)                                            # round half to even
+    r = np.clip(r, -vmax, vmax)
+    r = np.where(zero, np.float32(0.0), r)
+    return r.astype(np.int8), s[..., 0]
+
+
+def dequant_int8_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """W = q * s per output channel, exactly in fp64 (an 8-bit times a 24-bit significand fits in 53 bits)."""
+    return np.asarray(q, np.float64) * np.asarray(s, np.float64)[..., None]
+
+
+# ---------------------------------------------------------------------------
+# a2: softmax top-k router
+# ---------------------------------------------------------------------------
+
+
+def route_softmax_topk(logits: np.ndarray, k: int, renormalize: bool = True):
+    """Softmax scoring, top-k selection and optional renormalisation.
+
+    experts_int8 page, ``ExpertsInt8MoEMethod.apply``: ``select_experts`` is called
+    with ``scoring_func="softmax"``, ``top_k`` and ``renormalize``; its body is not
+    on the pages.  Reading: the softmax over all E experts is taken in fp64; the k
+    experts with the largest fp32 logits are chosen (the same set as the largest
+    probabilities, decided by exact comparisons of the inputs), listed in
+    descending order, equal logits broken toward the lower expert id.  With
+    ``renormalize`` the k chosen probabilities are divided by their sum.
+
+    Returns (weights float64 [T, k], ids int32 [T, k]).
+    """
+    l32 = np.asarray(logits, dtype=np.float32)
+    T, E = l32.shape
+    if not 1 <= k <= E:
+        raise ValueError("k must be in [1, E]")
+    # stable sort on the negated fp32 logits: descending, ties keep the lower id first
+    ids = np.argsort(-l32, axis=1, kind="stable")[:, :k].astype(np.int32)
+    l = l32.astype(np.float64)
+    m = np.max(l, axis=1, keepdims=True)
+    ex = np.exp(l - m)
+    p = ex / np.sum(ex, axis=1, keepdims=True)
+    w = np.take_along_axis(p, ids, axis=1)
+    if renormalize:
+        w = w / np.sum(w, axis=1, keepdims=True)
+    return w, ids
+
+
+# ---------------------------------------------------------------------------
+# a3: token -> expert align (histogram, prefix scan, padded-block permutation)
+# ---------------------------------------------------------------------------
+
+
+def align_capacity(T: int, k: int, E: int, block_m: int) -> int:
+    """Rows reserved for the padded permutation: at most min(E, T*k) experts are
+    non-empty and each pads to a multiple of block_m, so the number of blocks is
+    at most floor((T*k + min(E, T*k)*(block_m-1)) / block_m)."""
+    tk = T * k
+    if tk == 0:
+        return 0
+    return ((tk + min(E, tk) * (block_m - 1)) // block_m) * block_m
+
+
+def align_block(topk_ids: np.ndarray, E: int, block_m: int):
+    """Group the flat assignments f = t*k + j by expert into padded blocks.
+
+    Not on the pages (the fused kernel that consumes it is only called, on the
+    experts_int8 page, ``apply``).  Reading: experts in ascending id; inside an
+    expert the flat indices ascend (a stable order); each expert's list is padded
+    with the sentinel T*k up to a multiple of block_m; experts without tokens get
+    no block; ids outside [0, E) are dropped.  Every row of the capacity that is
+    not part of a block holds the sentinel, every block past the last holds -1.
+
+    Returns (sorted_ids int32 [cap], block_expert int32 [cap/block_m], num_padded int).
+    """
+    ids = np.asarray(topk_ids).reshape(-1).astype(np.int64)
+    tk = ids.size
+    cap = align_capacity(1, tk, E, block_m)
+    sorted_ids = np.full(cap, tk, dtype=np.int32)
+    block_expert = np.full(cap // block_m if block_m else 0, -1, dtype=np.int32)
+    valid = (ids >= 0) & (ids < E)
+    counts = np.bincount(ids[valid], minlength=E)
+    padded = -(-counts // block_m) * block_m
+    off = np.concatenate([[0], np.cumsum(padded)])
+    for e in range(E):
+        rows = np.nonzero(ids == e)[0]                       # ascending flat index
+        sorted_ids[off[e]:off[e] + rows.size] = rows
+        block_expert[off[e] // block_m:off[e + 1] // block_m] = e
+    return sorted_ids, block_expert, int(off[E])
+
+
+def align_block_bruteforce(topk_ids, E: int, block_m: int):
+    """Pure-Python loops restating the same definition (small inputs only)."""
+    ids = [int(v) for v in np.asarray(topk_ids).reshape(-1)]
+    tk = len(ids)
+    cap = align_capacity(1, tk, E, block_m) if tk else 0
+    out, be = [], []
+    for e in range(E):
+        mine = [f for f in range(tk) if ids[f] == e]
+        if not mine:
+            continue
+        nb = (len(mine) + block_m - 1) // block_m
+        out += mine + [tk] * (nb * block_m - len(mine))
+        be += [e] * nb
+    num_padded = len(out)
+    out += [tk] * (cap - len(out))
+    be += [-1] * (cap // block_m - len(be)) if block_m else []
+    return np.array(out, np.int32), np.array(be, np.int32), num_padded
+
+
+# ---------------------------------------------------------------------------
+# a4 - a6: layer forward
+# ---------------------------------------------------------------------------
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU(g) = g / (1 + exp(-g)) (activation "silu" of ``fused_experts``)."""
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def moe_forward_dense(x: np.ndarray, w13_of, w2_of, topk_w: np.ndarray, topk_ids: np.ndarray,
+                      I: int) -> np.ndarray:
+    """Routed MoE layer with dense fp64 expert weights.
+
+    experts_int8 page, ``ExpertsInt8MoEMethod.apply`` and ``create_weights``: for
+    every assignment (t, j) of token t to expert e = topk_ids[t, j]:
+    h = W13[e] x_t (rows 0..I-1 are the gate projection, rows I..2I-1 the up
+    projection, ``quantizing_weight_loader``), a = silu(h_gate) * h_up,
+    y = W2[e] a, and out_t = sum_j topk_w[t, j] * y (the routing weight multiplies
+    the expert output: ``apply_router_weight_on_input=False``).  Ids outside
+    [0, E) contribute nothing.
+
+    x: float64 [T, H]; w13_of(e) -> float64 [2I, H]; w2_of(e) -> float64 [H, I].
+    Returns float64 [T, H].
+    """
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    ids = np.asarray(topk_ids).reshape(T, -1)
+    w = np.asarray(topk_w, np.float64).reshape(T, -1)
+    out = np.zeros((T, H), np.float64)
+    for e in np.unique(ids):
+        e = int(e)
+        t_idx, j_idx = np.nonzero(ids == e)
+        if t_idx.size == 0:
+            continue
+        W13 = w13_of(e)
+        W2 = w2_of(e)
+        if W13 is None or W2 is None:      # expert not present (id out of range)
+            continue
+        hmat = x[t_idx] @ W13.T            # [n, 2I]
+        a = silu(hmat[:, :I]) * hmat[:, I:]
+        y = a @ W2.T                       # [n, H]
+        np.add.at(out, t_idx, w[t_idx, j_idx][:, None] * y)
+    return out
+
+
+def moe_forward_w8(x: np.ndarray, q13: np.ndarray, s13: np.ndarray, q2: np.ndarray, s2: np.ndarray,
+                   topk_w: np.ndarray, topk_ids: np.ndarray) -> np.ndarray:
+    """The W8A16 layer: dequantize each used expert exactly in fp64 (W = q*s), then ``moe_forward_dense``."""
+    E = q13.shape[0]
+    I = q13.shape[1] // 2
+
+    def w13_of(e):
+        return dequant_int8_rows(q13[e], s13[e]) if 0 <= e < E else None
+
+    def w2_of(e):
+        return dequant_int8_rows(q2[e], s2[e]) if 0 <= e < E else None
+
+    return moe_forward_dense(x, w13_of, w2_of, topk_w, topk_ids, I)
+
+
+def moe_expert_intermediate(x: np.ndarray, W13: np.ndarray, I: int) -> np.ndarray:
+    """a = silu(x W13_gate^T) * (x W13_up^T) for rows x [n, H] (fp64)."""
+    hmat = np.asarray(x, np.float64) @ W13.T
+    return silu(hmat[:, :I]) * hmat[:, I:]
+
+
+# ---------------------------------------------------------------------------
+# a7: group-wise asymmetric 4-bit weights with zero points
+# ---------------------------------------------------------------------------
+
+
+def f32_to_f16_rne(a) -> np.ndarray:
+    return np.asarray(a, np.float32).astype(np.float16)
+
+
+def quantize_w4_groups(w: np.ndarray, group_size: int):
+    """Asymmetric uint4 quantization per (output row, group of K).
+
+    The moe_wna16 page loads GPTQ/AWQ checkpoints and prints no quantizer; the
+    reading used here: for each row n and group g of ``group_size`` consecutive K,
+    lo = min(min w, 0), hi = max(max w, 0); the scale is (hi - lo) / 15 in fp32,
+    rounded to fp16; with that fp16 scale s (as fp32): zero z = clamp(rne(-lo / s), 0, 15)
+    and code q = clamp(rne(w / s) + z, 0, 15).  If the fp16 scale is 0 (a flat
+    group), s = 1.  The dequantized weight is (q - z) * s (the stored zero is the
+    true zero: moe_wna16 page, weight loader, GPTQ zeros get +1 to match AWQ).
+
+    w: float32 [..., N, K].  Returns (q uint8 [..., N, K], s float16 [..., N, K/g],
+    z uint8 [..., N, K/g]).
+    """
+    w = np.asarray(w, np.float32)
+    *lead, N, K = w.shape
+    if K % group_size:
+        raise ValueError("K must be a multiple of group_size")
+    G = K // group_size
+    wg = w.reshape(*lead, N, G, group_size)
+    lo = np.minimum(wg.min(axis=-1), np.float32(0.0))
+    hi = np.maximum(wg.max(axis=-1), np.float32(0.0))
+    s32 = ((hi - lo) / np.float32(15.0)).astype(np.float32)
+    s16 = f32_to_f16_rne(s32)
+    s = s16.astype(np.float32)
+    flat = s == 0
+    s = np.where(flat, np.float32(1.0), s)
+    s16 = np.where(flat, np.float16(1.0), s16)
+    z = np.clip(np.rint((-lo / s).astype(np.float32)), 0, 15)
+    qf = np.rint((wg / s[..., None]).astype(np.float32)) + z[..., None]
+    q = np.clip(qf, 0, 15).astype(np.uint8).reshape(*lead, N, K)
+    return q, s16.astype(np.float16), z.astype(np.uint8)
+
+
+def pack_w4_along_k(q: np.ndarray) -> np.ndarray:
+    """uint4 codes [..., N, K] -> int32 [..., N, K/8] with code k at bits 4*(k mod 8).
+
+    Byte-identical to the moe_wna16 page's canonical uint8 layout (two codes per
+    byte along K, the even one in the low nibble) read as little-endian int32.
+    """
+    q = np.asarray(q, np.uint32)
+    *lead, N, K = q.shape
+    qq = q.reshape(*lead, N, K // 8, 8)
+    word = np.zeros((*lead, N, K // 8), np.uint32)
+    for i in range(8):
+        word |= qq[..., i] << np.uint32(4 * i)
+    return word.view(np.int32)
+
+
+def unpack_w4_along_k(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed).view(np.uint32)
+    *lead, N, KW = p.shape
+    out = np.zeros((*lead, N, KW, 8), np.uint8)
+    for i in range(8):
+        out[..., i] = (p >> np.uint32(4 * i)) & 0xF
+    return out.reshape(*lead, N, KW * 8)
+
+
+def pack_w4_along_n(z: np.ndarray) -> np.ndarray:
+    """uint4 zeros [..., N, G] -> int32 [..., N/8, G] with row n at bits 4*(n mod 8)
+    (moe_wna16 page, ``create_weights``: zeros are packed along the output dimension)."""
+    z = np.asarray(z, np.uint32)
+    *lead, N, G = z.shape
+    zz = z.reshape(*lead, N // 8, 8, G)
+    word = np.zeros((*lead, N // 8, G), np.uint32)
+    for i in range(8):
+        word |= zz[..., i, :] << np.uint32(4 * i)
+    return word.view(np.int32)
+
+
+def unpack_w4_along_n(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed).view(np.uint32)
+    *lead, NW, G = p.shape
+    out = np.zeros((*lead, NW, 8, G), np.uint8)
+    for i in range(8):
+        out[..., i, :] = (p >> np.uint32(4 * i)) & 0xF
+    return out.reshape(*lead, NW * 8, G)
+
+
+def dequant_w4(qweight: np.ndarray, scales: np.ndarray, qzeros: np.ndarray, group_size: int) -> np.ndarray:
+    """W[n, k] = (q[n, k] - z[n, k // g]) * s[n, k // g], exactly in fp64 (one expert)."""
+    q = unpack_w4_along_k(qweight).astype(np.float64)
+    z = unpack_w4_along_n(qzeros).astype(np.float64)
+    s = np.asarray(scales, np.float16).astype(np.float64)
+    zk = np.repeat(z, group_size, axis=-1)
+    sk = np.repeat(s, group_size, axis=-1)
+    return (q - zk) * sk
+
+
+def moe_forward_w4(x: np.ndarray, qw13, s13, z13, qw2, s2, z2, group_size: int,
+                   topk_w: np.ndarray, topk_ids: np.ndarray) -> np.ndarray:
+    """The W4A16 layer: per used expert, dense fp64 dequantization, then ``moe_forward_dense``."""
+    E = qw13.shape[0]
+    I = qw13.shape[1] // 2
+
+    def w13_of(e):
+        return dequant_w4(qw13[e], s13[e], z13[e], group_size) if 0 <= e < E else None
+
+    def w2_of(e):
+        return dequant_w4(qw2[e], s2[e], z2[e], group_size) if 0 <= e < E else None
+
+    return moe_forward_dense(x, w13_of, w2_of, topk_w, topk_ids, I)
+
+
+# ---------------------------------------------------------------------------
+# Tolerance of the layer output (floating-point result)
+# ---------------------------------------------------------------------------
+
+
+def layer_within_tolerance(got: np.ndarray, ref: np.ndarray, rel: float = 2e-2, abs_: float = 1e-3):
+    """max|got-ref| <= rel*max|ref| and |got-ref| <= rel*|ref| + abs_ per element.
+
+    Returns (ok, detail dict)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    lim = rel * np.abs(ref) + abs_
+    bad = d > lim
+    mx = float(d.max()) if d.size else 0.0
+    mref = float(np.abs(ref).max()) if ref.size else 0.0
+    ok = (not bad.any()) and (mx <= rel * mref or mx == 0.0)
+    return ok, {"max_abs_err": mx, "max_abs_ref": mref, "n_bad": int(bad.sum()),
+                "worst_ratio": float((d / lim).max()) if d.size else 0.0}
+
+
+def topk_subsets_bruteforce(logits_row: np.ndarray, k: int):
+    """All k-subsets whose every member's logit is >= every non-member's logit (E small)."""
+    l = np.asarray(logits_row, np.float32)
+    E = l.size
+    good = []
+    for sub in itertools.combinations(range(E), k):
+        rest = [e for e in range(E) if e not in sub]
+        if all(l[a] >= l[b] for a in sub for b in rest):
+            good.append(sub)
+    return good
