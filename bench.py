@@ -1,0 +1,294 @@
+"""Benchmark of the weight-only-quantized MoE layer on one MI355X.
+
+One step = one layer call on one batch: softmax top-k routing, align,
+GEMM1 + SiLU-and-mul, GEMM2 and the weighted combine (moe_route_topk followed
+by moe_w8a16_forward / moe_w4a16_forward), inputs resident in HBM.  Weight
+quantization runs once at set-up and is not part of a step.
+
+Default workload: the Mixtral-shaped decode batch (E=8, top-2, H=4096,
+I=14336, int8 per-channel weights, bf16 activations) at T=64 tokens.
+
+Prints one JSON line with the throughput (tokens/s), the roofline of the
+dominant kernel (from HIP events on the launch stream) and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_decode",
+                    choices=["tiny", "mixtral_decode", "mixtral_prefill", "fine_grained", "w4a16"])
+    ap.add_argument("--tokens", type=int, default=None, help="T (default: the workload's headline size)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--flush-mb", type=int, default=None,
+                    help="write this many MB between timed steps (outside the events) so the "
+                         "256 MB Infinity Cache does not serve the weights; default: 512 when the "
+                         "active weights are below 1 GB, else 0")
+    return ap.parse_args()
+
+
+HEADLINE_T = {"tiny": 16, "mixtral_decode": 64, "mixtral_prefill": 4096, "fine_grained": 512, "w4a16": 256}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the layer is data-parallel over tokens with no exchange; see the design notes).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import weight_quantized_mixture_amd as pkg
+    from weight_quantized_mixture_amd import synthetic
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = synthetic.WORKLOADS[args.workload]
+    T = args.tokens or HEADLINE_T[args.workload]
+    E, k, H, I = wl.E, wl.k, wl.H, wl.I
+    w4 = wl.weights == "w4"
+
+    # ---- set-up: seeded inputs, weights quantized on the GPU ------------------
+    t0 = time.time()
+    if w4:
+        layer = pkg.W4A16MoE(E, H, I, wl.group_size, device=dev)
+    else:
+        layer = pkg.W8A16MoE(E, H, I, device=dev)
+    for e in range(E):
+        m13 = torch.from_numpy(synthetic.expert_master(wl, "w13", e, args.seed)).to(dev)
+        m2 = torch.from_numpy(synthetic.expert_master(wl, "w2", e, args.seed)).to(dev)
+        layer.load_expert(e, m13, m2)
+        del m13, m2
+    torch.cuda.synchronize()
+    log(f"[bench] weights ready ({time.time() - t0:.1f}s) workload={wl.name} T={T}")
+    xb = synthetic.activations(wl, T, args.seed)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16 if wl.act == "bf16" else torch.float16).to(dev)
+    logits_np = synthetic.router_logits(wl, T, args.seed)
+    logits = torch.from_numpy(logits_np).to(dev)
+    out = torch.empty_like(x)
+    tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    ti = torch.empty(T, k, dtype=torch.int32, device=dev)
+    block_m = pkg.moe_w8a16_block_m(T, H, I, E, k)
+    splits = pkg.moe_w8a16_splits(T, H, I, E, k, block_m)
+    ws_bytes = (pkg.moe_w4a16_workspace_bytes if w4 else pkg.moe_w8a16_workspace_bytes)(T, H, I, E, k, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pkg.moe_route_topk(logits, k, wl.renormalize, tw, ti, stream)
+        if w4:
+            pkg.moe_w4a16_forward(x, layer.w13_qweight, layer.w13_scales, layer.w13_qzeros, layer.w2_qweight,
+                                  layer.w2_scales, layer.w2_qzeros, wl.group_size, tw, ti, out, ws, 0, stream)
+        else:
+            pkg.moe_w8a16_forward(x, layer.w13_weight, layer.w13_scale, layer.w2_weight, layer.w2_scale,
+                                  tw, ti, out, ws, 0, stream)
+
+    step()
+    torch.cuda.synchronize()
+    ids_np = ti.cpu().numpy()
+    active = np.unique(ids_np[(ids_np >= 0) & (ids_np < E)])
+    n_active = int(active.size)
+
+    # algorithmic work (what the method must move / compute; padding, the a/y
+    # round trips and the hi+lo second MFMA are not counted)
+    if w4:
+        g = wl.group_size
+        per_expert_w13 = (2 * I * H) // 2 + (2 * I * (H // g)) * 2 + (2 * I * (H // g)) // 2
+        per_expert_w2 = (H * I) // 2 + (H * (I // g)) * 2 + (H * (I // g)) // 2
+    else:
+        per_expert_w13 = 2 * I * H + 2 * I * 4
+        per_expert_w2 = H * I + H * 4
+    act_bytes = 2
+    bytes_layer = (n_active * (per_expert_w13 + per_expert_w2) + T * H * act_bytes * 2 + T * E * 4 + T * k * 8)
+    bytes_gemm1 = n_active * per_expert_w13 + T * H * act_bytes
+    flops_layer = 6 * T * k * H * I
+    flops_gemm1 = 4 * T * k * H * I
+
+    flush_mb = args.flush_mb
+    if flush_mb is None:
+        flush_mb = 512 if n_active * (per_expert_w13 + per_expert_w2) < (1 << 30) else 0
+    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev) if flush_mb else None
+
+    # ---- warm-up -----------------------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed steps ---------------------------------------------------------------
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xff)
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = float(np.mean(step_ms))
+    ms_median = float(np.median(step_ms))
+    value = T / (ms_per_step / 1e3)
+
+    # ---- per-kernel durations (same kernels, one stage call at a time) ----------------
+    stage_ms = {}
+    if not w4:
+        cap = pkg.moe_align_capacity(T, k, E, block_m)
+        s_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+        b_exp = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
+        npad = torch.empty(1, dtype=torch.int32, device=dev)
+        a_buf = torch.empty(cap, I, dtype=torch.float32, device=dev)
+        y_buf = torch.empty(splits, T * k, H, dtype=torch.float32, device=dev)
+        names = ["route", "align", "gemm1", "gemm2", "combine"]
+        acc = {n: [] for n in names}
+        reps = max(5, min(args.steps, 20))
+        for i in range(reps + 2):
+            if flush is not None:
+                flush.fill_(i & 0xff)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            ev[0].record(stream)
+            pkg.moe_route_topk(logits, k, wl.renormalize, tw, ti, stream)
+            ev[1].record(stream)
+            pkg.moe_align_block(ti, E, block_m, s_ids, b_exp, npad, stream)
+            ev[2].record(stream)
+            pkg.moe_w8a16_gemm1(x, layer.w13_weight, layer.w13_scale, s_ids, b_exp, npad, block_m, k, a_buf, stream)
+            ev[3].record(stream)
+            pkg.moe_w8a16_gemm2(a_buf, T, k, layer.w2_weight, layer.w2_scale, s_ids, b_exp, npad, block_m, splits,
+                                y_buf, stream)
+            ev[4].record(stream)
+            pkg.moe_combine_topk(y_buf, splits, tw, ti, E, out, stream)
+            ev[5].record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                for j, n in enumerate(names):
+                    acc[n].append(ev[j].elapsed_time(ev[j + 1]))
+        stage_ms = {n: float(np.mean(v)) for n, v in acc.items()}
+
+    if stage_ms:
+        dominant = "gemm1"
+        dur_s = stage_ms["gemm1"] / 1e3
+        if T >= 1024:
+            roof = {"bound": "mfma", "achieved": flops_gemm1 / dur_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": bytes_gemm1 / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = None
+        roof["kernel"] = "gemm1_w8_kernel"
+        roof["kernel_ms"] = stage_ms["gemm1"]
+    else:
+        dur_s = ms_per_step / 1e3
+        roof = {"bound": "hbm", "achieved": bytes_layer / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": bytes_layer / dur_s / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": "whole layer"}
+
+    layer_hbm_frac = bytes_layer / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS
+    layer_mfma_frac = flops_layer / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS
+
+    # ---- CPU oracle on a bounded sample ---------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, T, xb, logits_np, args, active)
+
+    res = {
+        "metric": "MoE-layer tokens/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "ms_per_step_median": ms_median,
+        "wall_s_timed_region": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ("fp16" if wl.act == "fp16" else "bf16") + (" x uint4" if w4 else " x int8"),
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "E": E, "top_k": k, "H": H, "I": I,
+                   "weights": "uint4 g128 asym" if w4 else "int8 per-channel sym",
+                   "block_m": block_m, "splits": splits, "active_experts": n_active,
+                   "flush_mb_between_steps": flush_mb},
+        "layer": {"algorithmic_bytes": bytes_layer, "algorithmic_flops": flops_layer,
+                  "hbm_frac": layer_hbm_frac, "mfma_frac": layer_mfma_frac},
+        "stage_ms": stage_ms,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(wl, T, xb, logits_np, args, active):
+    """The fp64 oracle (as it stands) on the host cores: routing + quantized-expert forward."""
+    import oracle
+    from weight_quantized_mixture_amd import synthetic
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    Ts = args.cpu_sample_tokens or min(T, 64)
+    rows = np.linspace(0, T - 1, Ts).astype(int)
+    w_ref, ids_ref = oracle.route_softmax_topk(logits_np[rows], wl.k, wl.renormalize)
+    used = np.unique(ids_ref)
+    # the oracle quantizes its own weights (not timed: offline in the method too)
+    t0 = time.time()
+    if wl.weights == "w8":
+        q13 = {}; s13 = {}; q2 = {}; s2 = {}
+        for e in used:
+            q13[e], s13[e] = oracle.quantize_int8_rows(synthetic.expert_master(wl, "w13", e, args.seed))
+            q2[e], s2[e] = oracle.quantize_int8_rows(synthetic.expert_master(wl, "w2", e, args.seed))
+        w13_of = lambda e: oracle.dequant_int8_rows(q13[e], s13[e])  # noqa: E731
+        w2_of = lambda e: oracle.dequant_int8_rows(q2[e], s2[e])  # noqa: E731
+    else:
+        g = wl.group_size
+        P = {}
+        for e in used:
+            q, s, z = oracle.quantize_w4_groups(synthetic.expert_master(wl, "w13", e, args.seed), g)
+            q2_, s2_, z2_ = oracle.quantize_w4_groups(synthetic.expert_master(wl, "w2", e, args.seed), g)
+            P[e] = (oracle.pack_w4_along_k(q), s, oracle.pack_w4_along_n(z),
+                    oracle.pack_w4_along_k(q2_), s2_, oracle.pack_w4_along_n(z2_))
+        w13_of = lambda e: oracle.dequant_w4(P[e][0], P[e][1], P[e][2], g)  # noqa: E731
+        w2_of = lambda e: oracle.dequant_w4(P[e][3], P[e][4], P[e][5], g)  # noqa: E731
+    log(f"[bench] oracle weights ready ({time.time() - t0:.1f}s)")
+    x = oracle.act_bits_to_f64(xb[rows], wl.act)
+    t1 = time.perf_counter()
+    w_ref, ids_ref = oracle.route_softmax_topk(logits_np[rows], wl.k, wl.renormalize)
+    oracle.moe_forward_dense(x, w13_of, w2_of, w_ref, ids_ref, wl.I)
+    dt = time.perf_counter() - t1
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{Ts} of the {T} tokens (evenly spaced), routing + fp64 forward with per-expert "
+                      f"dequantization of the {used.size} experts they use; weight quantization not timed"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * moe_wq.h -- C ABI of the weight-only-quantized fused MoE layer for MI355X (gfx950).
+ *
+ * What is computed (the pages' statement of the problem):
+ *   experts_int8 page (vllm.model_executor.layers.quantization.experts_int8):
+ *     - quantize_in_place_and_get_scales: per-row symmetric int8 weights;
+ *     - ExpertsInt8MoEMethod.create_weights: w13 int8 [E, 2I, H] (gate rows
+ *       0..I-1, up rows I..2I-1), w2 int8 [E, H, I], w13_scale fp32 [E, 2I],
+ *       w2_scale fp32 [E, H];
+ *     - ExpertsInt8MoEMethod.apply: select_experts (softmax, top_k,
+ *       renormalize) then fused_experts (activation "silu",
+ *       use_int8_w8a16, apply_router_weight_on_input=False, inplace=True).
+ *   moe_wna16 page (vllm.model_executor.layers.quantization.moe_wna16):
+ *     - MoeWNA16Method.create_weights: 4-bit codes packed along K, group
+ *       scales [E, N, K/g], zeros packed along N; the weight loader stores the
+ *       true zero point (GPTQ zeros get +1).
+ *     - MoeWNA16Method.apply: the layer takes precomputed topk_weights and
+ *       topk_ids (routing is a separate call).
+ *
+ * Conventions for every call:
+ *   - Pointers named "device" are device memory of the current HIP device;
+ *     the caller allocates and owns every buffer.  The library allocates no
+ *     device memory and keeps no state apart from a thread-local error text.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and never
+ *     synchronised; results are ready when the stream reaches them.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error nothing is launched.  No C++ exception crosses this boundary.
+ *   - Layouts are row-major with the last index contiguous.
+ *   - Return value: MOE_OK (0) or an moe_status code; moe_last_error() gives
+ *     the detail of the last failure on the calling thread.
+ */
+#ifndef MOE_WQ_H_
+#define MOE_WQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad dimension, k > E, misaligned size  */
+  MOE_ERR_UNSUPPORTED = 2,        /* dtype or size outside what the kernels implement     */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP launch or runtime call failed                  */
+};
+
+enum moe_act_dtype { MOE_BF16 = 0, MOE_FP16 = 1 };
+
+/* Text of a status code (static storage). */
+const char* moe_status_string(int status);
+/* Detail of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * a1. Per-output-channel symmetric int8 quantization.
+ * experts_int8 page, quantize_in_place_and_get_scales: for every row n of
+ * every expert e, s[e,n] = max_k |w[e,n,k]| / 127 (fp32 IEEE divide), then
+ * q[e,n,k] = clamp(rint(w[e,n,k] / s[e,n]), -127, 127) with the fp32 IEEE
+ * divide and round half to even.  An all-zero row gets s = 0 and q = 0.
+ *   w     device fp32 [E, N, K]   (read only)
+ *   q     device int8 [E, N, K]   (written)
+ *   scale device fp32 [E, N]      (written)
+ * For w13 pass N = 2I, K = H (gate rows then up rows); for w2 N = H, K = I.
+ * Errors: MOE_ERR_INVALID_ARGUMENT for null pointers or E, N, K < 1.
+ * ---------------------------------------------------------------------- */
+int moe_quantize_weights_int8(const float* w, int64_t E, int64_t N, int64_t K,
+                              int8_t* q, float* scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * a2. Softmax top-k router.
+ * experts_int8 page, ExpertsInt8MoEMethod.apply -> select_experts with
+ * scoring_func "softmax", top_k, renormalize.  For each token t: the k ids
+ * with the largest logits in descending order (equal logits: lower id
+ * first); p = softmax over all E in fp32; topk_w[t,j] = p[id_j], divided by
+ * the sum of the k chosen p when renormalize != 0.
+ *   logits   device fp32  [T, E]
+ *   topk_w   device fp32  [T, k]  (written)
+ *   topk_ids device int32 [T, k]  (written)
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null pointer with T > 0, E < 1, k < 1,
+ * k > E, T < 0); MOE_ERR_UNSUPPORTED if E > 1024.  T = 0 launches nothing.
+ * ---------------------------------------------------------------------- */
+int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t k, int renormalize,
+                   float* topk_w, int32_t* topk_ids, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * a3. Token -> expert align: histogram, prefix scan, padded-block permutation.
+ * The pages call the fused kernel that consumes this grouping without
+ * printing it (experts_int8 page, ExpertsInt8MoEMethod.apply).  Definition:
+ * with f = t*k + j the flat assignment index and c_e the number of f with
+ * topk_ids[f] == e (ids outside [0, E) are dropped), each expert owns
+ * ceil(c_e / block_m) blocks of block_m rows, experts in ascending order;
+ * inside an expert the f ascend, and the rest of its last block holds the
+ * sentinel T*k.  block_expert[b] is the expert of block b.  Rows and blocks
+ * past the used ones hold T*k and -1.  *num_padded = block_m * (blocks used).
+ *   topk_ids     device int32 [T*k]
+ *   sorted_ids   device int32 [moe_align_capacity(T,k,E,block_m)]         (written)
+ *   block_expert device int32 [moe_align_capacity(T,k,E,block_m)/block_m] (written)
+ *   num_padded   device int32 [1]                                         (written)
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null pointer with T*k > 0, E < 1,
+ * block_m < 1); MOE_ERR_UNSUPPORTED if E > 1024 or block_m > 1024.
+ * T*k = 0 writes *num_padded = 0 only.
+ * ---------------------------------------------------------------------- */
+int64_t moe_align_capacity(int64_t T, int64_t k, int64_t E, int64_t block_m);
+int moe_align_block(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int64_t block_m,
+                    int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * a4-a6. The W8A16 layer forward.
+ * experts_int8 page, ExpertsInt8MoEMethod.apply -> fused_experts with
+ * use_int8_w8a16: for every assignment (t, j) to expert e = topk_ids[t,j]:
+ *   h = (w13[e] * w13_scale[e]) x_t              (fp32 accumulation, scale on the accumulator)
+ *   a = silu(h[0:I]) * h[I:2I]                   (silu(g) = g / (1 + exp(-g)))
+ *   y = (w2[e] * w2_scale[e]) a
+ *   out_t = sum_j topk_w[t,j] * y                (fp32, j ascending; cast to the activation type)
+ *   x          device bf16/fp16 [T, H] (act_dtype)
+ *   w13        device int8 [E, 2I, w13_row_stride]  (row stride in elements, 0 means H)
+ *   w13_scale  device fp32 [E, 2I]
+ *   w2         device int8 [E, H, w2_row_stride]    (0 means I)
+ *   w2_scale   device fp32 [E, H]
+ *   topk_w     device fp32 [T, k];  topk_ids device int32 [T, k]
+ *   block_m    rows per align block: 0 = moe_w8a16_block_m(...), else 16, 32 or 64
+ *              (multiples of 16 up to 256 use the large-tile path)
+ *   out        device bf16/fp16 [T, H]; may be the same buffer as x (inplace=True)
+ *   workspace  device, at least moe_w8a16_workspace_bytes(...) bytes, 256-byte aligned
+ * Requirements: H and I multiples of 128; row strides multiples of 16 and
+ * at least the row length; 1 <= k <= E <= 1024.
+ * Errors: MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED (act_dtype, block_m),
+ * MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP.  T = 0 launches nothing.
+ * ---------------------------------------------------------------------- */
+int64_t moe_w8a16_block_m(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k);
+size_t moe_w8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                                 int64_t block_m);
+int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I,
+                      int64_t E, int64_t k,
+                      const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                      const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                      const float* topk_w, const int32_t* topk_ids, int64_t block_m,
+                      void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Stages of the forward, exported so that each kernel can be checked and
+ * timed alone.  moe_w8a16_forward is exactly moe_align_block followed by
+ * these three calls on the workspace regions.
+ *
+ * moe_w8a16_gemm1: for every padded row r < *num_padded with
+ * f = sorted_ids[r] < T*k, t = f / k, e = block_expert[r / block_m]:
+ *   a[r, i] = silu(h_i) * h_{I+i},  h_n = w13_scale[e,n] * sum_c x[t,c] w13[e,n,c]
+ * Padding rows get a = 0.  a is device fp32 [cap, I], cap = moe_align_capacity.
+ *
+ * moe_w8a16_gemm2: for every valid padded row r (f = sorted_ids[r] < T*k),
+ * split s < splits, h < H:
+ *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} a[r, i] w2[e,h,i]
+ * The K range [0, I) is cut into `splits` equal parts (I/splits a multiple
+ * of 128).  y is device fp32 [splits, T*k, H]; rows of dropped ids are not
+ * written.  moe_w8a16_splits gives the split count the forward uses.
+ *
+ * moe_combine_topk: out[t, h] = sum_j topk_w[t,j] * sum_s y[s, t*k+j, h]
+ * over the j with topk_ids in [0, E), in fp32 with j and s ascending, cast
+ * to act_dtype (round to nearest even).
+ * ---------------------------------------------------------------------- */
+int64_t moe_w8a16_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m);
+int moe_w8a16_gemm1(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
+                    int64_t k, const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                    const int32_t* sorted_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, int64_t block_m, float* a, hipStream_t stream);
+int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                    const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                    const int32_t* sorted_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, int64_t block_m, int64_t splits, float* y,
+                    hipStream_t stream);
+int moe_combine_topk(const float* y, int64_t splits, int64_t T, int64_t k, int64_t H, int64_t E,
+                     const float* topk_w, const int32_t* topk_ids, int act_dtype, void* out,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * a7. Group-wise asymmetric 4-bit weights with zero points (W4A16).
+ * moe_wna16 page, MoeWNA16Method.create_weights: codes packed 8 per int32
+ * along K (code k at bits 4*(k mod 8), byte-identical to the page's uint8
+ * packing with the even code in the low nibble), scales fp16 [E, N, K/g],
+ * zeros packed 8 per int32 along N (row n at bits 4*(n mod 8)), the zero
+ * being the true zero: W[n,k] = (q[n,k] - z[n,k/g]) * s[n,k/g].
+ *
+ * moe_quantize_weights_w4 (the pages print no 4-bit quantizer; this is the
+ * min/max reading): per row n and group of g consecutive K,
+ * lo = min(w, 0), hi = max(w, 0), s = fp16((hi - lo) / 15) (s = 1 if that
+ * rounds to 0), z = clamp(rint(-lo / s), 0, 15),
+ * q = clamp(rint(w / s) + z, 0, 15), all in fp32 with the fp16 s.
+ *   w        device fp32 [E, N, K]
+ *   qweight  device int32  [E, N, K/8]    (written)
+ *   scales   device uint16 [E, N, K/g]    (fp16 bits, written)
+ *   qzeros   device int32  [E, N/8, K/g]  (written)
+ * Requirements: N % 8 == 0, g % 8 == 0, K % g == 0.
+ *
+ * moe_w4a16_forward: as moe_w8a16_forward with the weights above
+ * (w13: N = 2I, K = H; w2: N = H, K = I).  Requirements: H and I multiples
+ * of 128 and of g; g a multiple of 128 (MOE_ERR_UNSUPPORTED otherwise).
+ * With fp16 activations the intermediate a is carried in fp16 (hi + lo
+ * pair), so it must stay inside the fp16 range like the activations.
+ * moe_w4a16_workspace_bytes equals moe_w8a16_workspace_bytes.
+ * ---------------------------------------------------------------------- */
+int moe_quantize_weights_w4(const float* w, int64_t E, int64_t N, int64_t K, int64_t group_size,
+                            int32_t* qweight, uint16_t* scales, int32_t* qzeros,
+                            hipStream_t stream);
+size_t moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                                 int64_t block_m);
+int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I,
+                      int64_t E, int64_t k,
+                      const int32_t* w13_qweight, const uint16_t* w13_scales,
+                      const int32_t* w13_qzeros,
+                      const int32_t* w2_qweight, const uint16_t* w2_scales,
+                      const int32_t* w2_qzeros, int64_t group_size,
+                      const float* topk_w, const int32_t* topk_ids, int64_t block_m,
+                      void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_WQ_H_ */

@@ -1,0 +1,121 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import weight_quantized_mixture_amd as pkg
+from weight_quantized_mixture_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_wq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ["moe_quantize_weights_int8", "moe_route_topk", "moe_align_block", "moe_w8a16_forward"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = pkg.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in B.SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings():
+    L = pkg.lib()
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert L.moe_status_string(99) == b"MOE_UNKNOWN_STATUS"
+
+
+@pytest.mark.parametrize("T,k,E,bm", [(0, 2, 8, 16), (3, 2, 4, 2), (16, 2, 8, 16), (37, 6, 64, 16),
+                                      (4096, 2, 8, 64), (1, 8, 128, 32), (5, 1, 1000, 1)])
+def test_capacity_matches_oracle(T, k, E, bm):
+    assert pkg.moe_align_capacity(T, k, E, bm) == oracle.align_capacity(T, k, E, bm)
+
+
+def test_heuristics():
+    for (T, H, I, E, k) in [(1, 4096, 14336, 8, 2), (64, 4096, 14336, 8, 2), (4096, 4096, 14336, 8, 2),
+                            (16, 2048, 1408, 64, 6), (256, 2048, 768, 128, 8), (16, 256, 512, 8, 2)]:
+        bm = pkg.moe_w8a16_block_m(T, H, I, E, k)
+        assert bm % 16 == 0 and 16 <= bm <= 256
+        s = pkg.moe_w8a16_splits(T, H, I, E, k, 0)
+        assert s >= 1 and (I // 128) % s == 0
+        assert pkg.moe_w8a16_workspace_bytes(T, H, I, E, k, 0) > 0
+    assert pkg.moe_w8a16_workspace_bytes(0, 4096, 14336, 8, 2, 0) == 0
+
+
+FAKE = 0x100000          # an aligned address that is never dereferenced: every call below fails first
+
+
+def _fwd(T=4, H=256, I=512, E=8, k=2, act=0, ld13=0, ld2=0, bm=0, ws_bytes=1 << 40, nullx=False,
+         x=FAKE, ws=FAKE):
+    L = pkg.lib()
+    p = ctypes.c_void_p
+    return L.moe_w8a16_forward(None if nullx else p(x), act, T, H, I, E, k, p(FAKE), p(FAKE), ld13,
+                               p(FAKE), p(FAKE), ld2, p(FAKE), p(FAKE), bm, p(FAKE), p(ws), ws_bytes, None)
+
+
+def test_forward_argument_errors():
+    assert _fwd(H=200) == B.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(I=100) == B.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(k=9) == B.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(T=-1) == B.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(E=2048, k=2) == B.MOE_ERR_UNSUPPORTED
+    assert _fwd(act=7) == B.MOE_ERR_UNSUPPORTED
+    assert _fwd(bm=24) == B.MOE_ERR_UNSUPPORTED
+    assert _fwd(bm=512) == B.MOE_ERR_UNSUPPORTED
+    assert _fwd(ld13=100) == B.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(ld13=264) == B.MOE_ERR_INVALID_ARGUMENT     # not a multiple of 16
+    assert _fwd(nullx=True) == B.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(x=FAKE + 2) == B.MOE_ERR_INVALID_ARGUMENT   # misaligned activations
+    assert _fwd(ws=FAKE + 64) == B.MOE_ERR_INVALID_ARGUMENT  # workspace must be 256-byte aligned
+    need = pkg.moe_w8a16_workspace_bytes(4, 256, 512, 8, 2, 0)
+    assert _fwd(ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert b"workspace" in pkg.lib().moe_last_error()
+    assert _fwd(T=0, nullx=True) == B.MOE_OK                # T = 0 is a no-op
+
+
+def test_other_argument_errors():
+    L = pkg.lib()
+    p = ctypes.c_void_p
+    assert L.moe_route_topk(p(FAKE), 4, 8, 9, 1, p(FAKE), p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_route_topk(p(FAKE), 4, 2048, 2, 1, p(FAKE), p(FAKE), None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(None, 4, 8, 2, 1, None, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_route_topk(None, 0, 8, 2, 1, None, None, None) == B.MOE_OK
+    assert L.moe_quantize_weights_int8(None, 1, 1, 1, None, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_quantize_weights_int8(p(FAKE), 0, 1, 1, p(FAKE), p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_align_block(p(FAKE), 4, 2, 8, 0, p(FAKE), p(FAKE), p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_align_block(p(FAKE), 4, 2, 2000, 16, p(FAKE), p(FAKE), p(FAKE), None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_weights_w4(p(FAKE), 1, 12, 256, 128, p(FAKE), p(FAKE), p(FAKE), None) == \
+        B.MOE_ERR_INVALID_ARGUMENT                         # N not a multiple of 8
+    assert L.moe_quantize_weights_w4(p(FAKE), 1, 16, 200, 128, p(FAKE), p(FAKE), p(FAKE), None) == \
+        B.MOE_ERR_INVALID_ARGUMENT                         # K not a multiple of the group
+    r = L.moe_w4a16_forward(p(FAKE), 1, 4, 256, 512, 8, 2, p(FAKE), p(FAKE), p(FAKE), p(FAKE), p(FAKE),
+                            p(FAKE), 64, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), 1 << 40, None)
+    assert r == B.MOE_ERR_UNSUPPORTED                       # group 64 not implemented by the forward
+    assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 16, 3,
+                             p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # 3 does not divide I/128
+    assert L.moe_combine_topk(p(FAKE), 1, 4, 2, 256, 8, p(FAKE), p(FAKE), 5, p(FAKE), None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_binding_raises_python_errors():
+    with pytest.raises(ValueError):
+        B._check(B.MOE_ERR_INVALID_ARGUMENT, "x")
+    with pytest.raises(NotImplementedError):
+        B._check(B.MOE_ERR_UNSUPPORTED, "x")
+    with pytest.raises(B.MoeError):
+        B._check(B.MOE_ERR_HIP, "x")

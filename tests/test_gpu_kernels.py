@@ -1,0 +1,189 @@
+"""GPU parity of the single kernels against the oracle: the int8 and uint4
+quantizers and the align permutation bit for bit, router ids bit for bit and
+weights within 1e-6, GEMM1's SiLU-gated intermediate against fp64."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_quantized_mixture_amd as pkg
+from weight_quantized_mixture_amd import synthetic
+
+from moe_cases import DEV, log, route_both, small_w8, to_dev_act
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    pkg.lib()
+
+
+def _quant_gpu(w):
+    E, N, K = w.shape
+    q = torch.empty(E, N, K, dtype=torch.int8, device=DEV)
+    s = torch.empty(E, N, dtype=torch.float32, device=DEV)
+    pkg.moe_quantize_weights_int8(torch.from_numpy(w).to(DEV), q, s)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def test_quantize_int8_golden():
+    g = json.load(open(os.path.join(GOLD, "quantize_int8_handworked.json")))
+    q, s = _quant_gpu(np.array([g["w"]], np.float32))
+    np.testing.assert_array_equal(q[0], np.array(g["q"], np.int8))
+    np.testing.assert_array_equal(s[0], np.array(g["scale"], np.float32))
+
+
+@pytest.mark.parametrize("shape", [(3, 64, 257), (2, 96, 512), (1, 5, 14336), (4, 33, 4)])
+def test_quantize_int8_random(shape):
+    log(f"[quantize_int8] shape={shape}")
+    w = synthetic.random_master(shape, seed=sum(shape))
+    w[0, 1, :] = 0.0                    # an all-zero row
+    q, s = _quant_gpu(w)
+    qr, sr = oracle.quantize_int8_rows(w)
+    np.testing.assert_array_equal(s.view(np.uint32), sr.view(np.uint32))
+    np.testing.assert_array_equal(q, qr)
+
+
+def test_quantize_int8_halfway_cases():
+    # rows whose quotients sit on or next to k + 1/2, where divide, reciprocal and rounding mode differ
+    rng = np.random.default_rng(0)
+    rows = []
+    for _ in range(256):
+        m = np.float32(rng.uniform(0.01, 0.1))
+        s = np.float32(m / np.float32(127))
+        kk = int(rng.integers(0, 126))
+        w = np.float32((kk + 0.5) * float(s))
+        rows.append([m, np.nextafter(w, np.float32(-1)), w, np.nextafter(w, np.float32(1))])
+    w = np.array(rows, np.float32)[None]
+    q, s = _quant_gpu(w)
+    qr, sr = oracle.quantize_int8_rows(w)
+    np.testing.assert_array_equal(q, qr)
+
+
+@pytest.mark.parametrize("group", [8, 32, 128])
+def test_quantize_w4_random_and_golden(group):
+    g = json.load(open(os.path.join(GOLD, "w4_handworked.json")))
+    w = synthetic.random_master((2, 24, 256), seed=group)
+    w[0, 3, :group] = 0.0               # a flat group
+    w[1, 0, :8] = np.array(g["w"], np.float32)
+    qw = torch.empty(2, 24, 32, dtype=torch.int32, device=DEV)
+    sc = torch.empty(2, 24, 256 // group, dtype=torch.float16, device=DEV)
+    qz = torch.empty(2, 3, 256 // group, dtype=torch.int32, device=DEV)
+    pkg.moe_quantize_weights_w4(torch.from_numpy(w).to(DEV), group, qw, sc, qz)
+    torch.cuda.synchronize()
+    q, s, z = oracle.quantize_w4_groups(w, group)
+    np.testing.assert_array_equal(qw.cpu().numpy(), oracle.pack_w4_along_k(q))
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint16), s.view(np.uint16))
+    np.testing.assert_array_equal(qz.cpu().numpy(), np.stack([oracle.pack_w4_along_n(z[e]) for e in range(2)]))
+    if group == 8:
+        assert format(int(qw.cpu().numpy().view(np.uint32)[1, 0, 0]), "08X") == g["packed_word_hex"]
+
+
+@pytest.mark.parametrize("T,E,k,renorm", [(37, 8, 2, True), (16, 64, 6, True), (33, 128, 8, True),
+                                          (5, 1024, 8, True), (9, 5, 5, False), (64, 8, 1, True),
+                                          (3, 100, 7, False), (1, 1, 1, True)])
+def test_route(T, E, k, renorm):
+    log(f"[route] T={T} E={E} k={k} renorm={renorm}")
+    logits = synthetic.random_logits(T, E, seed=T * E + k)
+    if E >= 4:
+        logits[0, 1] = logits[0, 3] = np.float32(logits[0].max() + 1)   # a tie at the top
+    tw, ti, w_ref, ids_ref = route_both(logits, k, renorm)
+    np.testing.assert_array_equal(ti.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(tw.cpu().numpy(), w_ref, rtol=0, atol=1e-6)
+    if k == 1 and renorm:
+        assert np.all(tw.cpu().numpy() == 1.0)
+
+
+def test_route_t0():
+    tw = torch.empty(0, 2, dtype=torch.float32, device=DEV)
+    ti = torch.empty(0, 2, dtype=torch.int32, device=DEV)
+    pkg.moe_route_topk(torch.empty(0, 8, dtype=torch.float32, device=DEV), 2, True, tw, ti)
+    torch.cuda.synchronize()
+
+
+def _align_gpu(ids, E, bm):
+    T, k = ids.shape
+    cap = pkg.moe_align_capacity(T, k, E, bm)
+    s = torch.full((max(cap, 1),), -7, dtype=torch.int32, device=DEV)[:cap]
+    b = torch.full((max(cap // bm, 1),), -7, dtype=torch.int32, device=DEV)[:cap // bm]
+    n = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    pkg.moe_align_block(torch.from_numpy(ids).to(DEV), E, bm, s, b, n)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), b.cpu().numpy(), int(n.item())
+
+
+@pytest.mark.parametrize("T,k,E,bm,skew", [(3, 2, 4, 2, False), (37, 6, 64, 16, True), (64, 2, 8, 32, False),
+                                           (4096, 2, 8, 64, True), (512, 6, 64, 16, True), (1, 8, 128, 16, False),
+                                           (256, 8, 128, 32, False), (100, 3, 1, 16, False),
+                                           (300, 4, 1024, 16, False), (129, 2, 8, 1, False),
+                                           (77, 3, 16, 128, True), (4096, 2, 8, 256, False)])
+def test_align(T, k, E, bm, skew):
+    log(f"[align] T={T} k={k} E={E} bm={bm} skew={skew}")
+    rng = np.random.default_rng(T + E + bm)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if skew:
+        ids[: (3 * T) // 4, 0] = 0
+    s, b, n = _align_gpu(ids, E, bm)
+    sr, br, nr = oracle.align_block(ids, E, bm)
+    assert n == nr
+    np.testing.assert_array_equal(s, sr)
+    np.testing.assert_array_equal(b, br)
+
+
+def test_align_drops_out_of_range_ids():
+    ids = np.array([[0, 9], [-1, 1], [1, 0], [5, 5]], np.int32)
+    s, b, n = _align_gpu(ids, 2, 2)
+    sr, br, nr = oracle.align_block(ids, 2, 2)
+    assert n == nr
+    np.testing.assert_array_equal(s, sr)
+    np.testing.assert_array_equal(b, br)
+
+
+def test_align_empty():
+    n = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    e = torch.empty(0, dtype=torch.int32, device=DEV)
+    pkg.moe_align_block(torch.empty(0, 2, dtype=torch.int32, device=DEV), 8, 16, e, e, n)
+    torch.cuda.synchronize()
+    assert int(n.item()) == 0
+
+
+@pytest.mark.parametrize("act,bm", [("bf16", 16), ("fp16", 32), ("bf16", 64), ("bf16", 48)])
+def test_gemm1_intermediate(act, bm):
+    E, k, H, I, T = 8, 2, 384, 640, 29
+    log(f"[gemm1] act={act} bm={bm} E={E} H={H} I={I} T={T}")
+    W = small_w8(E, H, I, seed=3)
+    assert W.mismatch == 0
+    xb = synthetic.random_activations(T, H, act, seed=4)
+    logits = synthetic.random_logits(T, E, seed=5)
+    tw, ti, w_ref, ids_ref = route_both(logits, k)
+    cap = pkg.moe_align_capacity(T, k, E, bm)
+    s = torch.empty(cap, dtype=torch.int32, device=DEV)
+    b = torch.empty(cap // bm, dtype=torch.int32, device=DEV)
+    n = torch.empty(1, dtype=torch.int32, device=DEV)
+    pkg.moe_align_block(ti, E, bm, s, b, n)
+    a = torch.full((cap, I), float("nan"), dtype=torch.float32, device=DEV)
+    x = to_dev_act(xb, act)
+    pkg.moe_w8a16_gemm1(x, W.w13, W.s13, s, b, n, bm, k, a)
+    torch.cuda.synchronize()
+    sr, br, nr = oracle.align_block(ids_ref, E, bm)
+    a_g = a.cpu().numpy().astype(np.float64)
+    xf = oracle.act_bits_to_f64(xb, act)
+    for blk in range(nr // bm):
+        e = br[blk]
+        W13 = oracle.dequant_int8_rows(W.q13[e], W.hs13[e])
+        rows = sr[blk * bm:(blk + 1) * bm]
+        for r_local, f in enumerate(rows):
+            r = blk * bm + r_local
+            if f >= T * k:
+                assert np.all(a_g[r] == 0.0)
+                continue
+            ref = oracle.moe_expert_intermediate(xf[f // k][None], W13, I)[0]
+            err = np.abs(a_g[r] - ref)
+            assert np.all(err <= 2e-5 * np.abs(ref).max() + 1e-4 * np.abs(ref)), (blk, f, err.max())

@@ -1,0 +1,175 @@
+"""GPU parity of the whole layer (route + align + GEMM1/SiLU + GEMM2 + combine)
+against the fp64 oracle, to the layer tolerance
+max|gpu - ref| <= 2e-2 max|ref| and |gpu - ref| <= 2e-2 |ref| + 1e-3 per element,
+with router ids bit for bit.  Full-size workloads use every token when the
+oracle is quick and an even sample of tokens for the long prefill."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import weight_quantized_mixture_amd as pkg
+from weight_quantized_mixture_amd import synthetic
+
+from moe_cases import (DEV, act_f64, assert_layer_close, log, ref_w8, route_both, run_w8_layer, small_w8,
+                       to_dev_act, workload_weights)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    pkg.lib()
+
+
+def _check_routing(ti, tw, ids_ref, w_ref):
+    np.testing.assert_array_equal(ti, ids_ref)
+    np.testing.assert_allclose(tw, w_ref, rtol=0, atol=1e-6)
+
+
+def test_tiny_workload():
+    wl = synthetic.WORKLOADS["tiny"]
+    W = workload_weights(wl)
+    assert W.mismatch == 0
+    T = wl.tokens[0]
+    xb = synthetic.activations(wl, T)
+    logits = synthetic.router_logits(wl, T)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, wl.act, logits, wl.k)
+    _check_routing(ti, tw, ids_ref, w_ref)
+    assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), "tiny T=16")
+
+
+@pytest.mark.parametrize("act,bm,T", [("bf16", 0, 37), ("fp16", 0, 37), ("bf16", 16, 5), ("bf16", 32, 61),
+                                      ("bf16", 64, 130), ("fp16", 48, 77), ("bf16", 128, 300)])
+def test_ragged_shapes(act, bm, T):
+    E, k, H, I = 8, 2, 384, 640
+    log(f"[layer] ragged act={act} bm={bm} T={T}")
+    W = small_w8(E, H, I, seed=7)
+    assert W.mismatch == 0
+    xb = synthetic.random_activations(T, H, act, seed=T)
+    logits = synthetic.random_logits(T, E, seed=T + 1)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, act, logits, k, block_m=bm)
+    _check_routing(ti, tw, ids_ref, w_ref)
+    assert_layer_close(got, ref_w8(W, xb, act, w_ref, ids_ref), f"ragged {act} bm={bm} T={T}")
+
+
+def test_edge_cases_routing_shapes():
+    H, I = 256, 256
+    # k = E, one token, renormalize off
+    W = small_w8(4, H, I, seed=11)
+    xb = synthetic.random_activations(1, H, "bf16", seed=12)
+    logits = synthetic.random_logits(1, 4, seed=13)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, "bf16", logits, 4, renormalize=False)
+    _check_routing(ti, tw, ids_ref, w_ref)
+    assert_layer_close(got, ref_w8(W, xb, "bf16", w_ref, ids_ref), "k=E T=1")
+    # every token to one expert (others empty)
+    W = small_w8(16, H, I, seed=14)
+    xb = synthetic.random_activations(50, H, "bf16", seed=15)
+    bias = np.zeros(16, np.float32); bias[9] = 30.0
+    logits = synthetic.random_logits(50, 16, seed=16, bias=bias)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, "bf16", logits, 1)
+    assert np.all(ti == 9)
+    assert_layer_close(got, ref_w8(W, xb, "bf16", w_ref, ids_ref), "all tokens to one expert")
+    # many experts, few tokens (most experts empty)
+    W = small_w8(64, H, I, seed=17)
+    xb = synthetic.random_activations(2, H, "bf16", seed=18)
+    logits = synthetic.random_logits(2, 64, seed=19)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, "bf16", logits, 6)
+    assert_layer_close(got, ref_w8(W, xb, "bf16", w_ref, ids_ref), "E=64 T=2")
+
+
+def test_inplace_and_determinism():
+    E, k, H, I, T = 8, 2, 256, 384, 40
+    W = small_w8(E, H, I, seed=21)
+    xb = synthetic.random_activations(T, H, "bf16", seed=22)
+    logits = synthetic.random_logits(T, E, seed=23)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, "bf16", logits, k, inplace=True)
+    assert_layer_close(got, ref_w8(W, xb, "bf16", w_ref, ids_ref), "inplace out == x")
+    outs = []
+    for _ in range(2):
+        g2, *_ = run_w8_layer(W, xb, "bf16", logits, k)
+        outs.append(g2)
+    assert np.array_equal(outs[0], outs[1]), "two runs differ bitwise"
+    assert np.array_equal(outs[0], got), "inplace result differs from out-of-place"
+
+
+def test_out_of_range_ids_dropped():
+    E, k, H, I, T = 8, 2, 256, 256, 6
+    W = small_w8(E, H, I, seed=31)
+    xb = synthetic.random_activations(T, H, "bf16", seed=32)
+    ids = np.array([[0, 9], [-1, 3], [2, 2], [7, 8], [1, 0], [5, 4]], np.int32)
+    w = np.full((T, k), 0.5, np.float32)
+    x = to_dev_act(xb, "bf16")
+    out = torch.empty_like(x)
+    ws = torch.empty(pkg.moe_w8a16_workspace_bytes(T, H, I, E, k, 0), dtype=torch.uint8, device=DEV)
+    pkg.moe_w8a16_forward(x, W.w13, W.s13, W.w2, W.s2, torch.from_numpy(w).to(DEV),
+                          torch.from_numpy(ids).to(DEV), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward_w8(act_f64(xb, "bf16"), W.q13, W.hs13, W.q2, W.hs2, w.astype(np.float64), ids)
+    assert_layer_close(out.float().cpu().numpy().astype(np.float64), ref, "out-of-range ids")
+
+
+def test_zero_tokens():
+    H, I, E, k = 256, 256, 8, 2
+    W = small_w8(E, H, I, seed=41)
+    x = torch.empty(0, H, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    tw = torch.empty(0, k, dtype=torch.float32, device=DEV)
+    ti = torch.empty(0, k, dtype=torch.int32, device=DEV)
+    pkg.moe_w8a16_forward(x, W.w13, W.s13, W.w2, W.s2, tw, ti, torch.empty_like(x), ws)
+    torch.cuda.synchronize()
+
+
+def test_bad_shapes_raise():
+    W = small_w8(2, 256, 256, seed=1)
+    x = torch.zeros(4, 256, dtype=torch.bfloat16, device=DEV)
+    tw = torch.zeros(4, 2, dtype=torch.float32, device=DEV)
+    ti = torch.zeros(4, 2, dtype=torch.int32, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        pkg.moe_w8a16_forward(x, W.w13, W.s13, W.w2, W.s2, tw, ti, torch.empty_like(x), ws)   # workspace
+
+
+# ---- full-size workloads ------------------------------------------------------
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
+def test_mixtral_decode(T):
+    wl = synthetic.WORKLOADS["mixtral_decode"]
+    W = workload_weights(wl)
+    assert W.mismatch == 0, "GPU int8 codes or scales differ from the oracle"
+    xb = synthetic.activations(wl, T)
+    logits = synthetic.router_logits(wl, T)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, wl.act, logits, wl.k)
+    _check_routing(ti, tw, ids_ref, w_ref)
+    assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), f"mixtral decode T={T}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T,nsample", [(1024, 96), (4096, 64)])
+def test_mixtral_prefill_sampled(T, nsample):
+    wl = synthetic.WORKLOADS["mixtral_prefill"]
+    W = workload_weights(wl)
+    assert W.mismatch == 0
+    xb = synthetic.activations(wl, T)
+    logits = synthetic.router_logits(wl, T)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, wl.act, logits, wl.k)
+    _check_routing(ti, tw, ids_ref, w_ref)
+    rows = np.unique(np.concatenate([[0, T - 1], np.linspace(0, T - 1, nsample).astype(int)]))
+    assert_layer_close(got[rows], ref_w8(W, xb, wl.act, w_ref, ids_ref, rows=rows),
+                       f"mixtral prefill T={T} ({rows.size} sampled tokens)")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [16, 512])
+def test_fine_grained(T):
+    wl = synthetic.WORKLOADS["fine_grained"]
+    W = workload_weights(wl)
+    assert W.mismatch == 0
+    xb = synthetic.activations(wl, T)
+    logits = synthetic.router_logits(wl, T)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, wl.act, logits, wl.k)
+    _check_routing(ti, tw, ids_ref, w_ref)
+    assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), f"fine-grained T={T}")

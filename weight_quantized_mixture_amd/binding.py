@@ -1,0 +1,255 @@
+"""ctypes binding of libmoe_wq.so (the C ABI declared in include/moe_wq.h).
+
+Argument marshalling only: every function takes torch tensors (device memory
+the caller owns), passes their data pointers, sizes and the current HIP
+stream to the C call of the same name, and raises on a non-zero status
+(``ValueError`` for invalid arguments and workspace sizes, ``NotImplementedError``
+for unsupported cases, ``RuntimeError`` for HIP failures), mirroring the
+pages' error types (experts_int8 page, quantizing_weight_loader raises
+ValueError; apply raises NotImplementedError).  There is no fallback: if the
+library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_wq.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_BF16, MOE_FP16 = 0, 1
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_size = ctypes.c_size_t
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_c_int]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_quantize_weights_int8": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "moe_route_topk": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p]),
+    "moe_align_capacity": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "moe_align_block": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+    "moe_w8a16_block_m": (_c_i64, [_c_i64] * 5),
+    "moe_w8a16_workspace_bytes": (_c_size, [_c_i64] * 6),
+    "moe_w8a16_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                   _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                   _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_w8a16_splits": (_c_i64, [_c_i64] * 6),
+    "moe_w8a16_gemm1": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                 _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p]),
+    "moe_w8a16_gemm2": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                 _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
+    "moe_combine_topk": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                  _c_p, _c_p, _c_int, _c_p, _c_p]),
+    "moe_quantize_weights_w4": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+    "moe_w4a16_workspace_bytes": (_c_size, [_c_i64] * 6),
+    "moe_w4a16_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                   _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                   _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_wq.so (built in-tree by __graft_entry__.build()); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def _check(status: int, name: str):
+    if status == MOE_OK:
+        return
+    detail = lib().moe_last_error().decode(errors="replace")
+    text = f"{name}: {lib().moe_status_string(status).decode()}: {detail}"
+    if status in (MOE_ERR_INVALID_ARGUMENT, MOE_ERR_WORKSPACE_TOO_SMALL):
+        raise ValueError(text)
+    if status == MOE_ERR_UNSUPPORTED:
+        raise NotImplementedError(text)
+    raise MoeError(text)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _act(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float16:
+        return MOE_FP16
+    raise NotImplementedError(f"activation dtype {t.dtype} (bf16 or fp16 only)")
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+# ---------------------------------------------------------------------------
+# C calls of the same names
+# ---------------------------------------------------------------------------
+
+
+def moe_quantize_weights_int8(w: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=None):
+    E, N, K = w.shape
+    _need(w, torch.float32, (E, N, K), "w")
+    _need(q, torch.int8, (E, N, K), "q")
+    _need(scale, torch.float32, (E, N), "scale")
+    _check(lib().moe_quantize_weights_int8(_ptr(w), E, N, K, _ptr(q), _ptr(scale), _stream(stream)),
+           "moe_quantize_weights_int8")
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool, topk_w: torch.Tensor,
+                   topk_ids: torch.Tensor, stream=None):
+    T, E = logits.shape
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _check(lib().moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(topk_w),
+                                _ptr(topk_ids), _stream(stream)), "moe_route_topk")
+
+
+def moe_align_capacity(T: int, k: int, E: int, block_m: int) -> int:
+    return int(lib().moe_align_capacity(T, k, E, block_m))
+
+
+def moe_align_block(topk_ids: torch.Tensor, E: int, block_m: int, sorted_ids: torch.Tensor,
+                    block_expert: torch.Tensor, num_padded: torch.Tensor, stream=None):
+    T, k = topk_ids.shape
+    cap = moe_align_capacity(T, k, E, block_m)
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(sorted_ids, torch.int32, (cap,), "sorted_ids")
+    _need(block_expert, torch.int32, (cap // block_m,), "block_expert")
+    _need(num_padded, torch.int32, (1,), "num_padded")
+    _check(lib().moe_align_block(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids), _ptr(block_expert),
+                                 _ptr(num_padded), _stream(stream)), "moe_align_block")
+
+
+def moe_w8a16_block_m(T, H, I, E, k) -> int:
+    return int(lib().moe_w8a16_block_m(T, H, I, E, k))
+
+
+def moe_w8a16_splits(T, H, I, E, k, block_m=0) -> int:
+    return int(lib().moe_w8a16_splits(T, H, I, E, k, block_m))
+
+
+def moe_w8a16_workspace_bytes(T, H, I, E, k, block_m=0) -> int:
+    return int(lib().moe_w8a16_workspace_bytes(T, H, I, E, k, block_m))
+
+
+def moe_w4a16_workspace_bytes(T, H, I, E, k, block_m=0) -> int:
+    return int(lib().moe_w4a16_workspace_bytes(T, H, I, E, k, block_m))
+
+
+def _w8_shapes(w13, w2):
+    E, N2, H = w13.shape
+    I = N2 // 2
+    return E, H, I
+
+
+def moe_w8a16_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, workspace,
+                      block_m: int = 0, stream=None):
+    """out = MoE(x) for int8 experts; `workspace` is a uint8 device tensor of
+    at least moe_w8a16_workspace_bytes(...) bytes; `out` may be `x`."""
+    T, H = x.shape
+    E, _, I = _w8_shapes(w13, w2)
+    k = topk_ids.shape[1]
+    _need(w13, torch.int8, (E, 2 * I, H), "w13")
+    _need(w13_scale, torch.float32, (E, 2 * I), "w13_scale")
+    _need(w2, torch.int8, (E, H, I), "w2")
+    _need(w2_scale, torch.float32, (E, H), "w2_scale")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    _check(lib().moe_w8a16_forward(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), 0,
+                                   _ptr(w2), _ptr(w2_scale), 0, _ptr(topk_w), _ptr(topk_ids), block_m,
+                                   _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "moe_w8a16_forward")
+
+
+def moe_w8a16_gemm1(x, w13, w13_scale, sorted_ids, block_expert, num_padded, block_m, k, a, stream=None):
+    T, H = x.shape
+    E, N2, _ = w13.shape
+    I = N2 // 2
+    _check(lib().moe_w8a16_gemm1(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), 0,
+                                 _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), block_m, _ptr(a),
+                                 _stream(stream)), "moe_w8a16_gemm1")
+
+
+def moe_w8a16_gemm2(a, T, k, w2, w2_scale, sorted_ids, block_expert, num_padded, block_m, splits, y,
+                    stream=None):
+    E, H, I = w2.shape
+    _check(lib().moe_w8a16_gemm2(_ptr(a), T, H, I, E, k, _ptr(w2), _ptr(w2_scale), 0, _ptr(sorted_ids),
+                                 _ptr(block_expert), _ptr(num_padded), block_m, splits, _ptr(y),
+                                 _stream(stream)), "moe_w8a16_gemm2")
+
+
+def moe_combine_topk(y, splits, topk_w, topk_ids, E, out, stream=None):
+    T, H = out.shape
+    k = topk_ids.shape[1]
+    _check(lib().moe_combine_topk(_ptr(y), splits, T, k, H, E, _ptr(topk_w), _ptr(topk_ids), _act(out),
+                                  _ptr(out), _stream(stream)), "moe_combine_topk")
+
+
+def moe_quantize_weights_w4(w, group_size, qweight, scales, qzeros, stream=None):
+    E, N, K = w.shape
+    _need(w, torch.float32, (E, N, K), "w")
+    _need(qweight, torch.int32, (E, N, K // 8), "qweight")
+    _need(scales, torch.float16, (E, N, K // group_size), "scales")
+    _need(qzeros, torch.int32, (E, N // 8, K // group_size), "qzeros")
+    _check(lib().moe_quantize_weights_w4(_ptr(w), E, N, K, group_size, _ptr(qweight), _ptr(scales),
+                                         _ptr(qzeros), _stream(stream)), "moe_quantize_weights_w4")
+
+
+def moe_w4a16_forward(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales, w2_qzeros,
+                      group_size, topk_w, topk_ids, out, workspace, block_m: int = 0, stream=None):
+    T, H = x.shape
+    E, N2, _ = w13_qweight.shape
+    I = N2 // 2
+    k = topk_ids.shape[1]
+    _need(w13_qweight, torch.int32, (E, 2 * I, H // 8), "w13_qweight")
+    _need(w13_scales, torch.float16, (E, 2 * I, H // group_size), "w13_scales")
+    _need(w13_qzeros, torch.int32, (E, 2 * I // 8, H // group_size), "w13_qzeros")
+    _need(w2_qweight, torch.int32, (E, H, I // 8), "w2_qweight")
+    _need(w2_scales, torch.float16, (E, H, I // group_size), "w2_scales")
+    _need(w2_qzeros, torch.int32, (E, H // 8, I // group_size), "w2_qzeros")
+    _need(out, x.dtype, (T, H), "out")
+    _check(lib().moe_w4a16_forward(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13_qweight), _ptr(w13_scales),
+                                   _ptr(w13_qzeros), _ptr(w2_qweight), _ptr(w2_scales), _ptr(w2_qzeros),
+                                   group_size, _ptr(topk_w), _ptr(topk_ids), block_m, _ptr(out),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "moe_w4a16_forward")

@@ -1,0 +1,137 @@
+// Token -> expert align: histogram, prefix scan, padded-block permutation.
+//
+// The pages only call the fused expert kernel that consumes this grouping
+// (experts_int8 page, ExpertsInt8MoEMethod.apply); the definition is in
+// moe_wq.h.  One workgroup of 8 waves does all of it, with no atomics on
+// positions, so the result is the unique stable order:
+//   1. histogram of valid ids (LDS integer atomics: counts are order free);
+//   2. wave 0 scans the padded counts into block offsets and writes the
+//      block -> expert table; all threads write the padding sentinels;
+//   3. the flat indices are walked in chunks of 512; inside a wave, lanes
+//      with the same expert find each other with ballots over the id bits
+//      (their rank is a popcount of the lower lanes), per-wave counts go to
+//      LDS, and each element's slot is off[e] + done[e] + (counts of earlier
+//      waves of the chunk) + rank.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kAlignWaves = 8;
+constexpr int kAlignThreads = kAlignWaves * kWave;
+constexpr int kMaxExperts = 1024;
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int64_t Tk, int E, int bm, int64_t cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int off[kMaxExperts];
+  __shared__ int done[kMaxExperts];
+  __shared__ int wc[kAlignWaves][kMaxExperts];
+  __shared__ int total_padded;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int sentinel = static_cast<int>(Tk);
+
+  for (int e = tid; e < E; e += kAlignThreads) {
+    cnt[e] = 0;
+    done[e] = 0;
+  }
+  __syncthreads();
+
+  // 1. histogram
+  for (int64_t f = tid; f < Tk; f += kAlignThreads) {
+    const int e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // 2. exclusive scan of padded counts (wave 0, 64 experts per step)
+  if (wave == 0) {
+    int carry = 0;
+    for (int base = 0; base < E; base += kWave) {
+      const int e = base + lane;
+      const int c = (e < E) ? cnt[e] : 0;
+      const int p = (c + bm - 1) / bm * bm;
+      int incl = p;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += n;
+      }
+      if (e < E) off[e] = carry + incl - p;
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+      total_padded = carry;
+      *num_padded = carry;
+    }
+  }
+  __syncthreads();
+
+  const int used = total_padded;
+  // block -> expert table and sentinels inside each expert's last block
+  for (int e = tid; e < E; e += kAlignThreads) {
+    const int c = cnt[e];
+    const int p = (c + bm - 1) / bm * bm;
+    for (int b = off[e] / bm; b < (off[e] + p) / bm; ++b) block_expert[b] = e;
+    for (int r = off[e] + c; r < off[e] + p; ++r) sorted_ids[r] = sentinel;
+  }
+  // unused blocks / rows
+  for (int64_t b = used / bm + tid; b < cap / bm; b += kAlignThreads) block_expert[b] = -1;
+  for (int64_t r = used + tid; r < cap; r += kAlignThreads) sorted_ids[r] = sentinel;
+
+  // 3. stable scatter
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int64_t c0 = 0; c0 < Tk; c0 += kAlignThreads) {
+    for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wc[i / E][i % E] = 0;
+    __syncthreads();
+    const int64_t f = c0 + tid;
+    int e = -1;
+    if (f < Tk) {
+      e = ids[f];
+      if (e < 0 || e >= E) e = -1;
+    }
+    const bool active = (e >= 0);
+    uint64_t mask = __ballot(active);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = active && ((e >> b) & 1);
+      const uint64_t bal = __ballot(bit);
+      mask &= bit ? bal : ~bal;
+    }
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int rank = __popcll(mask & lower);
+    if (active && rank == 0) wc[wave][e] = __popcll(mask);
+    __syncthreads();
+    if (active) {
+      int pos = off[e] + done[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wc[w][e];
+      sorted_ids[pos] = static_cast<int32_t>(f);
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kAlignThreads) {
+      int s = 0;
+      for (int w = 0; w < kAlignWaves; ++w) s += wc[w][x];
+      done[x] += s;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_align(const int32_t* topk_ids, int64_t Tk, int E, int block_m, int64_t cap,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, topk_ids, Tk, E,
+                     block_m, cap, sorted_ids, block_expert, num_padded);
+  return hipGetLastError();
+}
+
+}  // namespace moe

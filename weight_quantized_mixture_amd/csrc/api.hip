@@ -1,0 +1,388 @@
+// C ABI of the MoE library: argument checks, workspace layout and the launch
+// sequence.  Every check runs on the host before anything is enqueued, so an
+// error leaves the stream untouched (the pages raise ValueError for a bad
+// shard or bit width and NotImplementedError for unsupported features:
+// experts_int8 page, quantizing_weight_loader and apply; moe_wna16 page,
+// MoeWNA16Method.__init__).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe_wq.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxExperts = 1024;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+int64_t capacity(int64_t T, int64_t k, int64_t E, int64_t bm) {
+  const int64_t tk = T * k;
+  if (tk <= 0 || bm <= 0) return 0;
+  const int64_t ne = E < tk ? E : tk;
+  return (tk + ne * (bm - 1)) / bm * bm;
+}
+
+int64_t auto_block_m(int64_t T, int64_t E, int64_t k) {
+  const int64_t avg = (T * k + E - 1) / E;
+  if (avg <= 8) return 16;
+  if (avg <= 24) return 32;
+  return 64;
+}
+
+// Split count of GEMM2's K = I range: enough workgroups to cover the chip
+// (about 1024), equal parts of whole 128-wide steps.
+int64_t auto_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
+  const int64_t tk = T * k;
+  const int64_t ne = E < tk ? E : tk;
+  const int64_t blocks_est = (tk + ne * (bm - 1) / 2) / bm + 1;
+  const int64_t ntiles = H / 128;
+  const int64_t steps = I / 128;
+  int64_t want = 1;
+  while (ntiles * blocks_est * want < 1024 && want < 64) want *= 2;
+  int64_t best = 1;
+  for (int64_t s = 1; s <= want && s <= steps; ++s)
+    if (steps % s == 0) best = s;
+  return best;
+}
+
+struct Layout {
+  int64_t cap, nblocks, splits;
+  size_t off_sorted, off_block, off_npad, off_a, off_y, total;
+};
+
+Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, int64_t splits) {
+  Layout L{};
+  L.cap = capacity(T, k, E, bm);
+  L.nblocks = bm > 0 ? L.cap / bm : 0;
+  L.splits = splits;
+  size_t o = 0;
+  L.off_sorted = o; o += align_up(static_cast<size_t>(L.cap) * 4);
+  L.off_block = o;  o += align_up(static_cast<size_t>(L.nblocks) * 4);
+  L.off_npad = o;   o += align_up(4);
+  L.off_a = o;      o += align_up(static_cast<size_t>(L.cap) * static_cast<size_t>(I) * 4);
+  L.off_y = o;      o += align_up(static_cast<size_t>(splits) * static_cast<size_t>(T * k) *
+                                  static_cast<size_t>(H) * 4);
+  L.total = o;
+  return L;
+}
+
+int check_block_m(int64_t bm) {
+  if (bm < 16 || bm > 256 || bm % 16 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "block_m must be a multiple of 16 in [16, 256], got %lld",
+                static_cast<long long>(bm));
+  return MOE_OK;
+}
+
+int check_layer_dims(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T must be >= 0");
+  if (H < 1 || I < 1 || E < 1 || k < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "H, I, E and k must be >= 1");
+  if (k > E) return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) > E (%lld)", (long long)k, (long long)E);
+  if (E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E > %lld", (long long)kMaxExperts);
+  if (H % 128 != 0 || I % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "H (%lld) and I (%lld) must be multiples of 128",
+                (long long)H, (long long)I);
+  return MOE_OK;
+}
+
+int check_act(int act) {
+  if (act != MOE_BF16 && act != MOE_FP16)
+    return fail(MOE_ERR_UNSUPPORTED, "act_dtype %d is neither MOE_BF16 nor MOE_FP16", act);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_UNKNOWN_STATUS";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_quantize_weights_int8(const float* w, int64_t E, int64_t N, int64_t K, int8_t* q,
+                              float* scale, hipStream_t stream) {
+  if (E < 1 || N < 1 || K < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "E, N and K must be >= 1");
+  if (!w || !q || !scale) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_quantize_int8(w, E * N, K, q, scale, stream), "quantize_int8");
+}
+
+int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t k, int renormalize,
+                   float* topk_w, int32_t* topk_ids, hipStream_t stream) {
+  if (T < 0 || E < 1 || k < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "need T >= 0, E >= 1, k >= 1");
+  if (k > E) return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) > E (%lld)", (long long)k, (long long)E);
+  if (E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E > %lld", (long long)kMaxExperts);
+  if (T == 0) return ok();
+  if (!logits || !topk_w || !topk_ids) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_route(logits, T, static_cast<int>(E), static_cast<int>(k),
+                                      renormalize, topk_w, topk_ids, stream),
+                    "route_topk");
+}
+
+int64_t moe_align_capacity(int64_t T, int64_t k, int64_t E, int64_t block_m) {
+  if (T < 0 || k < 1 || E < 1 || block_m < 1) return 0;
+  return capacity(T, k, E, block_m);
+}
+
+int moe_align_block(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int64_t block_m,
+                    int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                    hipStream_t stream) {
+  if (T < 0 || k < 1 || E < 1 || block_m < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need T >= 0, k >= 1, E >= 1, block_m >= 1");
+  if (E > kMaxExperts || block_m > 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "E or block_m above 1024");
+  if (!num_padded) return fail(MOE_ERR_INVALID_ARGUMENT, "null num_padded");
+  const int64_t tk = T * k;
+  if (tk > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^31-1");
+  if (tk == 0)   // the kernel with no assignments only writes *num_padded = 0
+    return hip_status(moe::launch_align(topk_ids, 0, static_cast<int>(E), static_cast<int>(block_m), 0,
+                                        sorted_ids, block_expert, num_padded, stream),
+                      "align");
+  if (!topk_ids || !sorted_ids || !block_expert) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  const int64_t cap = capacity(T, k, E, block_m);
+  return hip_status(moe::launch_align(topk_ids, tk, static_cast<int>(E), static_cast<int>(block_m), cap,
+                                      sorted_ids, block_expert, num_padded, stream),
+                    "align");
+}
+
+int64_t moe_w8a16_block_m(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  (void)H;
+  (void)I;
+  if (T < 0 || E < 1 || k < 1) return 16;
+  return auto_block_m(T, E, k);
+}
+
+int64_t moe_w8a16_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m) {
+  if (T <= 0 || H < 128 || I < 128 || E < 1 || k < 1) return 1;
+  if (block_m == 0) block_m = auto_block_m(T, E, k);
+  return auto_splits(T, H, I, E, k, block_m);
+}
+
+size_t moe_w8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                                 int64_t block_m) {
+  if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
+  if (block_m == 0) block_m = auto_block_m(T, E, k);
+  return layout(T, H, I, E, k, block_m, auto_splits(T, H, I, E, k, block_m)).total;
+}
+
+int moe_w8a16_gemm1(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
+                    int64_t k, const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                    const int32_t* sorted_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, int64_t block_m, float* a, hipStream_t stream) {
+  int st;
+  if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
+  if ((st = check_act(act_dtype)) != MOE_OK) return st;
+  if ((st = check_block_m(block_m)) != MOE_OK) return st;
+  const int64_t ldw = w13_row_stride ? w13_row_stride : H;
+  if (ldw < H || ldw % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "w13_row_stride must be >= H and a multiple of 16");
+  if (T == 0) return ok();
+  if (!x || !w13 || !w13_scale || !sorted_ids || !block_expert || !num_padded || !a)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(a, 16))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x, w13 and a must be 16-byte aligned");
+  moe::Gemm1Args p{};
+  p.x = x; p.f16 = act_dtype == MOE_FP16; p.T = T; p.H = H; p.I = I; p.k = k; p.Tk = T * k;
+  p.w13 = w13; p.s13 = w13_scale; p.ldw = ldw;
+  p.sorted_ids = sorted_ids; p.block_expert = block_expert; p.num_padded = num_padded;
+  p.block_m = static_cast<int>(block_m); p.cap = capacity(T, k, E, block_m); p.a = a;
+  return hip_status(moe::launch_gemm1_w8(p, stream), "gemm1_w8");
+}
+
+int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                    const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                    const int32_t* sorted_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, int64_t block_m, int64_t splits, float* y,
+                    hipStream_t stream) {
+  int st;
+  if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
+  if ((st = check_block_m(block_m)) != MOE_OK) return st;
+  const int64_t ldw = w2_row_stride ? w2_row_stride : I;
+  if (ldw < I || ldw % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "w2_row_stride must be >= I and a multiple of 16");
+  if (splits < 1 || (I / 128) % splits != 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "splits must divide I/128");
+  if (T == 0) return ok();
+  if (!a || !w2 || !w2_scale || !sorted_ids || !block_expert || !num_padded || !y)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(a, 16) || !aligned(w2, 16)) return fail(MOE_ERR_INVALID_ARGUMENT, "a and w2 must be 16-byte aligned");
+  moe::Gemm2Args p{};
+  p.a = a; p.H = H; p.I = I; p.Tk = T * k; p.w2 = w2; p.s2 = w2_scale; p.ldw = ldw;
+  p.sorted_ids = sorted_ids; p.block_expert = block_expert; p.num_padded = num_padded;
+  p.block_m = static_cast<int>(block_m); p.cap = capacity(T, k, E, block_m);
+  p.splits = static_cast<int>(splits); p.y = y;
+  return hip_status(moe::launch_gemm2_w8(p, stream), "gemm2_w8");
+}
+
+int moe_combine_topk(const float* y, int64_t splits, int64_t T, int64_t k, int64_t H, int64_t E,
+                     const float* topk_w, const int32_t* topk_ids, int act_dtype, void* out,
+                     hipStream_t stream) {
+  int st;
+  if ((st = check_act(act_dtype)) != MOE_OK) return st;
+  if (T < 0 || k < 1 || H < 1 || E < 1 || splits < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need T >= 0 and k, H, E, splits >= 1");
+  if (H % 4) return fail(MOE_ERR_INVALID_ARGUMENT, "H must be a multiple of 4");
+  if (T == 0) return ok();
+  if (!y || !topk_w || !topk_ids || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(y, 16) || !aligned(out, 8)) return fail(MOE_ERR_INVALID_ARGUMENT, "y / out misaligned");
+  return hip_status(moe::launch_combine(y, static_cast<int>(splits), T, static_cast<int>(k), H,
+                                        static_cast<int>(E), topk_w, topk_ids,
+                                        act_dtype == MOE_FP16, out, stream),
+                    "combine");
+}
+
+int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
+                      int64_t k, const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                      const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                      const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
+  if ((st = check_act(act_dtype)) != MOE_OK) return st;
+  if (block_m == 0) block_m = auto_block_m(T, E, k);
+  if ((st = check_block_m(block_m)) != MOE_OK) return st;
+  const int64_t ld13 = w13_row_stride ? w13_row_stride : H;
+  const int64_t ld2 = w2_row_stride ? w2_row_stride : I;
+  if (ld13 < H || ld13 % 16 || ld2 < I || ld2 % 16)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "row strides must cover the row and be multiples of 16");
+  if (T == 0) return ok();
+  if (T * k > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^31-1");
+  if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !topk_w || !topk_ids || !out || !workspace)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 8) ||
+      !aligned(workspace, kAlign))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x, w13, w2 16-byte, out 8-byte, workspace 256-byte alignment required");
+  const int64_t splits = auto_splits(T, H, I, E, k, block_m);
+  const Layout L = layout(T, H, I, E, k, block_m, splits);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.off_sorted);
+  int32_t* blocks = reinterpret_cast<int32_t*>(ws + L.off_block);
+  int32_t* npad = reinterpret_cast<int32_t*>(ws + L.off_npad);
+  float* a = reinterpret_cast<float*>(ws + L.off_a);
+  float* y = reinterpret_cast<float*>(ws + L.off_y);
+  hipError_t e = moe::launch_align(topk_ids, T * k, static_cast<int>(E), static_cast<int>(block_m), L.cap,
+                                   sorted, blocks, npad, stream);
+  if (e != hipSuccess) return hip_status(e, "align");
+  moe::Gemm1Args p1{};
+  p1.x = x; p1.f16 = act_dtype == MOE_FP16; p1.T = T; p1.H = H; p1.I = I; p1.k = k; p1.Tk = T * k;
+  p1.w13 = w13; p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = sorted; p1.block_expert = blocks;
+  p1.num_padded = npad; p1.block_m = static_cast<int>(block_m); p1.cap = L.cap; p1.a = a;
+  if ((e = moe::launch_gemm1_w8(p1, stream)) != hipSuccess) return hip_status(e, "gemm1_w8");
+  moe::Gemm2Args p2{};
+  p2.a = a; p2.H = H; p2.I = I; p2.Tk = T * k; p2.w2 = w2; p2.s2 = w2_scale; p2.ldw = ld2;
+  p2.sorted_ids = sorted; p2.block_expert = blocks; p2.num_padded = npad;
+  p2.block_m = static_cast<int>(block_m); p2.cap = L.cap; p2.splits = static_cast<int>(splits); p2.y = y;
+  if ((e = moe::launch_gemm2_w8(p2, stream)) != hipSuccess) return hip_status(e, "gemm2_w8");
+  return hip_status(moe::launch_combine(y, static_cast<int>(splits), T, static_cast<int>(k), H,
+                                        static_cast<int>(E), topk_w, topk_ids, act_dtype == MOE_FP16,
+                                        out, stream),
+                    "combine");
+}
+
+// ---------------------------------------------------------------------------
+// W4A16
+// ---------------------------------------------------------------------------
+
+int moe_quantize_weights_w4(const float* w, int64_t E, int64_t N, int64_t K, int64_t group_size,
+                            int32_t* qweight, uint16_t* scales, int32_t* qzeros, hipStream_t stream) {
+  if (E < 1 || N < 1 || K < 1 || group_size < 8)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "E, N, K >= 1 and group_size >= 8 required");
+  if (N % 8 || group_size % 8 || K % group_size)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need N %% 8 == 0, group_size %% 8 == 0, K %% group_size == 0");
+  if (!w || !qweight || !scales || !qzeros) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_quantize_w4(w, E, N, K, group_size, qweight, scales, qzeros, stream),
+                    "quantize_w4");
+}
+
+size_t moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                                 int64_t block_m) {
+  return moe_w8a16_workspace_bytes(T, H, I, E, k, block_m);
+}
+
+int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
+                      int64_t k, const int32_t* w13_qweight, const uint16_t* w13_scales,
+                      const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                      const uint16_t* w2_scales, const int32_t* w2_qzeros, int64_t group_size,
+                      const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
+  if ((st = check_act(act_dtype)) != MOE_OK) return st;
+  if (group_size < 128 || group_size % 128 || H % group_size || I % group_size)
+    return fail(MOE_ERR_UNSUPPORTED, "group_size must be a multiple of 128 dividing H and I (got %lld)",
+                (long long)group_size);
+  if (block_m == 0) block_m = auto_block_m(T, E, k);
+  if ((st = check_block_m(block_m)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (T * k > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^31-1");
+  if (!x || !w13_qweight || !w13_scales || !w13_qzeros || !w2_qweight || !w2_scales || !w2_qzeros ||
+      !topk_w || !topk_ids || !out || !workspace)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(x, 16) || !aligned(w13_qweight, 16) || !aligned(w2_qweight, 16) || !aligned(out, 8) ||
+      !aligned(workspace, kAlign))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "alignment: x and qweights 16 bytes, out 8, workspace 256");
+  const int64_t splits = auto_splits(T, H, I, E, k, block_m);
+  const Layout L = layout(T, H, I, E, k, block_m, splits);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.off_sorted);
+  int32_t* blocks = reinterpret_cast<int32_t*>(ws + L.off_block);
+  int32_t* npad = reinterpret_cast<int32_t*>(ws + L.off_npad);
+  float* a = reinterpret_cast<float*>(ws + L.off_a);
+  float* y = reinterpret_cast<float*>(ws + L.off_y);
+  hipError_t e = moe::launch_align(topk_ids, T * k, static_cast<int>(E), static_cast<int>(block_m), L.cap,
+                                   sorted, blocks, npad, stream);
+  if (e != hipSuccess) return hip_status(e, "align");
+  moe::Gemm1W4Args p1{};
+  p1.x = x; p1.f16 = act_dtype == MOE_FP16; p1.T = T; p1.H = H; p1.I = I; p1.k = k; p1.Tk = T * k;
+  p1.qw = w13_qweight; p1.sc = w13_scales; p1.qz = w13_qzeros; p1.group = static_cast<int>(group_size);
+  p1.sorted_ids = sorted; p1.block_expert = blocks; p1.num_padded = npad;
+  p1.block_m = static_cast<int>(block_m); p1.cap = L.cap; p1.a = a;
+  if ((e = moe::launch_gemm1_w4(p1, stream)) != hipSuccess) return hip_status(e, "gemm1_w4");
+  moe::Gemm2W4Args p2{};
+  p2.a = a; p2.f16 = act_dtype == MOE_FP16; p2.H = H; p2.I = I; p2.Tk = T * k;
+  p2.qw = w2_qweight; p2.sc = w2_scales; p2.qz = w2_qzeros; p2.group = static_cast<int>(group_size);
+  p2.sorted_ids = sorted; p2.block_expert = blocks; p2.num_padded = npad;
+  p2.block_m = static_cast<int>(block_m); p2.cap = L.cap; p2.splits = static_cast<int>(splits); p2.y = y;
+  if ((e = moe::launch_gemm2_w4(p2, stream)) != hipSuccess) return hip_status(e, "gemm2_w4");
+  return hip_status(moe::launch_combine(y, static_cast<int>(splits), T, static_cast<int>(k), H,
+                                        static_cast<int>(E), topk_w, topk_ids, act_dtype == MOE_FP16,
+                                        out, stream),
+                    "combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Routing-weighted top-k combine (experts_int8 page, ExpertsInt8MoEMethod.apply:
+// fused_experts with apply_router_weight_on_input=False, so the routing weight
+// multiplies each expert's output; inplace=True lets `out` be the input buffer).
+//
+// out[t, h] = sum_j topk_w[t, j] * sum_s y[s, t*k + j, h], fp32, j and s
+// ascending, one writer per output element (no atomics: bitwise deterministic),
+// then rounded to the activation type.  Each thread owns 4 consecutive h.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+template <bool F16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int splits,
+                                                      int64_t T, int k, int64_t H, int E,
+                                                      const float* __restrict__ topk_w,
+                                                      const int32_t* __restrict__ topk_ids,
+                                                      void* __restrict__ out) {
+  const int64_t H4 = H / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= T * H4) return;
+  const int64_t t = idx / H4;
+  const int64_t h = (idx % H4) * 4;
+  const int64_t Tk = T * k;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int64_t f = t * k + j;
+    const int e = topk_ids[f];
+    if (e < 0 || e >= E) continue;
+    const float wj = topk_w[f];
+    float4 ys = *reinterpret_cast<const float4*>(y + f * H + h);
+    for (int s = 1; s < splits; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(y + (s * Tk + f) * H + h);
+      ys.x += v.x; ys.y += v.y; ys.z += v.z; ys.w += v.w;
+    }
+    acc.x += wj * ys.x; acc.y += wj * ys.y; acc.z += wj * ys.z; acc.w += wj * ys.w;
+  }
+  uint2 packed;
+  if constexpr (F16) {
+    packed.x = static_cast<uint32_t>(f32_to_f16(acc.x)) | (static_cast<uint32_t>(f32_to_f16(acc.y)) << 16);
+    packed.y = static_cast<uint32_t>(f32_to_f16(acc.z)) | (static_cast<uint32_t>(f32_to_f16(acc.w)) << 16);
+  } else {
+    packed.x = pack_bf16_rne(acc.x, acc.y);
+    packed.y = pack_bf16_rne(acc.z, acc.w);
+  }
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + t * H + h) = packed;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,
+                          const float* topk_w, const int32_t* topk_ids, int f16, void* out,
+                          hipStream_t stream) {
+  const int64_t n = T * (H / 4);
+  const int64_t blocks = (n + 255) / 256;
+  if (f16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       y, splits, T, k, H, E, topk_w, topk_ids, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       y, splits, T, k, H, E, topk_w, topk_ids, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,99 @@
+// Host-side launchers of the gfx950 kernels.  Arguments are validated by the
+// C-ABI layer before these are called; the launchers only shape the grids.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Per-row symmetric int8 quantizer over `rows` rows of K fp32 values.
+hipError_t launch_quantize_int8(const float* w, int64_t rows, int64_t K, int8_t* q, float* scale,
+                                hipStream_t stream);
+
+// Group-wise uint4 quantizer over E experts of [N, K].
+hipError_t launch_quantize_w4(const float* w, int64_t E, int64_t N, int64_t K, int64_t group,
+                              int32_t* qweight, uint16_t* scales, int32_t* qzeros,
+                              hipStream_t stream);
+
+// Softmax top-k router, one wave per token.
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renormalize,
+                        float* topk_w, int32_t* topk_ids, hipStream_t stream);
+
+// Padded-block align, one workgroup.
+hipError_t launch_align(const int32_t* topk_ids, int64_t Tk, int E, int block_m, int64_t cap,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                        hipStream_t stream);
+
+struct Gemm1Args {
+  const void* x;          // [T, H] bf16 / fp16
+  int f16;                // activation type is fp16
+  int64_t T, H, I, k, Tk;
+  const int8_t* w13;      // [E, 2I, ldw]
+  const float* s13;       // [E, 2I]
+  int64_t ldw;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  int block_m;
+  int64_t cap;
+  float* a;               // [cap, I]
+};
+hipError_t launch_gemm1_w8(const Gemm1Args& p, hipStream_t stream);
+
+struct Gemm2Args {
+  const float* a;         // [cap, I]
+  int64_t H, I, Tk;
+  const int8_t* w2;       // [E, H, ldw]
+  const float* s2;        // [E, H]
+  int64_t ldw;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  int block_m;
+  int64_t cap;
+  int splits;
+  float* y;               // [splits, Tk, H]
+};
+hipError_t launch_gemm2_w8(const Gemm2Args& p, hipStream_t stream);
+
+struct Gemm1W4Args {
+  const void* x;
+  int f16;
+  int64_t T, H, I, k, Tk;
+  const int32_t* qw;      // [E, 2I, H/8]
+  const uint16_t* sc;     // [E, 2I, H/g]
+  const int32_t* qz;      // [E, 2I/8, H/g]
+  int group;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  int block_m;
+  int64_t cap;
+  float* a;
+};
+hipError_t launch_gemm1_w4(const Gemm1W4Args& p, hipStream_t stream);
+
+struct Gemm2W4Args {
+  const float* a;
+  int f16;                // use the fp16 MFMA path (activations are fp16)
+  int64_t H, I, Tk;
+  const int32_t* qw;      // [E, H, I/8]
+  const uint16_t* sc;     // [E, H, I/g]
+  const int32_t* qz;      // [E, H/8, I/g]
+  int group;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  int block_m;
+  int64_t cap;
+  int splits;
+  float* y;
+};
+hipError_t launch_gemm2_w4(const Gemm2W4Args& p, hipStream_t stream);
+
+// Weighted top-k combine of the split partials.
+hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,
+                          const float* topk_w, const int32_t* topk_ids, int f16, void* out,
+                          hipStream_t stream);
+
+}  // namespace moe
