@@ -45,10 +45,14 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MB (3 times) and exit: the known "
+                         "byte count that scales the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--flush-mb", type=int, default=None,
-                    help="write this many MB between timed steps (outside the events) so the "
-                         "256 MB Infinity Cache does not serve the weights; default: 512 when the "
-                         "active weights are below 1 GB, else 0")
+                    help="read this many MB of other data between timed steps (outside the events) so "
+                         "the 256 MB Infinity Cache does not serve the weights; default: 512 when the "
+                         "active weights are below 1 GB, else 0.  A read, not a write: written lines "
+                         "would be written back to HBM during the next timed step")
     return ap.parse_args()
 
 
@@ -58,8 +62,8 @@ HEADLINE_T = {"tiny": 16, "mixtral_decode": 64, "mixtral_prefill": 4096, "fine_g
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the layer is data-parallel over tokens with no exchange; see the design notes).",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this library runs on a "
+              f"single GPU (the layer is data-parallel over tokens, with no exchange between GPUs).",
               file=sys.stderr, flush=True)
         sys.exit(2)
 
@@ -70,6 +74,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.calibrate_copy_mb:
+        n = args.calibrate_copy_mb << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+        return
     wl = synthetic.WORKLOADS[args.workload]
     T = args.tokens or HEADLINE_T[args.workload]
     E, k, H, I = wl.E, wl.k, wl.H, wl.I
@@ -134,7 +147,11 @@ def main():
     flush_mb = args.flush_mb
     if flush_mb is None:
         flush_mb = 512 if n_active * (per_expert_w13 + per_expert_w2) < (1 << 30) else 0
-    flush = torch.empty(flush_mb << 20, dtype=torch.uint8, device=dev) if flush_mb else None
+    flush = torch.ones(flush_mb << 18, dtype=torch.int32, device=dev) if flush_mb else None
+    flush_sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def evict():
+        torch.amax(flush, dim=0, out=flush_sink[0])
 
     # ---- warm-up -----------------------------------------------------------------
     for _ in range(args.warmup):
@@ -147,7 +164,7 @@ def main():
     wall0 = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
-            flush.fill_(i & 0xff)
+            evict()
         evs[i][0].record(stream)
         step()
         evs[i][1].record(stream)
@@ -172,7 +189,7 @@ def main():
         reps = max(5, min(args.steps, 20))
         for i in range(reps + 2):
             if flush is not None:
-                flush.fill_(i & 0xff)
+                evict()
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
             ev[0].record(stream)
             pkg.moe_route_topk(logits, k, wl.renormalize, tw, ti, stream)

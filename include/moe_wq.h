@@ -149,15 +149,20 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
  *
  * moe_w8a16_gemm1: for every padded row r < *num_padded with
  * f = sorted_ids[r] < T*k, t = f / k, e = block_expert[r / block_m]:
- *   a[r, i] = silu(h_i) * h_{I+i},  h_n = w13_scale[e,n] * sum_c x[t,c] w13[e,n,c]
- * Padding rows get a = 0.  a is device fp32 [cap, I], cap = moe_align_capacity.
+ *   v[r, i] = silu(h_i) * h_{I+i},  h_n = w13_scale[e,n] * sum_c x[t,c] w13[e,n,c]
+ * stored as two bf16 planes, hi = rne(v) and lo = rne(v - hi) (16
+ * significant bits): `a` is device bf16 [2, cap, I] (hi plane first) with
+ * cap = moe_align_capacity; passed as float* for 4-byte alignment.  Padding
+ * rows of a block that holds rows get v = 0; 16-row groups made only of
+ * padding may be left unwritten (GEMM2 never reads them).
  *
  * moe_w8a16_gemm2: for every valid padded row r (f = sorted_ids[r] < T*k),
  * split s < splits, h < H:
- *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} a[r, i] w2[e,h,i]
- * The K range [0, I) is cut into `splits` equal parts (I/splits a multiple
- * of 128).  y is device fp32 [splits, T*k, H]; rows of dropped ids are not
- * written.  moe_w8a16_splits gives the split count the forward uses.
+ *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} (hi + lo)[r, i] w2[e,h,i]
+ * The K range [0, I) is cut into `splits` parts of whole 128-wide steps
+ * (1 <= splits <= I/128; equal parts, so splits must divide I/128, when
+ * block_m > 64).  y is device fp32 [splits, T*k, H]; rows of dropped ids are
+ * not written.  moe_w8a16_splits gives the split count the forward uses.
  *
  * moe_combine_topk: out[t, h] = sum_j topk_w[t,j] * sum_s y[s, t*k+j, h]
  * over the j with topk_ids in [0, E), in fp32 with j and s ascending, cast
@@ -201,7 +206,7 @@ int moe_combine_topk(const float* y, int64_t splits, int64_t T, int64_t k, int64
  * of 128 and of g; g a multiple of 128 (MOE_ERR_UNSUPPORTED otherwise).
  * With fp16 activations the intermediate a is carried in fp16 (hi + lo
  * pair), so it must stay inside the fp16 range like the activations.
- * moe_w4a16_workspace_bytes equals moe_w8a16_workspace_bytes.
+ * Workspace: moe_w4a16_workspace_bytes (same regions as the int8 path).
  * ---------------------------------------------------------------------- */
 int moe_quantize_weights_w4(const float* w, int64_t E, int64_t N, int64_t K, int64_t group_size,
                             int32_t* qweight, uint16_t* scales, int32_t* qzeros,

@@ -9,6 +9,7 @@ import torch
 import oracle
 import weight_quantized_mixture_amd as pkg
 from weight_quantized_mixture_amd import synthetic
+from weight_quantized_mixture_amd.layer import padded_rows
 
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
 
@@ -30,11 +31,12 @@ def act_f64(bits, act):
 class W8Weights:
     """int8 expert weights quantized on the GPU (K1) and by the oracle, compared bit for bit."""
 
-    def __init__(self, E, H, I, master_fn):
+    def __init__(self, E, H, I, master_fn, pad=False):
         self.E, self.H, self.I = E, H, I
         self.w13 = torch.empty(E, 2 * I, H, dtype=torch.int8, device=DEV)
         self.s13 = torch.empty(E, 2 * I, dtype=torch.float32, device=DEV)
         self.w2 = torch.empty(E, H, I, dtype=torch.int8, device=DEV)
+        self.pad = pad
         self.s2 = torch.empty(E, H, dtype=torch.float32, device=DEV)
         self.q13 = np.empty((E, 2 * I, H), np.int8)
         self.hs13 = np.empty((E, 2 * I), np.float32)
@@ -57,6 +59,12 @@ class W8Weights:
                     and np.array_equal(self.w2[e].cpu().numpy(), self.q2[e])
                     and np.array_equal(self.s2[e].cpu().numpy().view(np.uint32), self.hs2[e].view(np.uint32))):
                 self.mismatch += 1
+        if pad:   # the row-padded layout the layer class allocates (same codes)
+            w13p = padded_rows(E, 2 * I, H, torch.int8, DEV)
+            w2p = padded_rows(E, H, I, torch.int8, DEV)
+            w13p.copy_(self.w13)
+            w2p.copy_(self.w2)
+            self.w13, self.w2 = w13p, w2p
 
 
 class W4Weights:
@@ -104,16 +112,16 @@ def workload_weights(wl: synthetic.Workload, seed: int = 0):
         fn = lambda which, e: synthetic.expert_master(wl, which, e, seed)  # noqa: E731
         log(f"[weights] quantizing {wl.name}-shaped experts E={wl.E} H={wl.H} I={wl.I} ({wl.weights})")
         if wl.weights == "w8":
-            _CACHE[key] = W8Weights(wl.E, wl.H, wl.I, fn)
+            _CACHE[key] = W8Weights(wl.E, wl.H, wl.I, fn, pad=True)
         else:
             _CACHE[key] = W4Weights(wl.E, wl.H, wl.I, wl.group_size, fn)
     return _CACHE[key]
 
 
-def small_w8(E, H, I, seed):
+def small_w8(E, H, I, seed, pad=False):
     fn = lambda which, e: synthetic.random_master((2 * I, H) if which == "w13" else (H, I),  # noqa: E731
                                                   seed * 1000 + e, tag=60 if which == "w13" else 61)
-    return W8Weights(E, H, I, fn)
+    return W8Weights(E, H, I, fn, pad=pad)
 
 
 def route_both(logits: np.ndarray, k: int, renormalize: bool = True):

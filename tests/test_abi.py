@@ -51,9 +51,10 @@ def test_heuristics():
     for (T, H, I, E, k) in [(1, 4096, 14336, 8, 2), (64, 4096, 14336, 8, 2), (4096, 4096, 14336, 8, 2),
                             (16, 2048, 1408, 64, 6), (256, 2048, 768, 128, 8), (16, 256, 512, 8, 2)]:
         bm = pkg.moe_w8a16_block_m(T, H, I, E, k)
-        assert bm % 16 == 0 and 16 <= bm <= 256
+        assert bm in (16, 32, 64)
         s = pkg.moe_w8a16_splits(T, H, I, E, k, 0)
-        assert s >= 1 and (I // 128) % s == 0
+        assert 1 <= s <= I // 128
+        assert (I // 128) % pkg.moe_w8a16_splits(T, H, I, E, k, 128) == 0     # tiled path: equal splits
         assert pkg.moe_w8a16_workspace_bytes(T, H, I, E, k, 0) > 0
     assert pkg.moe_w8a16_workspace_bytes(0, 4096, 14336, 8, 2, 0) == 0
 
@@ -107,8 +108,10 @@ def test_other_argument_errors():
     r = L.moe_w4a16_forward(p(FAKE), 1, 4, 256, 512, 8, 2, p(FAKE), p(FAKE), p(FAKE), p(FAKE), p(FAKE),
                             p(FAKE), 64, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), 1 << 40, None)
     assert r == B.MOE_ERR_UNSUPPORTED                       # group 64 not implemented by the forward
-    assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 16, 3,
-                             p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # 3 does not divide I/128
+    assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 16, 5,
+                             p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # more splits than 128-wide steps
+    assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 128, 3,
+                             p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # tiled kernels need equal splits
     assert L.moe_combine_topk(p(FAKE), 1, 4, 2, 256, 8, p(FAKE), p(FAKE), 5, p(FAKE), None) == B.MOE_ERR_UNSUPPORTED
 
 

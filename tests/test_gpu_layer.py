@@ -40,18 +40,19 @@ def test_tiny_workload():
     assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), "tiny T=16")
 
 
-@pytest.mark.parametrize("act,bm,T", [("bf16", 0, 37), ("fp16", 0, 37), ("bf16", 16, 5), ("bf16", 32, 61),
-                                      ("bf16", 64, 130), ("fp16", 48, 77), ("bf16", 128, 300)])
-def test_ragged_shapes(act, bm, T):
-    E, k, H, I = 8, 2, 384, 640
-    log(f"[layer] ragged act={act} bm={bm} T={T}")
-    W = small_w8(E, H, I, seed=7)
+@pytest.mark.parametrize("act,bm,T,pad", [("bf16", 0, 37, False), ("fp16", 0, 37, True), ("bf16", 16, 5, True),
+                                          ("bf16", 32, 61, False), ("bf16", 32, 61, True), ("bf16", 64, 130, True),
+                                          ("fp16", 48, 77, False), ("bf16", 128, 300, True), ("fp16", 64, 200, False)])
+def test_ragged_shapes(act, bm, T, pad):
+    E, k, H, I = 8, 2, 512, 1024
+    log(f"[layer] ragged act={act} bm={bm} T={T} padded_rows={pad}")
+    W = small_w8(E, H, I, seed=7, pad=pad)
     assert W.mismatch == 0
     xb = synthetic.random_activations(T, H, act, seed=T)
     logits = synthetic.random_logits(T, E, seed=T + 1)
     got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, act, logits, k, block_m=bm)
     _check_routing(ti, tw, ids_ref, w_ref)
-    assert_layer_close(got, ref_w8(W, xb, act, w_ref, ids_ref), f"ragged {act} bm={bm} T={T}")
+    assert_layer_close(got, ref_w8(W, xb, act, w_ref, ids_ref), f"ragged {act} bm={bm} T={T} pad={pad}")
 
 
 def test_edge_cases_routing_shapes():

@@ -108,6 +108,21 @@ def _act(t: torch.Tensor) -> int:
     raise NotImplementedError(f"activation dtype {t.dtype} (bf16 or fp16 only)")
 
 
+def _row_stride(t, dtype, shape, name) -> int:
+    """Weights may be row-padded views: [E, N, K] with strides (N*ld, ld, 1), ld >= K; returns ld."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    E, N, K = shape
+    ld = t.stride(1)
+    if t.stride(2) != 1 or ld < K or (E > 1 and t.stride(0) != N * ld):
+        raise ValueError(f"{name}: needs rows of stride >= K and experts of stride N*row_stride, got {t.stride()}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return ld
+
+
 def _need(t, dtype, shape, name):
     if t.dtype != dtype:
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
@@ -188,15 +203,15 @@ def moe_w8a16_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, wo
     T, H = x.shape
     E, _, I = _w8_shapes(w13, w2)
     k = topk_ids.shape[1]
-    _need(w13, torch.int8, (E, 2 * I, H), "w13")
+    ld13 = _row_stride(w13, torch.int8, (E, 2 * I, H), "w13")
     _need(w13_scale, torch.float32, (E, 2 * I), "w13_scale")
-    _need(w2, torch.int8, (E, H, I), "w2")
+    ld2 = _row_stride(w2, torch.int8, (E, H, I), "w2")
     _need(w2_scale, torch.float32, (E, H), "w2_scale")
     _need(topk_w, torch.float32, (T, k), "topk_w")
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
     _need(out, x.dtype, (T, H), "out")
-    _check(lib().moe_w8a16_forward(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), 0,
-                                   _ptr(w2), _ptr(w2_scale), 0, _ptr(topk_w), _ptr(topk_ids), block_m,
+    _check(lib().moe_w8a16_forward(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13,
+                                   _ptr(w2), _ptr(w2_scale), ld2, _ptr(topk_w), _ptr(topk_ids), block_m,
                                    _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "moe_w8a16_forward")
 
@@ -205,7 +220,8 @@ def moe_w8a16_gemm1(x, w13, w13_scale, sorted_ids, block_expert, num_padded, blo
     T, H = x.shape
     E, N2, _ = w13.shape
     I = N2 // 2
-    _check(lib().moe_w8a16_gemm1(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), 0,
+    ld13 = _row_stride(w13, torch.int8, (E, N2, H), "w13")
+    _check(lib().moe_w8a16_gemm1(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13,
                                  _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), block_m, _ptr(a),
                                  _stream(stream)), "moe_w8a16_gemm1")
 
@@ -213,7 +229,8 @@ def moe_w8a16_gemm1(x, w13, w13_scale, sorted_ids, block_expert, num_padded, blo
 def moe_w8a16_gemm2(a, T, k, w2, w2_scale, sorted_ids, block_expert, num_padded, block_m, splits, y,
                     stream=None):
     E, H, I = w2.shape
-    _check(lib().moe_w8a16_gemm2(_ptr(a), T, H, I, E, k, _ptr(w2), _ptr(w2_scale), 0, _ptr(sorted_ids),
+    ld2 = _row_stride(w2, torch.int8, (E, H, I), "w2")
+    _check(lib().moe_w8a16_gemm2(_ptr(a), T, H, I, E, k, _ptr(w2), _ptr(w2_scale), ld2, _ptr(sorted_ids),
                                  _ptr(block_expert), _ptr(num_padded), block_m, splits, _ptr(y),
                                  _stream(stream)), "moe_w8a16_gemm2")
 

@@ -6,6 +6,7 @@
 // MoeWNA16Method.__init__).
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 
 #include "../../include/moe_wq.h"
@@ -47,27 +48,114 @@ int64_t capacity(int64_t T, int64_t k, int64_t E, int64_t bm) {
   return (tk + ne * (bm - 1)) / bm * bm;
 }
 
+// Rows per align block.  Batches whose experts hold at most about 64 rows
+// take the weight-streaming kernels: the block (16, 32 or 64 rows) is sized
+// to cover the expected largest expert (mean + 3 sigma of a binomial count),
+// so each expert's weights are read once; larger loads take 64-row blocks of
+// the tiled kernels.
 int64_t auto_block_m(int64_t T, int64_t E, int64_t k) {
-  const int64_t avg = (T * k + E - 1) / E;
-  if (avg <= 8) return 16;
-  if (avg <= 24) return 32;
+  const double avg = static_cast<double>(T) * k / E;
+  const double need = avg + 3.0 * std::sqrt(avg) + 1.0;
+  if (need <= 16.0) return 16;
+  if (need <= 32.0) return 32;
   return 64;
 }
 
-// Split count of GEMM2's K = I range: enough workgroups to cover the chip
-// (about 1024), equal parts of whole 128-wide steps.
-int64_t auto_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
+bool use_stream(int64_t bm) { return bm <= 64; }
+
+// Rough count of align blocks that hold rows (the exact count stays on the device).
+int64_t blocks_estimate(int64_t T, int64_t E, int64_t k, int64_t bm) {
   const int64_t tk = T * k;
   const int64_t ne = E < tk ? E : tk;
-  const int64_t blocks_est = (tk + ne * (bm - 1) / 2) / bm + 1;
-  const int64_t ntiles = H / 128;
+  return (tk + bm - 1) / bm + ne / 2;
+}
+
+// ---- GEMM1 ----
+// Register-streaming kernel (blocks of 16 or 48 rows): K-ways inside the
+// workgroup until about 4096 waves keep every CU streaming.
+constexpr int64_t kTargetWaves = 4096;
+
+int gemm1_kways(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
+  const int64_t waves1 = (I / 16) * blocks_estimate(T, E, k, bm);
+  int kw = 1;
+  while (kw < 4 && waves1 * kw < kTargetWaves && H / 128 >= 2 * kw) kw *= 2;
+  return kw;
+}
+
+hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t stream) {
+  if (!use_stream(p.block_m)) return moe::launch_gemm1_w8(p, stream);
+  const int mt = p.block_m / 16;
+  if (mt == 2 && p.H % 256 == 0) return moe::launch_gemm1_w8_lds(p, 2, 1, stream);
+  if (mt == 4) return moe::launch_gemm1_w8_lds(p, 1, 1, stream);
+  return moe::launch_gemm1_w8_stream(p, gemm1_kways(T, p.H, p.I, E, p.k, p.block_m), stream);
+}
+
+// ---- GEMM2 ----
+// LDS kernel (blocks of 16, 32 or 64 rows): 4 or 2 column tiles per wave and
+// K cut into `splits` parts so that about 768 workgroups are in flight.
+bool gemm2_lds(int64_t bm) { return bm == 16 || bm == 32 || bm == 64; }
+
+int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
+  return (H / 256) * blocks_estimate(T, E, k, bm) >= 64 ? 4 : 2;
+}
+
+struct Gemm2Plan {
+  int64_t splits;
+  int kw;
+};
+
+Gemm2Plan gemm2_plan(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm,
+                     bool tiled = false) {
   const int64_t steps = I / 128;
-  int64_t want = 1;
-  while (ntiles * blocks_est * want < 1024 && want < 64) want *= 2;
-  int64_t best = 1;
-  for (int64_t s = 1; s <= want && s <= steps; ++s)
-    if (steps % s == 0) best = s;
-  return best;
+  const int64_t blocks = blocks_estimate(T, E, k, bm);
+  if (tiled || !use_stream(bm)) {
+    // tiled kernel: 128 columns x one split per workgroup, equal splits
+    const int64_t ntiles = H / 128;
+    int64_t want = 1;
+    while (ntiles * blocks * want < 1024 && want < 64) want *= 2;
+    int64_t best = 1;
+    for (int64_t sp = 1; sp <= want && sp <= steps; ++sp)
+      if (steps % sp == 0) best = sp;
+    return {best, 1};
+  }
+  if (gemm2_lds(bm)) {
+    const int64_t groups = (H / (64 * gemm2_nt(T, H, E, k, bm))) * blocks;
+    int64_t sp = 1;
+    while (sp * 2 <= 16 && sp * 2 <= steps && groups * sp * 2 <= 768) sp *= 2;
+    return {sp, 1};
+  }
+  // register-streaming kernel (blocks of 48 rows)
+  const int64_t waves1 = (H / 32) * blocks;
+  int64_t ways = 1;
+  while (ways < 32 && waves1 * ways < kTargetWaves && steps >= 2 * ways) ways *= 2;
+  const int kw = ways >= 4 ? 4 : static_cast<int>(ways);
+  return {ways / kw, kw};
+}
+
+int64_t splits_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
+  return gemm2_plan(T, H, I, E, k, bm).splits;
+}
+
+// The uint4 kernels cut K into equal parts of whole 128-wide steps.
+int64_t w4_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
+  return gemm2_plan(T, H, I, E, k, bm, true).splits;
+}
+
+// In-workgroup K ways of the register-streaming GEMM2 for a given split count.
+int gemm2_kw_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, int64_t splits) {
+  const Gemm2Plan pl = gemm2_plan(T, H, I, E, k, bm);
+  if (pl.splits == splits) return pl.kw;
+  const int64_t steps = I / 128;
+  int kw = 1;
+  while (kw < 4 && splits * kw * 2 <= steps) kw *= 2;
+  return kw;
+}
+
+hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, hipStream_t stream) {
+  if (!use_stream(p.block_m)) return moe::launch_gemm2_w8(p, stream);
+  if (gemm2_lds(p.block_m))
+    return moe::launch_gemm2_w8_lds(p, 1, gemm2_nt(T, p.H, E, k, p.block_m), stream);
+  return moe::launch_gemm2_w8_stream(p, gemm2_kw_for(T, p.H, p.I, E, k, p.block_m, p.splits), stream);
 }
 
 struct Layout {
@@ -188,14 +276,14 @@ int64_t moe_w8a16_block_m(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k)
 int64_t moe_w8a16_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m) {
   if (T <= 0 || H < 128 || I < 128 || E < 1 || k < 1) return 1;
   if (block_m == 0) block_m = auto_block_m(T, E, k);
-  return auto_splits(T, H, I, E, k, block_m);
+  return splits_for(T, H, I, E, k, block_m);
 }
 
 size_t moe_w8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                                  int64_t block_m) {
   if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
   if (block_m == 0) block_m = auto_block_m(T, E, k);
-  return layout(T, H, I, E, k, block_m, auto_splits(T, H, I, E, k, block_m)).total;
+  return layout(T, H, I, E, k, block_m, splits_for(T, H, I, E, k, block_m)).total;
 }
 
 int moe_w8a16_gemm1(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
@@ -218,7 +306,7 @@ int moe_w8a16_gemm1(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
   p.w13 = w13; p.s13 = w13_scale; p.ldw = ldw;
   p.sorted_ids = sorted_ids; p.block_expert = block_expert; p.num_padded = num_padded;
   p.block_m = static_cast<int>(block_m); p.cap = capacity(T, k, E, block_m); p.a = a;
-  return hip_status(moe::launch_gemm1_w8(p, stream), "gemm1_w8");
+  return hip_status(run_gemm1(p, T, E, stream), "gemm1_w8");
 }
 
 int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
@@ -231,8 +319,8 @@ int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, 
   if ((st = check_block_m(block_m)) != MOE_OK) return st;
   const int64_t ldw = w2_row_stride ? w2_row_stride : I;
   if (ldw < I || ldw % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "w2_row_stride must be >= I and a multiple of 16");
-  if (splits < 1 || (I / 128) % splits != 0)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "splits must divide I/128");
+  if (splits < 1 || splits > I / 128 || (!use_stream(block_m) && (I / 128) % splits != 0))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "splits must be in [1, I/128] (and divide I/128 when block_m > 64)");
   if (T == 0) return ok();
   if (!a || !w2 || !w2_scale || !sorted_ids || !block_expert || !num_padded || !y)
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
@@ -242,7 +330,7 @@ int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, 
   p.sorted_ids = sorted_ids; p.block_expert = block_expert; p.num_padded = num_padded;
   p.block_m = static_cast<int>(block_m); p.cap = capacity(T, k, E, block_m);
   p.splits = static_cast<int>(splits); p.y = y;
-  return hip_status(moe::launch_gemm2_w8(p, stream), "gemm2_w8");
+  return hip_status(run_gemm2(p, T, E, k, stream), "gemm2_w8");
 }
 
 int moe_combine_topk(const float* y, int64_t splits, int64_t T, int64_t k, int64_t H, int64_t E,
@@ -283,7 +371,7 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
   if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 8) ||
       !aligned(workspace, kAlign))
     return fail(MOE_ERR_INVALID_ARGUMENT, "x, w13, w2 16-byte, out 8-byte, workspace 256-byte alignment required");
-  const int64_t splits = auto_splits(T, H, I, E, k, block_m);
+  const int64_t splits = splits_for(T, H, I, E, k, block_m);
   const Layout L = layout(T, H, I, E, k, block_m, splits);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
@@ -300,12 +388,12 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
   p1.x = x; p1.f16 = act_dtype == MOE_FP16; p1.T = T; p1.H = H; p1.I = I; p1.k = k; p1.Tk = T * k;
   p1.w13 = w13; p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = sorted; p1.block_expert = blocks;
   p1.num_padded = npad; p1.block_m = static_cast<int>(block_m); p1.cap = L.cap; p1.a = a;
-  if ((e = moe::launch_gemm1_w8(p1, stream)) != hipSuccess) return hip_status(e, "gemm1_w8");
+  if ((e = run_gemm1(p1, T, E, stream)) != hipSuccess) return hip_status(e, "gemm1_w8");
   moe::Gemm2Args p2{};
   p2.a = a; p2.H = H; p2.I = I; p2.Tk = T * k; p2.w2 = w2; p2.s2 = w2_scale; p2.ldw = ld2;
   p2.sorted_ids = sorted; p2.block_expert = blocks; p2.num_padded = npad;
   p2.block_m = static_cast<int>(block_m); p2.cap = L.cap; p2.splits = static_cast<int>(splits); p2.y = y;
-  if ((e = moe::launch_gemm2_w8(p2, stream)) != hipSuccess) return hip_status(e, "gemm2_w8");
+  if ((e = run_gemm2(p2, T, E, k, stream)) != hipSuccess) return hip_status(e, "gemm2_w8");
   return hip_status(moe::launch_combine(y, static_cast<int>(splits), T, static_cast<int>(k), H,
                                         static_cast<int>(E), topk_w, topk_ids, act_dtype == MOE_FP16,
                                         out, stream),
@@ -329,7 +417,9 @@ int moe_quantize_weights_w4(const float* w, int64_t E, int64_t N, int64_t K, int
 
 size_t moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                                  int64_t block_m) {
-  return moe_w8a16_workspace_bytes(T, H, I, E, k, block_m);
+  if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
+  if (block_m == 0) block_m = auto_block_m(T, E, k);
+  return layout(T, H, I, E, k, block_m, w4_splits(T, H, I, E, k, block_m)).total;
 }
 
 int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
@@ -354,7 +444,7 @@ int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
   if (!aligned(x, 16) || !aligned(w13_qweight, 16) || !aligned(w2_qweight, 16) || !aligned(out, 8) ||
       !aligned(workspace, kAlign))
     return fail(MOE_ERR_INVALID_ARGUMENT, "alignment: x and qweights 16 bytes, out 8, workspace 256");
-  const int64_t splits = auto_splits(T, H, I, E, k, block_m);
+  const int64_t splits = w4_splits(T, H, I, E, k, block_m);
   const Layout L = layout(T, H, I, E, k, block_m, splits);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);

@@ -64,18 +64,18 @@ __device__ __forceinline__ void split_bf16x4(float4 v, u32x2& hi, u32x2& lo) {
 
 // ---- int8 -> 16-bit float, exact ----------------------------------------------
 
-// Four signed int8 codes in one dword -> four bf16 values (two dwords).
-// q + 128 is taken as an unsigned byte, converted to fp32, 128 subtracted
-// (exact), and the high halves packed (exact for |q| <= 128).
+// Four signed int8 codes in one dword -> four bf16 values (two dwords), exact:
+// each byte is sign-extended and converted to fp32 in one instruction
+// (v_cvt_f32_i32 with an SDWA byte select), and pairs are packed with
+// v_cvt_pk_bf16_f32 (integers |q| <= 128 are exact in bf16).
 __device__ __forceinline__ u32x2 i8x4_to_bf16x4(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
-  const float f0 = static_cast<float>(u & 0xffu) - 128.0f;
-  const float f1 = static_cast<float>((u >> 8) & 0xffu) - 128.0f;
-  const float f2 = static_cast<float>((u >> 16) & 0xffu) - 128.0f;
-  const float f3 = static_cast<float>(u >> 24) - 128.0f;
+  const float f0 = static_cast<float>(static_cast<int8_t>(w & 0xffu));
+  const float f1 = static_cast<float>(static_cast<int8_t>((w >> 8) & 0xffu));
+  const float f2 = static_cast<float>(static_cast<int8_t>((w >> 16) & 0xffu));
+  const float f3 = static_cast<float>(static_cast<int32_t>(w) >> 24);
   u32x2 r;
-  r.x = pack_hi16(f0, f1);
-  r.y = pack_hi16(f2, f3);
+  r.x = pack_bf16_rne(f0, f1);
+  r.y = pack_bf16_rne(f2, f3);
   return r;
 }
 

@@ -8,7 +8,7 @@
 //          (gate rows 0..I-1 and up rows I..2I-1 of w13, quantizing_weight_loader);
 //   GEMM2: y = a * dequant(w2[e])^T, scale on the accumulator.
 //
-// Tiling (wave64, v_mfma_f32_16x16x32_{bf16,f16}):
+// Tiling for blocks of more than 64 rows (wave64, v_mfma_f32_16x16x32_{bf16,f16}):
 //   * a workgroup is 4 waves and one align block of block_m rows, walked in
 //     chunks of 16*MT rows; every lane of a wave owns one weight row (MFMA
 //     column l%16) and a 32-byte slice of K (l/16), so one wave reads 16 rows x
@@ -19,8 +19,9 @@
 //     leaves the dot products unchanged;
 //   * GEMM1: each wave owns 16 gate rows and the matching 16 up rows, so the
 //     SiLU-and-mul epilogue needs no data exchange;
-//   * GEMM2: a is fp32; it is split into bf16 hi + lo (16 significant bits)
-//     and both halves go through the MFMA with the same dequantized weights;
+//   * GEMM1 writes a as two bf16 planes, hi = rne(a) and lo = rne(a - hi)
+//     (16 significant bits); GEMM2 feeds both halves through the MFMA with
+//     the same dequantized weights;
 //     K is cut into `splits` ranges (grid z) whose partial sums the combine
 //     kernel adds in a fixed order.
 #include "common.hpp"
@@ -91,12 +92,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_w8_kernel(const Gemm1Args 
         }
       }
     }
+    uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.a);
+    uint16_t* a_lo = a_hi + p.cap * I;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t r = row0 + rc + mt * 16 + kg * 4 + i;
-        p.a[r * I + n0 + col] = silu_mul(accg[mt][i] * sg, accu[mt][i] * su);
+        const float v = silu_mul(accg[mt][i] * sg, accu[mt][i] * su);
+        const uint32_t hi = pack_bf16_rne(v, 0.0f) & 0xffffu;
+        const uint32_t lo = pack_bf16_rne(v - __uint_as_float(hi << 16), 0.0f) & 0xffffu;
+        a_hi[r * I + n0 + col] = static_cast<uint16_t>(hi);
+        a_lo[r * I + n0 + col] = static_cast<uint16_t>(lo);
       }
     }
   }
@@ -121,10 +128,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_w8_kernel(const Gemm2Args 
   const float s0 = p.s2[static_cast<int64_t>(e) * H + h0 + col];
   const float s1 = p.s2[static_cast<int64_t>(e) * H + h0 + 16 + col];
 
+  const uint16_t* a_hi = reinterpret_cast<const uint16_t*>(p.a);
+  const uint16_t* a_lo = a_hi + p.cap * I;
   for (int rc = 0; rc < p.block_m; rc += 16 * MT) {
-    const float* ar[MT];
+    int64_t ar[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) ar[mt] = p.a + (row0 + rc + mt * 16 + col) * I + kbeg + kg * 32;
+    for (int mt = 0; mt < MT; ++mt) ar[mt] = (row0 + rc + mt * 16 + col) * I + kbeg + kg * 32;
     f32x4 acc0[MT], acc1[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -145,13 +154,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_w8_kernel(const Gemm2Args 
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float4 v0 = *reinterpret_cast<const float4*>(ar[mt] + k0 + 8 * i);
-          const float4 v1 = *reinterpret_cast<const float4*>(ar[mt] + k0 + 8 * i + 4);
-          u32x2 h0v, l0v, h1v, l1v;
-          split_bf16x4(v0, h0v, l0v);
-          split_bf16x4(v1, h1v, l1v);
-          const u32x4 ahi = {h0v.x, h0v.y, h1v.x, h1v.y};
-          const u32x4 alo = {l0v.x, l0v.y, l1v.x, l1v.y};
+          const u32x4 ahi = *reinterpret_cast<const u32x4*>(a_hi + ar[mt] + k0 + 8 * i);
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(a_lo + ar[mt] + k0 + 8 * i);
           acc0[mt] = mfma16_bf16(ahi, b0[i], acc0[mt]);
           acc0[mt] = mfma16_bf16(alo, b0[i], acc0[mt]);
           acc1[mt] = mfma16_bf16(ahi, b1[i], acc1[mt]);

@@ -36,12 +36,14 @@ struct Gemm1Args {
   const int32_t* num_padded;
   int block_m;
   int64_t cap;
-  float* a;               // [cap, I]
+  float* a;               // int8 path: two bf16 planes [2, cap, I] (hi, lo); uint4 path: fp32 [cap, I]
 };
 hipError_t launch_gemm1_w8(const Gemm1Args& p, hipStream_t stream);
+// Weight-streaming variant for block_m <= 64; kw = K-ways inside a workgroup (1, 2, 4).
+hipError_t launch_gemm1_w8_stream(const Gemm1Args& p, int kw, hipStream_t stream);
 
 struct Gemm2Args {
-  const float* a;         // [cap, I]
+  const float* a;         // two bf16 planes [2, cap, I] written by GEMM1
   int64_t H, I, Tk;
   const int8_t* w2;       // [E, H, ldw]
   const float* s2;        // [E, H]
@@ -55,6 +57,11 @@ struct Gemm2Args {
   float* y;               // [splits, Tk, H]
 };
 hipError_t launch_gemm2_w8(const Gemm2Args& p, hipStream_t stream);
+hipError_t launch_gemm2_w8_stream(const Gemm2Args& p, int kw, hipStream_t stream);
+// LDS-staged variants: GEMM1 for blocks of 32 or 64 rows (kw <= 2 at 32, 1 at 64); GEMM2 for
+// blocks of 16, 32 or 64 rows (kw <= 2 at 16, else 1), nt = 16-column tiles per wave (2 or 4).
+hipError_t launch_gemm1_w8_lds(const Gemm1Args& p, int kw, int ng, hipStream_t stream);
+hipError_t launch_gemm2_w8_lds(const Gemm2Args& p, int kw, int nt, hipStream_t stream);
 
 struct Gemm1W4Args {
   const void* x;

@@ -18,6 +18,19 @@ import torch
 from . import binding as B
 
 
+def padded_rows(E: int, N: int, K: int, dtype, device) -> torch.Tensor:
+    """[E, N, K] view whose rows are padded by 256 bytes when a row is a multiple of 512 bytes.
+
+    Rows that start a multiple of 512 bytes apart fall on the same HBM channels when a wave
+    reads 16 of them at the same offset; the fp8 page pads such rows on ROCm for the same
+    reason (Fp8LinearMethod._maybe_pad_weight).  The library reads the row stride.
+    """
+    itemsize = torch.empty(0, dtype=dtype).element_size()
+    row_bytes = K * itemsize
+    ld = K + 256 // itemsize if row_bytes % 512 == 0 else K
+    return torch.empty(E, N, ld, dtype=dtype, device=device)[:, :, :K]
+
+
 class _Workspace:
     def __init__(self):
         self.buf = None
@@ -34,18 +47,20 @@ class W8A16MoE:
         E, H, I = num_experts, hidden_size, intermediate_size
         self.E, self.H, self.I = E, H, I
         self.params_dtype = params_dtype
-        self.w13_weight = torch.empty(E, 2 * I, H, dtype=torch.int8, device=device)
-        self.w2_weight = torch.empty(E, H, I, dtype=torch.int8, device=device)
+        self.w13_weight = padded_rows(E, 2 * I, H, torch.int8, device)
+        self.w2_weight = padded_rows(E, H, I, torch.int8, device)
         self.w13_scale = torch.zeros(E, 2 * I, dtype=torch.float32, device=device)
         self.w2_scale = torch.zeros(E, H, dtype=torch.float32, device=device)
         self._ws = _Workspace()
 
     def load_expert(self, e: int, w13_master: torch.Tensor, w2_master: torch.Tensor):
         """Quantize one expert's fp32 masters ([2I, H] gate then up, [H, I]) into the int8 parameters."""
-        B.moe_quantize_weights_int8(w13_master.reshape(1, 2 * self.I, self.H), self.w13_weight[e:e + 1],
-                                    self.w13_scale[e:e + 1])
-        B.moe_quantize_weights_int8(w2_master.reshape(1, self.H, self.I), self.w2_weight[e:e + 1],
-                                    self.w2_scale[e:e + 1])
+        q = torch.empty(1, 2 * self.I, self.H, dtype=torch.int8, device=w13_master.device)
+        B.moe_quantize_weights_int8(w13_master.reshape(1, 2 * self.I, self.H), q, self.w13_scale[e:e + 1])
+        self.w13_weight[e].copy_(q[0])
+        q = torch.empty(1, self.H, self.I, dtype=torch.int8, device=w2_master.device)
+        B.moe_quantize_weights_int8(w2_master.reshape(1, self.H, self.I), q, self.w2_scale[e:e + 1])
+        self.w2_weight[e].copy_(q[0])
 
     def route(self, router_logits: torch.Tensor, top_k: int, renormalize: bool = True):
         T = router_logits.shape[0]
