@@ -151,7 +151,7 @@ def main():
     flush_sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def evict():
-        torch.amax(flush, dim=0, out=flush_sink[0])
+        torch.amax(flush, dim=0, keepdim=True, out=flush_sink)
 
     # ---- warm-up -----------------------------------------------------------------
     for _ in range(args.warmup):

@@ -42,7 +42,8 @@ def test_tiny_workload():
 
 @pytest.mark.parametrize("act,bm,T,pad", [("bf16", 0, 37, False), ("fp16", 0, 37, True), ("bf16", 16, 5, True),
                                           ("bf16", 32, 61, False), ("bf16", 32, 61, True), ("bf16", 64, 130, True),
-                                          ("fp16", 48, 77, False), ("bf16", 128, 300, True), ("fp16", 64, 200, False)])
+                                          ("fp16", 48, 77, False), ("bf16", 128, 300, True), ("fp16", 64, 200, False),
+                                          ("bf16", 256, 700, True), ("fp16", 256, 333, False), ("bf16", 256, 9, True)])
 def test_ragged_shapes(act, bm, T, pad):
     E, k, H, I = 8, 2, 512, 1024
     log(f"[layer] ragged act={act} bm={bm} T={T} padded_rows={pad}")

@@ -51,15 +51,18 @@ int64_t capacity(int64_t T, int64_t k, int64_t E, int64_t bm) {
 // Rows per align block.  Batches whose experts hold at most about 64 rows
 // take the weight-streaming kernels: the block (16, 32 or 64 rows) is sized
 // to cover the expected largest expert (mean + 3 sigma of a binomial count),
-// so each expert's weights are read once; larger loads take 64-row blocks of
-// the tiled kernels.
+// so each expert's weights are read once.  Experts with 128 rows or more on
+// average take 256-row blocks of the MFMA-tiled kernels.
 int64_t auto_block_m(int64_t T, int64_t E, int64_t k) {
   const double avg = static_cast<double>(T) * k / E;
+  if (avg >= 128.0) return 256;                 // MFMA-bound: large tiles
   const double need = avg + 3.0 * std::sqrt(avg) + 1.0;
   if (need <= 16.0) return 16;
   if (need <= 32.0) return 32;
   return 64;
 }
+
+bool use_prefill(int64_t bm) { return bm == 256; }
 
 bool use_stream(int64_t bm) { return bm <= 64; }
 
@@ -83,6 +86,7 @@ int gemm1_kways(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t b
 }
 
 hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t stream) {
+  if (use_prefill(p.block_m) && p.H % 64 == 0) return moe::launch_gemm1_w8_prefill(p, stream);
   if (!use_stream(p.block_m)) return moe::launch_gemm1_w8(p, stream);
   const int mt = p.block_m / 16;
   if (mt == 2 && p.H % 256 == 0) return moe::launch_gemm1_w8_lds(p, 2, 1, stream);
@@ -108,6 +112,7 @@ Gemm2Plan gemm2_plan(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int6
                      bool tiled = false) {
   const int64_t steps = I / 128;
   const int64_t blocks = blocks_estimate(T, E, k, bm);
+  if (!tiled && use_prefill(bm)) return {1, 1};
   if (tiled || !use_stream(bm)) {
     // tiled kernel: 128 columns x one split per workgroup, equal splits
     const int64_t ntiles = H / 128;
@@ -152,6 +157,7 @@ int gemm2_kw_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t 
 }
 
 hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, hipStream_t stream) {
+  if (use_prefill(p.block_m)) return moe::launch_gemm2_w8_prefill(p, stream);
   if (!use_stream(p.block_m)) return moe::launch_gemm2_w8(p, stream);
   if (gemm2_lds(p.block_m))
     return moe::launch_gemm2_w8_lds(p, 1, gemm2_nt(T, p.H, E, k, p.block_m), stream);
@@ -319,8 +325,10 @@ int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, 
   if ((st = check_block_m(block_m)) != MOE_OK) return st;
   const int64_t ldw = w2_row_stride ? w2_row_stride : I;
   if (ldw < I || ldw % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "w2_row_stride must be >= I and a multiple of 16");
-  if (splits < 1 || splits > I / 128 || (!use_stream(block_m) && (I / 128) % splits != 0))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "splits must be in [1, I/128] (and divide I/128 when block_m > 64)");
+  if (splits < 1 || splits > I / 128 || (!use_stream(block_m) && (I / 128) % splits != 0) ||
+      (use_prefill(block_m) && splits != 1))
+    return fail(MOE_ERR_INVALID_ARGUMENT,
+                "splits must be in [1, I/128], divide I/128 when block_m > 64, and be 1 when block_m is 256");
   if (T == 0) return ok();
   if (!a || !w2 || !w2_scale || !sorted_ids || !block_expert || !num_padded || !y)
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
