@@ -1,8 +1,8 @@
 """Benchmark of the weight-only-quantized MoE layer on one MI355X.
 
-One step = one layer call on one batch: softmax top-k routing, align,
-GEMM1 + SiLU-and-mul, GEMM2 and the weighted combine (moe_route_topk followed
-by moe_w8a16_forward / moe_w4a16_forward), inputs resident in HBM.  Weight
+One step = one layer call on one batch, from router logits to the output:
+softmax top-k routing, align, GEMM1 + SiLU-and-mul, GEMM2 and the weighted
+combine (moe_w8a16_apply / moe_w4a16_apply), inputs resident in HBM.  Weight
 quantization runs once at set-up and is not part of a step.
 
 Default workload: the Mixtral-shaped decode batch (E=8, top-2, H=4096,
@@ -115,13 +115,14 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        pkg.moe_route_topk(logits, k, wl.renormalize, tw, ti, stream)
+        # logits -> output in one library call (routing, align, GEMM1+SiLU, GEMM2, combine)
         if w4:
-            pkg.moe_w4a16_forward(x, layer.w13_qweight, layer.w13_scales, layer.w13_qzeros, layer.w2_qweight,
-                                  layer.w2_scales, layer.w2_qzeros, wl.group_size, tw, ti, out, ws, 0, stream)
+            pkg.moe_w4a16_apply(x, logits, wl.renormalize, layer.w13_qweight, layer.w13_scales, layer.w13_qzeros,
+                                layer.w2_qweight, layer.w2_scales, layer.w2_qzeros, wl.group_size, tw, ti, out, ws,
+                                0, stream)
         else:
-            pkg.moe_w8a16_forward(x, layer.w13_weight, layer.w13_scale, layer.w2_weight, layer.w2_scale,
-                                  tw, ti, out, ws, 0, stream)
+            pkg.moe_w8a16_apply(x, logits, wl.renormalize, layer.w13_weight, layer.w13_scale, layer.w2_weight,
+                                layer.w2_scale, tw, ti, out, ws, 0, stream)
 
     step()
     torch.cuda.synchronize()

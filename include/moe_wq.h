@@ -143,6 +143,21 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Routing + forward in one call, from router logits (the moe_wna16 page's
+ * MoeWNA16Method.apply_monolithic form: the layer takes router_logits and
+ * routes itself).  Same result as moe_route_topk followed by
+ * moe_w8a16_forward; for T <= 16 one workgroup routes and aligns, which
+ * saves a launch.  topk_w / topk_ids (device fp32 / int32 [T, k]) receive
+ * the routing.  Arguments and errors as moe_route_topk + moe_w8a16_forward.
+ * ---------------------------------------------------------------------- */
+int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                    const float* router_logits, int renormalize,
+                    const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                    const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                    float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Stages of the forward, exported so that each kernel can be checked and
  * timed alone.  moe_w8a16_forward is exactly moe_align_block followed by
  * these three calls on the workspace regions.
@@ -221,6 +236,14 @@ int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
                       const int32_t* w2_qzeros, int64_t group_size,
                       const float* topk_w, const int32_t* topk_ids, int64_t block_m,
                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* moe_w4a16_forward with routing from logits (see moe_w8a16_apply). */
+int moe_w4a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                    const float* router_logits, int renormalize,
+                    const int32_t* w13_qweight, const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                    const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros,
+                    int64_t group_size, float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

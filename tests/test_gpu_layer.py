@@ -175,3 +175,26 @@ def test_fine_grained(T):
     got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, wl.act, logits, wl.k)
     _check_routing(ti, tw, ids_ref, w_ref)
     assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), f"fine-grained T={T}")
+
+
+@pytest.mark.parametrize("T,E,k,act", [(1, 8, 2, "bf16"), (16, 64, 6, "fp16"), (37, 8, 2, "fp16"),
+                                       (300, 16, 4, "bf16")])
+def test_apply_from_logits_matches_route_then_forward(T, E, k, act):
+    """moe_w8a16_apply (routing fused with align up to 16 tokens) equals route + forward bit for bit."""
+    H, I = 256, 384
+    W = small_w8(E, H, I, seed=51, pad=True)
+    xb = synthetic.random_activations(T, H, act, seed=52)
+    logits = synthetic.random_logits(T, E, seed=53)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, act, logits, k)
+    x = to_dev_act(xb, act)
+    dl = torch.from_numpy(logits).to(DEV)
+    out = torch.empty_like(x)
+    tw2 = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    ti2 = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    ws = torch.empty(pkg.moe_w8a16_workspace_bytes(T, H, I, E, k, 0), dtype=torch.uint8, device=DEV)
+    pkg.moe_w8a16_apply(x, dl, True, W.w13, W.s13, W.w2, W.s2, tw2, ti2, out, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ti2.cpu().numpy(), ti)
+    np.testing.assert_array_equal(tw2.cpu().numpy(), tw)
+    assert np.array_equal(out.float().cpu().numpy().astype(np.float64), got)
+    assert_layer_close(got, ref_w8(W, xb, act, w_ref, ids_ref), f"apply T={T} E={E} k={k}")

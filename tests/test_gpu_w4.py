@@ -58,3 +58,23 @@ def test_w4a16_workload(T):
     logits = synthetic.router_logits(wl, T)
     got, ref = _run(W, xb, wl.act, logits, wl.k)
     assert_layer_close(got, ref, f"w4a16 T={T}")
+
+
+def test_w4_apply_from_logits():
+    E, k, H, I, g, T = 8, 3, 256, 384, 128, 33
+    fn = lambda which, e: synthetic.random_master((2 * I, H) if which == "w13" else (H, I),  # noqa: E731
+                                                  200 + e, tag=72 if which == "w13" else 73)
+    W = W4Weights(E, H, I, g, fn)
+    xb = synthetic.random_activations(T, H, "fp16", seed=5)
+    logits = synthetic.random_logits(T, E, seed=6)
+    got, ref = _run(W, xb, "fp16", logits, k)
+    x = to_dev_act(xb, "fp16")
+    out = torch.empty_like(x)
+    tw = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    ti = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    ws = torch.empty(pkg.moe_w4a16_workspace_bytes(T, H, I, E, k, 0), dtype=torch.uint8, device=DEV)
+    pkg.moe_w4a16_apply(x, torch.from_numpy(logits).to(DEV), True, W.qw13, W.sc13, W.qz13, W.qw2, W.sc2, W.qz2, g,
+                        tw, ti, out, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy().astype(np.float64), got)
+    assert_layer_close(got, ref, "w4 apply from logits")

@@ -15,8 +15,10 @@ from .binding import (  # noqa: F401
     moe_quantize_weights_int8,
     moe_quantize_weights_w4,
     moe_route_topk,
+    moe_w4a16_apply,
     moe_w4a16_forward,
     moe_w4a16_workspace_bytes,
+    moe_w8a16_apply,
     moe_w8a16_block_m,
     moe_w8a16_forward,
     moe_w8a16_gemm1,

@@ -40,6 +40,12 @@ SIGNATURES = {
     "moe_w8a16_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                    _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
                                    _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_w8a16_apply": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int,
+                                 _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                 _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_w4a16_apply": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int,
+                                 _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                 _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_w8a16_splits": (_c_i64, [_c_i64] * 6),
     "moe_w8a16_gemm1": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p]),
@@ -270,3 +276,46 @@ def moe_w4a16_forward(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_sca
                                    group_size, _ptr(topk_w), _ptr(topk_ids), block_m, _ptr(out),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "moe_w4a16_forward")
+
+
+def moe_w8a16_apply(x, router_logits, renormalize, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out,
+                    workspace, block_m: int = 0, stream=None):
+    """Route from logits and run the layer in one call; topk_w / topk_ids receive the routing."""
+    T, H = x.shape
+    E, _, I = _w8_shapes(w13, w2)
+    k = topk_ids.shape[1]
+    _need(router_logits, torch.float32, (T, E), "router_logits")
+    ld13 = _row_stride(w13, torch.int8, (E, 2 * I, H), "w13")
+    _need(w13_scale, torch.float32, (E, 2 * I), "w13_scale")
+    ld2 = _row_stride(w2, torch.int8, (E, H, I), "w2")
+    _need(w2_scale, torch.float32, (E, H), "w2_scale")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    _check(lib().moe_w8a16_apply(_ptr(x), _act(x), T, H, I, E, k, _ptr(router_logits), int(bool(renormalize)),
+                                 _ptr(w13), _ptr(w13_scale), ld13, _ptr(w2), _ptr(w2_scale), ld2, _ptr(topk_w),
+                                 _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)), "moe_w8a16_apply")
+
+
+def moe_w4a16_apply(x, router_logits, renormalize, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
+                    w2_qzeros, group_size, topk_w, topk_ids, out, workspace, block_m: int = 0, stream=None):
+    T, H = x.shape
+    E, N2, _ = w13_qweight.shape
+    I = N2 // 2
+    k = topk_ids.shape[1]
+    _need(router_logits, torch.float32, (T, E), "router_logits")
+    _need(w13_qweight, torch.int32, (E, 2 * I, H // 8), "w13_qweight")
+    _need(w13_scales, torch.float16, (E, 2 * I, H // group_size), "w13_scales")
+    _need(w13_qzeros, torch.int32, (E, 2 * I // 8, H // group_size), "w13_qzeros")
+    _need(w2_qweight, torch.int32, (E, H, I // 8), "w2_qweight")
+    _need(w2_scales, torch.float16, (E, H, I // group_size), "w2_scales")
+    _need(w2_qzeros, torch.int32, (E, H // 8, I // group_size), "w2_qzeros")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    _check(lib().moe_w4a16_apply(_ptr(x), _act(x), T, H, I, E, k, _ptr(router_logits), int(bool(renormalize)),
+                                 _ptr(w13_qweight), _ptr(w13_scales), _ptr(w13_qzeros), _ptr(w2_qweight),
+                                 _ptr(w2_scales), _ptr(w2_qzeros), group_size, _ptr(topk_w), _ptr(topk_ids),
+                                 block_m, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)), "moe_w4a16_apply")

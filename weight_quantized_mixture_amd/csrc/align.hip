@@ -14,6 +14,7 @@
 //      waves of the chunk) + rank.
 #include "common.hpp"
 #include "launch.hpp"
+#include "router_dev.hpp"
 
 namespace moe {
 
@@ -23,7 +24,7 @@ constexpr int kAlignWaves = 8;
 constexpr int kAlignThreads = kAlignWaves * kWave;
 constexpr int kMaxExperts = 1024;
 
-__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+__device__ __forceinline__ void align_body(
     const int32_t* __restrict__ ids, int64_t Tk, int E, int bm, int64_t cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded) {
@@ -124,7 +125,36 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
 }
 
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int64_t Tk, int E, int bm, int64_t cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  align_body(ids, Tk, E, bm, cap, sorted_ids, block_expert, num_padded);
+}
+
+// Routing and align in one launch (small batches): the 8 waves route the
+// tokens round-robin, then the same workgroup groups the ids it just wrote.
+__global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int renormalize,
+    float* __restrict__ topk_w, int32_t* __restrict__ topk_ids, int bm, int64_t cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  const int wave = threadIdx.x / kWave;
+  for (int64_t t = wave; t < T; t += kAlignWaves)
+    route_token(logits + t * E, E, k, renormalize, topk_w + t * k, topk_ids + t * k);
+  __syncthreads();
+  align_body(topk_ids, T * k, E, bm, cap, sorted_ids, block_expert, num_padded);
+}
+
 }  // namespace
+
+hipError_t launch_route_align(const float* logits, int64_t T, int E, int k, int renormalize, float* topk_w,
+                              int32_t* topk_ids, int block_m, int64_t cap, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* num_padded, hipStream_t stream) {
+  hipLaunchKernelGGL(route_align_kernel, dim3(1), dim3(kAlignThreads), 0, stream, logits, T, E, k, renormalize,
+                     topk_w, topk_ids, block_m, cap, sorted_ids, block_expert, num_padded);
+  return hipGetLastError();
+}
 
 hipError_t launch_align(const int32_t* topk_ids, int64_t Tk, int E, int block_m, int64_t cap,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,

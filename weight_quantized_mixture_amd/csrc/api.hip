@@ -141,9 +141,17 @@ int64_t splits_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_
   return gemm2_plan(T, H, I, E, k, bm).splits;
 }
 
-// The uint4 kernels cut K into equal parts of whole 128-wide steps.
+// uint4 GEMM2 splits: the streaming kernel (blocks of 16/32/64 rows) takes any
+// count up to I/128 (about 768 workgroups in flight); the tiled kernel needs
+// equal parts of whole 128-wide steps.
+bool w4_stream(int64_t bm) { return bm == 16 || bm == 32 || bm == 64; }
+
 int64_t w4_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
-  return gemm2_plan(T, H, I, E, k, bm, true).splits;
+  if (!w4_stream(bm)) return gemm2_plan(T, H, I, E, k, bm, true).splits;
+  const int64_t groups = (H / 128) * blocks_estimate(T, E, k, bm);
+  int64_t sp = 1;
+  while (sp * 2 <= 16 && sp * 2 <= I / 128 && groups * sp * 2 <= 768) sp *= 2;
+  return sp;
 }
 
 // In-workgroup K ways of the register-streaming GEMM2 for a given split count.
@@ -208,6 +216,25 @@ int check_act(int act) {
   if (act != MOE_BF16 && act != MOE_FP16)
     return fail(MOE_ERR_UNSUPPORTED, "act_dtype %d is neither MOE_BF16 nor MOE_FP16", act);
   return MOE_OK;
+}
+
+
+// Routing (when logits are given) and align.  Up to 16 tokens (two per wave)
+// one workgroup does both and saves a launch; larger batches route with one
+// wave per token across the chip, then align.
+constexpr int64_t kFusedRouteTokens = 16;
+
+hipError_t route_and_align(const float* logits, int renormalize, float* topk_w_out, int32_t* topk_ids_out,
+                           const int32_t* topk_ids, int64_t T, int64_t E, int64_t k, int64_t bm, int64_t cap,
+                           int32_t* sorted, int32_t* blocks, int32_t* npad, hipStream_t stream) {
+  const int Ei = static_cast<int>(E), ki = static_cast<int>(k), bmi = static_cast<int>(bm);
+  if (!logits) return moe::launch_align(topk_ids, T * k, Ei, bmi, cap, sorted, blocks, npad, stream);
+  if (T <= kFusedRouteTokens)
+    return moe::launch_route_align(logits, T, Ei, ki, renormalize, topk_w_out, topk_ids_out, bmi, cap, sorted,
+                                   blocks, npad, stream);
+  hipError_t e = moe::launch_route(logits, T, Ei, ki, renormalize, topk_w_out, topk_ids_out, stream);
+  if (e != hipSuccess) return e;
+  return moe::launch_align(topk_ids_out, T * k, Ei, bmi, cap, sorted, blocks, npad, stream);
 }
 
 }  // namespace
@@ -358,11 +385,16 @@ int moe_combine_topk(const float* y, int64_t splits, int64_t T, int64_t k, int64
                     "combine");
 }
 
-int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
-                      int64_t k, const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
-                      const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
-                      const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Route (when logits are given) + align + GEMM1 + GEMM2 + combine.
+int forward_w8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+               const int8_t* w13, const float* w13_scale, int64_t w13_row_stride, const int8_t* w2,
+               const float* w2_scale, int64_t w2_row_stride, const float* logits, int renormalize,
+               float* topk_w_out, int32_t* topk_ids_out, const float* topk_w, const int32_t* topk_ids,
+               int64_t block_m, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st;
   if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
   if ((st = check_act(act_dtype)) != MOE_OK) return st;
@@ -374,8 +406,10 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
     return fail(MOE_ERR_INVALID_ARGUMENT, "row strides must cover the row and be multiples of 16");
   if (T == 0) return ok();
   if (T * k > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^31-1");
-  if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !topk_w || !topk_ids || !out || !workspace)
+  if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace)
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (logits ? (!topk_w_out || !topk_ids_out) : (!topk_w || !topk_ids))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null routing pointer");
   if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 8) ||
       !aligned(workspace, kAlign))
     return fail(MOE_ERR_INVALID_ARGUMENT, "x, w13, w2 16-byte, out 8-byte, workspace 256-byte alignment required");
@@ -389,9 +423,13 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
   int32_t* npad = reinterpret_cast<int32_t*>(ws + L.off_npad);
   float* a = reinterpret_cast<float*>(ws + L.off_a);
   float* y = reinterpret_cast<float*>(ws + L.off_y);
-  hipError_t e = moe::launch_align(topk_ids, T * k, static_cast<int>(E), static_cast<int>(block_m), L.cap,
-                                   sorted, blocks, npad, stream);
-  if (e != hipSuccess) return hip_status(e, "align");
+  hipError_t e = route_and_align(logits, renormalize, topk_w_out, topk_ids_out, topk_ids, T, E, k, block_m,
+                                 L.cap, sorted, blocks, npad, stream);
+  if (e != hipSuccess) return hip_status(e, "route/align");
+  if (logits) {
+    topk_w = topk_w_out;
+    topk_ids = topk_ids_out;
+  }
   moe::Gemm1Args p1{};
   p1.x = x; p1.f16 = act_dtype == MOE_FP16; p1.T = T; p1.H = H; p1.I = I; p1.k = k; p1.Tk = T * k;
   p1.w13 = w13; p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = sorted; p1.block_expert = blocks;
@@ -406,6 +444,32 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
                                         static_cast<int>(E), topk_w, topk_ids, act_dtype == MOE_FP16,
                                         out, stream),
                     "combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
+                      int64_t k, const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                      const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                      const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                    nullptr, 0, nullptr, nullptr, topk_w, topk_ids, block_m, out, workspace, workspace_bytes,
+                    stream);
+}
+
+int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                    const float* router_logits, int renormalize,
+                    const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                    const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                    float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
+  return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                    router_logits, renormalize, topk_w, topk_ids, nullptr, nullptr, block_m, out, workspace,
+                    workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -430,12 +494,16 @@ size_t moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int
   return layout(T, H, I, E, k, block_m, w4_splits(T, H, I, E, k, block_m)).total;
 }
 
-int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
-                      int64_t k, const int32_t* w13_qweight, const uint16_t* w13_scales,
-                      const int32_t* w13_qzeros, const int32_t* w2_qweight,
-                      const uint16_t* w2_scales, const int32_t* w2_qzeros, int64_t group_size,
-                      const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_w4(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+               const int32_t* w13_qweight, const uint16_t* w13_scales, const int32_t* w13_qzeros,
+               const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros, int64_t group_size,
+               const float* logits, int renormalize, float* topk_w_out, int32_t* topk_ids_out,
+               const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
   int st;
   if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
   if ((st = check_act(act_dtype)) != MOE_OK) return st;
@@ -446,9 +514,11 @@ int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
   if ((st = check_block_m(block_m)) != MOE_OK) return st;
   if (T == 0) return ok();
   if (T * k > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^31-1");
-  if (!x || !w13_qweight || !w13_scales || !w13_qzeros || !w2_qweight || !w2_scales || !w2_qzeros ||
-      !topk_w || !topk_ids || !out || !workspace)
+  if (!x || !w13_qweight || !w13_scales || !w13_qzeros || !w2_qweight || !w2_scales || !w2_qzeros || !out ||
+      !workspace)
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (logits ? (!topk_w_out || !topk_ids_out) : (!topk_w || !topk_ids))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null routing pointer");
   if (!aligned(x, 16) || !aligned(w13_qweight, 16) || !aligned(w2_qweight, 16) || !aligned(out, 8) ||
       !aligned(workspace, kAlign))
     return fail(MOE_ERR_INVALID_ARGUMENT, "alignment: x and qweights 16 bytes, out 8, workspace 256");
@@ -462,25 +532,60 @@ int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
   int32_t* npad = reinterpret_cast<int32_t*>(ws + L.off_npad);
   float* a = reinterpret_cast<float*>(ws + L.off_a);
   float* y = reinterpret_cast<float*>(ws + L.off_y);
-  hipError_t e = moe::launch_align(topk_ids, T * k, static_cast<int>(E), static_cast<int>(block_m), L.cap,
-                                   sorted, blocks, npad, stream);
-  if (e != hipSuccess) return hip_status(e, "align");
+  hipError_t e = route_and_align(logits, renormalize, topk_w_out, topk_ids_out, topk_ids, T, E, k, block_m,
+                                 L.cap, sorted, blocks, npad, stream);
+  if (e != hipSuccess) return hip_status(e, "route/align");
+  if (logits) {
+    topk_w = topk_w_out;
+    topk_ids = topk_ids_out;
+  }
   moe::Gemm1W4Args p1{};
   p1.x = x; p1.f16 = act_dtype == MOE_FP16; p1.T = T; p1.H = H; p1.I = I; p1.k = k; p1.Tk = T * k;
   p1.qw = w13_qweight; p1.sc = w13_scales; p1.qz = w13_qzeros; p1.group = static_cast<int>(group_size);
   p1.sorted_ids = sorted; p1.block_expert = blocks; p1.num_padded = npad;
   p1.block_m = static_cast<int>(block_m); p1.cap = L.cap; p1.a = a;
-  if ((e = moe::launch_gemm1_w4(p1, stream)) != hipSuccess) return hip_status(e, "gemm1_w4");
+  if ((e = w4_stream(block_m) ? moe::launch_gemm1_w4_stream(p1, stream) : moe::launch_gemm1_w4(p1, stream)) !=
+      hipSuccess)
+    return hip_status(e, "gemm1_w4");
   moe::Gemm2W4Args p2{};
   p2.a = a; p2.f16 = act_dtype == MOE_FP16; p2.H = H; p2.I = I; p2.Tk = T * k;
   p2.qw = w2_qweight; p2.sc = w2_scales; p2.qz = w2_qzeros; p2.group = static_cast<int>(group_size);
   p2.sorted_ids = sorted; p2.block_expert = blocks; p2.num_padded = npad;
   p2.block_m = static_cast<int>(block_m); p2.cap = L.cap; p2.splits = static_cast<int>(splits); p2.y = y;
-  if ((e = moe::launch_gemm2_w4(p2, stream)) != hipSuccess) return hip_status(e, "gemm2_w4");
+  if ((e = w4_stream(block_m) ? moe::launch_gemm2_w4_stream(p2, stream) : moe::launch_gemm2_w4(p2, stream)) !=
+      hipSuccess)
+    return hip_status(e, "gemm2_w4");
   return hip_status(moe::launch_combine(y, static_cast<int>(splits), T, static_cast<int>(k), H,
                                         static_cast<int>(E), topk_w, topk_ids, act_dtype == MOE_FP16,
                                         out, stream),
                     "combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
+                      int64_t k, const int32_t* w13_qweight, const uint16_t* w13_scales,
+                      const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                      const uint16_t* w2_scales, const int32_t* w2_qzeros, int64_t group_size,
+                      const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_w4(x, act_dtype, T, H, I, E, k, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
+                    w2_qzeros, group_size, nullptr, 0, nullptr, nullptr, topk_w, topk_ids, block_m, out, workspace,
+                    workspace_bytes, stream);
+}
+
+int moe_w4a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                    const float* router_logits, int renormalize,
+                    const int32_t* w13_qweight, const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                    const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros,
+                    int64_t group_size, float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
+  return forward_w4(x, act_dtype, T, H, I, E, k, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
+                    w2_qzeros, group_size, router_logits, renormalize, topk_w, topk_ids, nullptr, nullptr, block_m,
+                    out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

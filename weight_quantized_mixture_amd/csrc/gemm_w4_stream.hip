@@ -1,0 +1,340 @@
+// Weight-streaming grouped GEMMs for group-wise uint4 experts (W4A16) when
+// each align block holds at most 64 rows.
+//
+// moe_wna16 page, MoeWNA16Method.create_weights: codes packed along K
+// (here 8 per int32, code k at bits 4*(k mod 8)), fp16 scales [E, N, K/g],
+// zeros packed along N (8 per int32), W = (q - z) * s with the true zero.
+//
+// Same structure as the int8 streaming kernels with the activation tile in
+// LDS: a workgroup is one align block (16 * MT rows, padding tiles skipped)
+// and 4 waves side by side in N; per 128-K step a lane holds one int32x4 of
+// its weight row (32 codes), the whole step lies in one group (g is a
+// multiple of 128), and the step's MFMA partial sum is multiplied by the
+// group scale of the lane's column before it joins the running total, so the
+// scale never rounds a weight.  The weights of the next three steps are in
+// flight while a step is converted and multiplied (packed rows are short, so a
+// wave needs several steps of loads outstanding to cover HBM latency).
+//
+// fp16 activations: 0x6400 | q is the half 1024 + q and one packed subtraction
+// of 1024 + z leaves q - z exactly; decoding nibble pairs (q_i, q_{i+4}) puts
+// the MFMA K slots in the order 0,4,1,5,2,6,3,7, so the activation chunks are
+// permuted the same way while they are copied into LDS.  GEMM1 writes the
+// intermediate as fp16 hi/lo planes in natural order (it must stay inside the
+// fp16 range, like the activations), GEMM2 permutes them on the same copy.
+// bf16 activations: codes go through fp32 into bf16 (natural order) and the
+// planes are bf16.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kStep = 128;
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ uint32_t zero_code(const int32_t* qz_e, int64_t G, int64_t g, int64_t n) {
+  return (static_cast<uint32_t>(qz_e[(n >> 3) * G + g]) >> (4 * (n & 7))) & 0xFu;
+}
+
+// One int32 of 8 codes -> MFMA operand of (q - z).
+template <bool F16>
+__device__ __forceinline__ u32x4 w4_op(uint32_t w, uint32_t z) {
+  u32x4 r;
+  if constexpr (F16) {
+    const _Float16 zo = static_cast<_Float16>(static_cast<float>(1024u + z));
+    const f16x2 off = {zo, zo};
+    const uint32_t m = 0x000F000Fu, magic = 0x64006400u;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, (w & m) | magic) - off);
+    r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 4) & m) | magic) - off);
+    r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 8) & m) | magic) - off);
+    r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, ((w >> 12) & m) | magic) - off);
+  } else {
+    const float zf = static_cast<float>(z);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = static_cast<float>((w >> (4 * i)) & 0xFu) - zf;
+    r.x = pack_hi16(v[0], v[1]);
+    r.y = pack_hi16(v[2], v[3]);
+    r.z = pack_hi16(v[4], v[5]);
+    r.w = pack_hi16(v[6], v[7]);
+  }
+  return r;
+}
+
+// 8 natural-order 16-bit values -> slot order 0,4,1,5,2,6,3,7.
+__device__ __forceinline__ u32x4 perm0415(u32x4 v) {
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+  r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+  r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+  r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+  return r;
+}
+
+__device__ __forceinline__ void split16(float v, bool f16, uint16_t& hi, uint16_t& lo) {
+  if (f16) {
+    const _Float16 h = static_cast<_Float16>(v);
+    const _Float16 l = static_cast<_Float16>(v - static_cast<float>(h));
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, l);
+  } else {
+    const uint32_t h = pack_bf16_rne(v, 0.0f) & 0xffffu;
+    hi = static_cast<uint16_t>(h);
+    lo = static_cast<uint16_t>(pack_bf16_rne(v - __uint_as_float(h << 16), 0.0f) & 0xffffu);
+  }
+}
+
+// ROLE 1: GEMM1, each wave 16 gate rows + the 16 matching up rows, A = gathered x.
+// ROLE 2: GEMM2, each wave NT*16 rows of w2, A = hi/lo planes of the intermediate.
+template <int ROLE, int MT, int NT, bool F16>
+__global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4Args p1, const Gemm2W4Args p2) {
+  constexpr int NPLANE = ROLE == 1 ? 1 : 2;
+  constexpr int ROWS = 16 * MT;
+  constexpr int PITCH = kStep + 8;
+  constexpr int QPR = kStep / 8;
+  constexpr int CPT = (ROWS * QPR + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][NPLANE][ROWS * PITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int32_t* sorted_ids = ROLE == 1 ? p1.sorted_ids : p2.sorted_ids;
+  const int64_t Tk = ROLE == 1 ? p1.Tk : p2.Tk;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * ROWS;
+  if (row0 >= *(ROLE == 1 ? p1.num_padded : p2.num_padded)) return;
+  const int64_t e = (ROLE == 1 ? p1.block_expert : p2.block_expert)[blockIdx.y];
+  int ntiles = 0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    if (sorted_ids[row0 + mt * 16] < Tk) ntiles = mt + 1;
+  const int nrows = ntiles * 16;
+
+  const int64_t H = ROLE == 1 ? p1.H : p2.H;
+  const int64_t I = ROLE == 1 ? p1.I : p2.I;
+  const int64_t K = ROLE == 1 ? H : I;
+  const int64_t N = ROLE == 1 ? 2 * I : H;
+  const int g = ROLE == 1 ? p1.group : p2.group;
+  const int64_t G = K / g;
+  const int32_t* qw = ROLE == 1 ? p1.qw : p2.qw;
+  const uint16_t* sc = ROLE == 1 ? p1.sc : p2.sc;
+  const int32_t* qz_e = (ROLE == 1 ? p1.qz : p2.qz) + e * (N / 8) * G;
+
+  // rows of w owned by this lane (tile j)
+  int64_t nrow[NT];
+  if constexpr (ROLE == 1) {
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16 + col;
+    nrow[0] = n0;
+    nrow[1] = I + n0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) nrow[j] = static_cast<int64_t>(blockIdx.x) * (64 * NT) + wave * 16 * NT + 16 * j + col;
+  }
+  const int32_t* wp[NT];
+  const uint16_t* sp[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    wp[j] = qw + (e * N + nrow[j]) * (K / 8) + kg * 4;
+    sp[j] = sc + (e * N + nrow[j]) * G;
+  }
+
+  // K range: GEMM2 cuts K into splits of whole steps
+  const int total = static_cast<int>(K / kStep);
+  int sbeg = 0, nsteps = total;
+  if constexpr (ROLE == 2) {
+    sbeg = static_cast<int>(blockIdx.z) * total / p2.splits;
+    nsteps = (static_cast<int>(blockIdx.z) + 1) * total / p2.splits - sbeg;
+  }
+
+  // cooperative copy of the activation rows of one step into LDS
+  int64_t src[CPT];
+  int dst[CPT];
+  bool cv[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ci = tid + c * kThreads;
+    const int r = ci / QPR, q = ci % QPR;
+    cv[c] = r < nrows;
+    dst[c] = r * PITCH + q * 8;
+    if constexpr (ROLE == 1) {
+      const int f = cv[c] ? sorted_ids[row0 + r] : static_cast<int>(Tk);
+      src[c] = f < Tk ? (static_cast<int64_t>(f) / p1.k) * H + q * 8 : -1;
+    } else {
+      src[c] = (row0 + r) * I + q * 8;
+    }
+  }
+  const uint16_t* xa = ROLE == 1 ? static_cast<const uint16_t*>(p1.x) : reinterpret_cast<const uint16_t*>(p2.a);
+  const int64_t plane = ROLE == 1 ? 0 : p2.cap * I;
+  auto load_a = [&](int s, u32x4 (&regs)[NPLANE][CPT]) {
+    const int64_t ko = static_cast<int64_t>(sbeg + s) * kStep;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int pl = 0; pl < NPLANE; ++pl) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (cv[c] && src[c] >= 0) v = ld16(xa + pl * plane + src[c] + ko);
+        regs[pl][c] = F16 ? perm0415(v) : v;
+      }
+  };
+  auto store_a = [&](int buf, const u32x4 (&regs)[NPLANE][CPT]) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (cv[c]) {
+#pragma unroll
+        for (int pl = 0; pl < NPLANE; ++pl) *reinterpret_cast<u32x4*>(&As[buf][pl][dst[c]]) = regs[pl][c];
+      }
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // weights of the next kPF steps are in flight while a step is multiplied
+  constexpr int kPF = 3;
+  auto wload = [&](int s, u32x4 (&v)[NT]) {
+    const int64_t kq = sbeg + (s < nsteps ? s : nsteps - 1);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) v[j] = ld16(wp[j] + kq * (kStep / 8));
+  };
+  u32x4 areg[NPLANE][CPT];
+  u32x4 wv[NT], w1[NT], w2[NT];
+  if (nsteps > 0) {
+    load_a(0, areg);
+    wload(0, wv);
+    wload(1, w1);
+    wload(2, w2);
+    store_a(0, areg);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nsteps;
+    if (more) load_a(s + 1, areg);
+    const int64_t ks = sbeg + s;
+    u32x4 nv[NT];
+    wload(s + kPF, nv);
+    const int64_t grp = ks * kStep / g;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const uint32_t z = zero_code(qz_e, G, grp, nrow[j]);
+      const float scale = f16_to_f32(sp[j][grp]);
+      u32x4 b[4];
+      b[0] = w4_op<F16>(wv[j].x, z);
+      b[1] = w4_op<F16>(wv[j].y, z);
+      b[2] = w4_op<F16>(wv[j].z, z);
+      b[3] = w4_op<F16>(wv[j].w, z);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (mt < ntiles) {
+          const int o = (mt * 16 + col) * PITCH + kg * 32;
+          f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(&As[buf][0][o + 8 * i]);
+            part = mfma16<F16>(a0, b[i], part);
+            if constexpr (ROLE == 2) {
+              const u32x4 a1 = *reinterpret_cast<const u32x4*>(&As[buf][1][o + 8 * i]);
+              part = mfma16<F16>(a1, b[i], part);
+            }
+          }
+          acc[mt][j] += part * scale;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      wv[j] = w1[j];
+      w1[j] = w2[j];
+      w2[j] = nv[j];
+    }
+    if (more) store_a(buf ^ 1, areg);
+    __syncthreads();
+  }
+
+  if constexpr (ROLE == 1) {
+    uint16_t* a_hi = reinterpret_cast<uint16_t*>(p1.a);
+    uint16_t* a_lo = a_hi + p1.cap * I;
+    const int64_t n = nrow[0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt < ntiles) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t r = row0 + mt * 16 + kg * 4 + i;
+          uint16_t hi, lo;
+          split16(silu_mul(acc[mt][0][i], acc[mt][1][i]), F16, hi, lo);
+          a_hi[r * I + n] = hi;
+          a_lo[r * I + n] = lo;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt < ntiles) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = sorted_ids[row0 + mt * 16 + kg * 4 + i];
+          if (f < Tk) {
+            float* yr = p2.y + (static_cast<int64_t>(blockIdx.z) * Tk + f) * H;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) yr[nrow[j]] = acc[mt][j][i];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MT, bool F16>
+hipError_t w4s_launch1(const Gemm1W4Args& p, hipStream_t stream) {
+  const Gemm2W4Args none{};
+  hipLaunchKernelGGL((gemm_w4_stream_kernel<1, MT, 2, F16>),
+                     dim3(static_cast<unsigned>(p.I / 64), static_cast<unsigned>(p.cap / p.block_m)),
+                     dim3(kThreads), 0, stream, p, none);
+  return hipGetLastError();
+}
+
+template <int MT, bool F16>
+hipError_t w4s_launch2(const Gemm2W4Args& p, hipStream_t stream) {
+  const Gemm1W4Args none{};
+  hipLaunchKernelGGL((gemm_w4_stream_kernel<2, MT, 2, F16>),
+                     dim3(static_cast<unsigned>(p.H / 128), static_cast<unsigned>(p.cap / p.block_m),
+                          static_cast<unsigned>(p.splits)),
+                     dim3(kThreads), 0, stream, none, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm1_w4_stream(const Gemm1W4Args& p, hipStream_t stream) {
+  const int mt = p.block_m / 16;
+  if (p.f16) {
+    if (mt == 4) return w4s_launch1<4, true>(p, stream);
+    if (mt == 2) return w4s_launch1<2, true>(p, stream);
+    return w4s_launch1<1, true>(p, stream);
+  }
+  if (mt == 4) return w4s_launch1<4, false>(p, stream);
+  if (mt == 2) return w4s_launch1<2, false>(p, stream);
+  return w4s_launch1<1, false>(p, stream);
+}
+
+hipError_t launch_gemm2_w4_stream(const Gemm2W4Args& p, hipStream_t stream) {
+  const int mt = p.block_m / 16;
+  if (p.f16) {
+    if (mt == 4) return w4s_launch2<4, true>(p, stream);
+    if (mt == 2) return w4s_launch2<2, true>(p, stream);
+    return w4s_launch2<1, true>(p, stream);
+  }
+  if (mt == 4) return w4s_launch2<4, false>(p, stream);
+  if (mt == 2) return w4s_launch2<2, false>(p, stream);
+  return w4s_launch2<1, false>(p, stream);
+}
+
+}  // namespace moe

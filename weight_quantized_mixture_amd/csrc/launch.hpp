@@ -19,6 +19,11 @@ hipError_t launch_quantize_w4(const float* w, int64_t E, int64_t N, int64_t K, i
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renormalize,
                         float* topk_w, int32_t* topk_ids, hipStream_t stream);
 
+// Routing followed by the padded-block align in one workgroup (small batches).
+hipError_t launch_route_align(const float* logits, int64_t T, int E, int k, int renormalize, float* topk_w,
+                              int32_t* topk_ids, int block_m, int64_t cap, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
+
 // Padded-block align, one workgroup.
 hipError_t launch_align(const int32_t* topk_ids, int64_t Tk, int E, int block_m, int64_t cap,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
@@ -100,6 +105,9 @@ struct Gemm2W4Args {
   float* y;
 };
 hipError_t launch_gemm2_w4(const Gemm2W4Args& p, hipStream_t stream);
+// Weight-streaming uint4 variants for blocks of 16, 32 or 64 rows (intermediate as 16-bit hi/lo planes).
+hipError_t launch_gemm1_w4_stream(const Gemm1W4Args& p, hipStream_t stream);
+hipError_t launch_gemm2_w4_stream(const Gemm2W4Args& p, hipStream_t stream);
 
 // Weighted top-k combine of the split partials.
 hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,

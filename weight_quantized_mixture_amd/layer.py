@@ -79,9 +79,17 @@ class W8A16MoE:
                             topk_ids, out, ws, block_m)
         return out
 
-    def apply(self, x, router_logits, top_k: int, renormalize: bool = True, inplace: bool = False):
-        topk_w, topk_ids = self.route(router_logits, top_k, renormalize)
-        return self.forward_topk(x, topk_w, topk_ids, out=x if inplace else None)
+    def apply(self, x, router_logits, top_k: int, renormalize: bool = True, inplace: bool = False,
+              block_m: int = 0):
+        """Route from logits and run the layer (one library call); returns the output."""
+        T = x.shape[0]
+        out = x if inplace else torch.empty_like(x)
+        self.topk_w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+        self.topk_ids = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+        ws = self._ws.get(B.moe_w8a16_workspace_bytes(T, self.H, self.I, self.E, top_k, block_m), x.device)
+        B.moe_w8a16_apply(x, router_logits, renormalize, self.w13_weight, self.w13_scale, self.w2_weight,
+                          self.w2_scale, self.topk_w, self.topk_ids, out, ws, block_m)
+        return out
 
 
 class W4A16MoE:
@@ -118,6 +126,14 @@ class W4A16MoE:
                             block_m)
         return out
 
-    def apply(self, x, router_logits, top_k: int, renormalize: bool = True, inplace: bool = False):
-        topk_w, topk_ids = self.route(router_logits, top_k, renormalize)
-        return self.forward_topk(x, topk_w, topk_ids, out=x if inplace else None)
+    def apply(self, x, router_logits, top_k: int, renormalize: bool = True, inplace: bool = False,
+              block_m: int = 0):
+        T = x.shape[0]
+        out = x if inplace else torch.empty_like(x)
+        self.topk_w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+        self.topk_ids = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+        ws = self._ws.get(B.moe_w4a16_workspace_bytes(T, self.H, self.I, self.E, top_k, block_m), x.device)
+        B.moe_w4a16_apply(x, router_logits, renormalize, self.w13_qweight, self.w13_scales, self.w13_qzeros,
+                          self.w2_qweight, self.w2_scales, self.w2_qzeros, self.group_size, self.topk_w,
+                          self.topk_ids, out, ws, block_m)
+        return out
