@@ -26,6 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "weight_quantized_mixture_amd", "csrc")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP16_PEAK_TFLOPS = 2500.0
 
@@ -48,6 +50,13 @@ def parse():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB (3 times) and exit: the known "
                          "byte count that scales the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of a bench run, then of "
+                         "--calibrate-copy-mb 1024) into the traffic summary under profiles/ and exit")
+    ap.add_argument("--pmc-command", default="", help="command line recorded in the traffic summary")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace --stats output folder into the kernel-time summary "
+                         "under profiles/ and exit")
     ap.add_argument("--flush-mb", type=int, default=None,
                     help="read this many MB of other data between timed steps (outside the events) so "
                          "the 256 MB Infinity Cache does not serve the weights; default: 512 when the "
@@ -59,8 +68,115 @@ def parse():
 HEADLINE_T = {"tiny": 16, "mixtral_decode": 64, "mixtral_prefill": 4096, "fine_grained": 512, "w4a16": 256}
 
 
+def sources_sha() -> str:
+    """Hash of the HIP sources: a traffic summary is valid only for the kernels it was taken on."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_rows(folder):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    out = {}
+    for r in csv.DictReader(open(files[0])):
+        name = r["Kernel_Name"]
+        out.setdefault((name, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(args):
+    """Traffic of every library kernel per launch, scaled by what the counters read for a copy of known size."""
+    fetch, write = _pmc_rows(args.summarize_pmc[0]), _pmc_rows(args.summarize_pmc[1])
+    cf, cw = _pmc_rows(args.summarize_pmc[2]), _pmc_rows(args.summarize_pmc[3])
+    copy_bytes = 1024 << 20
+
+    def copy_kib(rows, counter):
+        v = [x for (n, c), xs in rows.items() if c == counter and "copyBuffer" in n for x in xs]
+        if not v:
+            v = [x for (n, c), xs in rows.items() if c == counter and "copy" in n.lower() for x in xs]
+        return max(v)
+    f_scale = (copy_bytes / 1024) / copy_kib(cf, "FETCH_SIZE")
+    w_scale = (copy_bytes / 1024) / copy_kib(cw, "WRITE_SIZE")
+    kernels = {}
+    for (name, c), xs in fetch.items():
+        if c == "FETCH_SIZE" and "moe::" in name:
+            kernels.setdefault(name, {})["fetch_kib"] = sum(xs) / len(xs)
+    for (name, c), xs in write.items():
+        if c == "WRITE_SIZE" and "moe::" in name:
+            kernels.setdefault(name, {})["write_kib"] = sum(xs) / len(xs)
+    res = {"sources_sha": sources_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "command": args.pmc_command, "workload": args.workload,
+           "T": args.tokens or HEADLINE_T[args.workload], "kernels": {}}
+    lines = [f"# HBM traffic per launch: {args.workload}, T={res['T']}", "",
+             f"Command: `{args.pmc_command}`", "",
+             f"Copy calibration: a 1 GiB copy reads {copy_bytes / 1024 / f_scale:.0f} KiB in FETCH_SIZE "
+             f"(scale x{f_scale:.3f}) and writes {copy_bytes / 1024 / w_scale:.0f} KiB in WRITE_SIZE (scale x{w_scale:.3f}).",
+             "", "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled traffic MB |", "|---|---|---|---|"]
+    for name, d in sorted(kernels.items()):
+        fk, wk = d.get("fetch_kib", 0.0), d.get("write_kib", 0.0)
+        mb = (fk * f_scale + wk * w_scale) * 1024 / 1e6
+        short = name.replace("moe::(anonymous namespace)::", "").replace("void ", "").split("(moe::")[0][:90]
+        res["kernels"][short] = {"fetch_kib": fk, "write_kib": wk, "traffic_bytes": mb * 1e6}
+        lines.append(f"| `{short}` | {fk:.0f} | {wk:.0f} | {mb:.1f} |")
+    lines += ["", f"Kernel sources sha256[:16]: `{res['sources_sha']}`"]
+    stem = f"traffic_{args.workload}_T{res['T']}"
+    os.makedirs(PROFILES, exist_ok=True)
+    json.dump(res, open(os.path.join(PROFILES, stem + ".json"), "w"), indent=1)
+    open(os.path.join(PROFILES, stem + ".md"), "w").write("\n".join(lines) + "\n")
+    print(json.dumps(res), flush=True)
+
+
+def summarize_trace(args):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {args.summarize_trace}")
+    T = args.tokens or HEADLINE_T[args.workload]
+    lines = [f"# Kernel times: {args.workload}, T={T}", "", f"Command: `{args.pmc_command}`", "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(files[0])):
+        name = r["Name"].replace("moe::(anonymous namespace)::", "").replace("void ", "")
+        name = name.split("(moe::")[0].split("(float const")[0].split("(int const")[0][:90]
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", f"Kernel sources sha256[:16]: `{sources_sha()}`"]
+    stem = f"kernels_{args.workload}_T{T}"
+    os.makedirs(PROFILES, exist_ok=True)
+    open(os.path.join(PROFILES, stem + ".md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
+def recorded_traffic(workload, T, kernel_prefix):
+    """Scaled HBM bytes of the dominant kernel from the committed summary, if the kernels are unchanged."""
+    path = os.path.join(PROFILES, f"traffic_{workload}_T{T}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("sources_sha") != sources_sha():
+        return None
+    for name, v in d["kernels"].items():
+        if name.startswith(kernel_prefix):
+            return v["traffic_bytes"]
+    return None
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this library runs on a "
               f"single GPU (the layer is data-parallel over tokens, with no exchange between GPUs).",
@@ -219,8 +335,8 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": bytes_gemm1 / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["traffic"] = None
-        roof["kernel"] = "gemm1_w8_kernel"
+        roof["kernel"] = gemm1_kernel_name(block_m, H)
+        roof["traffic"] = recorded_traffic(wl.name, T, roof["kernel"])
         roof["kernel_ms"] = stage_ms["gemm1"]
     else:
         dur_s = ms_per_step / 1e3
@@ -261,6 +377,17 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def gemm1_kernel_name(block_m, H):
+    """Name prefix of the GEMM1 kernel the library launches for this block size."""
+    if block_m == 256:
+        return "gemm_prefill_kernel<1"
+    if block_m in (32, 64) and (block_m == 64 or H % 256 == 0):
+        return "gemm1_lds_kernel"
+    if block_m <= 64:
+        return "gemm1_stream_kernel"
+    return "gemm1_w8_kernel"
 
 
 def cpu_baseline(wl, T, xb, logits_np, args, active):

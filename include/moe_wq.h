@@ -146,7 +146,7 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
  * Routing + forward in one call, from router logits (the moe_wna16 page's
  * MoeWNA16Method.apply_monolithic form: the layer takes router_logits and
  * routes itself).  Same result as moe_route_topk followed by
- * moe_w8a16_forward; for T <= 16 one workgroup routes and aligns, which
+ * moe_w8a16_forward; for T <= 8 one workgroup routes and aligns, which
  * saves a launch.  topk_w / topk_ids (device fp32 / int32 [T, k]) receive
  * the routing.  Arguments and errors as moe_route_topk + moe_w8a16_forward.
  * ---------------------------------------------------------------------- */

@@ -177,10 +177,10 @@ def test_fine_grained(T):
     assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), f"fine-grained T={T}")
 
 
-@pytest.mark.parametrize("T,E,k,act", [(1, 8, 2, "bf16"), (16, 64, 6, "fp16"), (37, 8, 2, "fp16"),
+@pytest.mark.parametrize("T,E,k,act", [(1, 8, 2, "bf16"), (8, 64, 6, "fp16"), (37, 8, 2, "fp16"),
                                        (300, 16, 4, "bf16")])
 def test_apply_from_logits_matches_route_then_forward(T, E, k, act):
-    """moe_w8a16_apply (routing fused with align up to 16 tokens) equals route + forward bit for bit."""
+    """moe_w8a16_apply (routing fused with align up to 8 tokens) equals route + forward bit for bit."""
     H, I = 256, 384
     W = small_w8(E, H, I, seed=51, pad=True)
     xb = synthetic.random_activations(T, H, act, seed=52)

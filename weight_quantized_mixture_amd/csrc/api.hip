@@ -100,6 +100,7 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
 bool gemm2_lds(int64_t bm) { return bm == 16 || bm == 32 || bm == 64; }
 
 int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
+  if (bm == 64) return 2;   // 4 x 4 accumulator tiles would leave one wave per SIMD
   return (H / 256) * blocks_estimate(T, E, k, bm) >= 64 ? 4 : 2;
 }
 
@@ -219,10 +220,10 @@ int check_act(int act) {
 }
 
 
-// Routing (when logits are given) and align.  Up to 16 tokens (two per wave)
+// Routing (when logits are given) and align.  Up to 8 tokens (one per wave)
 // one workgroup does both and saves a launch; larger batches route with one
 // wave per token across the chip, then align.
-constexpr int64_t kFusedRouteTokens = 16;
+constexpr int64_t kFusedRouteTokens = 8;
 
 hipError_t route_and_align(const float* logits, int renormalize, float* topk_w_out, int32_t* topk_ids_out,
                            const int32_t* topk_ids, int64_t T, int64_t E, int64_t k, int64_t bm, int64_t cap,
