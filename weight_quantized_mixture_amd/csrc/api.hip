@@ -86,7 +86,7 @@ int gemm1_kways(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t b
 }
 
 hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t stream) {
-  if (use_prefill(p.block_m) && p.H % 64 == 0) return moe::launch_gemm1_w8_prefill(p, stream);
+  if (use_prefill(p.block_m)) return moe::launch_gemm1_w8_big(p, stream);
   if (!use_stream(p.block_m)) return moe::launch_gemm1_w8(p, stream);
   const int mt = p.block_m / 16;
   if (mt == 2 && p.H % 256 == 0) return moe::launch_gemm1_w8_lds(p, 2, 1, stream);

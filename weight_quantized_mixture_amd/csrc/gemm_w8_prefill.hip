@@ -275,16 +275,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(const Gemm1Ar
 
 }  // namespace
 
-hipError_t launch_gemm1_w8_prefill(const Gemm1Args& p, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(p.I / 64), static_cast<unsigned>(p.cap / kRows));
-  const Gemm2Args none{};
-  if (p.f16)
-    hipLaunchKernelGGL((gemm_prefill_kernel<1, 64, 1, true>), grid, dim3(kThreads), 0, stream, p, none);
-  else
-    hipLaunchKernelGGL((gemm_prefill_kernel<1, 64, 1, false>), grid, dim3(kThreads), 0, stream, p, none);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm2_w8_prefill(const Gemm2Args& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.H / 128), static_cast<unsigned>(p.cap / kRows));
   const Gemm1Args none{};
