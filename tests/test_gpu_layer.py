@@ -56,6 +56,17 @@ def test_ragged_shapes(act, bm, T, pad):
     assert_layer_close(got, ref_w8(W, xb, act, w_ref, ids_ref), f"ragged {act} bm={bm} T={T} pad={pad}")
 
 
+def test_block256_odd_hidden():
+    """256-row blocks with H not a multiple of 256 (the GEMM2 tile): the generic tiled kernel."""
+    E, k, H, I, T = 4, 2, 384, 256, 200
+    log(f"[layer] block_m=256 H={H} I={I} T={T}")
+    W = small_w8(E, H, I, seed=23, pad=True)
+    xb = synthetic.random_activations(T, H, "bf16", seed=24)
+    logits = synthetic.random_logits(T, E, seed=25)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, "bf16", logits, k, block_m=256)
+    assert_layer_close(got, ref_w8(W, xb, "bf16", w_ref, ids_ref), "block_m=256 H=384")
+
+
 def test_edge_cases_routing_shapes():
     H, I = 256, 256
     # k = E, one token, renormalize off

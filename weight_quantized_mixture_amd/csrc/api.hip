@@ -166,7 +166,7 @@ int gemm2_kw_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t 
 }
 
 hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, hipStream_t stream) {
-  if (use_prefill(p.block_m)) return moe::launch_gemm2_w8_prefill(p, stream);
+  if (use_prefill(p.block_m) && p.H % 256 == 0) return moe::launch_gemm2_w8_big(p, stream);
   if (!use_stream(p.block_m)) return moe::launch_gemm2_w8(p, stream);
   if (gemm2_lds(p.block_m))
     return moe::launch_gemm2_w8_lds(p, 1, gemm2_nt(T, p.H, E, k, p.block_m), stream);

@@ -1,4 +1,4 @@
-// Grouped int8-weight GEMM1 for 256-row align blocks (prefill-sized expert
+// Grouped int8-weight GEMMs for 256-row align blocks (prefill-sized expert
 // loads, where the bf16 MFMA work dominates), gfx950.
 //
 // experts_int8 page, ExpertsInt8MoEMethod.create_weights / apply ->
@@ -221,7 +221,156 @@ __global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) 
   }
 }
 
+// GEMM2 for 256-row blocks: y = (hi + lo) dequant(w2[e])^T, scale on the
+// accumulator.  A workgroup owns 128 rows (half an align block) and 256
+// output columns; 8 waves in a 2 x 4 grid, each 64 rows x 64 columns (4 x 4
+// tiles, both planes of a through the MFMA with the same converted weight
+// fragment).  Stages of 64 K in the same 3-deep LDS ring: 2 x 16 KB of the
+// hi/lo planes and 16 KB of int8 w2 rows per stage.
+constexpr int k2Rows = 128;
+constexpr int k2Cols = 256;
+constexpr int k2AStage = 2 * k2Rows * kARow;          // 32 KB
+constexpr int k2BStage = k2Cols * kBRow;              // 16 KB
+constexpr int k2StageBytes = k2AStage + k2BStage;
+constexpr int k2ADma = k2AStage / (kThreads * 16);
+constexpr int k2BDma = k2BStage / (kThreads * 16);
+
+__global__ __launch_bounds__(kThreads) void gemm2_big_kernel(const Gemm2Args p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * k2StageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+
+  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * k2Rows;
+  if (row0 >= *p.num_padded) return;
+  const int e = p.block_expert[row0 / kRows];
+  const int64_t Tk = p.Tk, H = p.H, I = p.I;
+
+  int nrows = 0;
+  for (int r = 0; r < k2Rows; r += 16)
+    if (p.sorted_ids[row0 + r] < Tk) nrows = r + 16;
+  if (nrows == 0) return;      // the second half of a block may be empty (uniform exit)
+  int ntw = (nrows - wm * 64) / 16;
+  ntw = ntw < 0 ? 0 : (ntw > 4 ? 4 : ntw);
+  const int nst = static_cast<int>(I / kBK);
+
+  // A copies: (plane, row) pairs q = 0..255, 8 per copy instruction
+  const uint16_t* a16 = reinterpret_cast<const uint16_t*>(p.a);
+  const uint16_t* asrc[k2ADma];
+#pragma unroll
+  for (int i = 0; i < k2ADma; ++i) {
+    const int q = wave * (2 * k2Rows / kWaves) + i * 8 + (lane >> 3);
+    const int pl = q / k2Rows, r = q % k2Rows;
+    const int c = (lane & 7) ^ swz_a(r);
+    asrc[i] = a16 + pl * p.cap * I + (row0 + r) * I + c * 8;
+  }
+  const int64_t hb = static_cast<int64_t>(blockIdx.x) * k2Cols;
+  const int8_t* bsrc[k2BDma];
+#pragma unroll
+  for (int i = 0; i < k2BDma; ++i) {
+    const int b = wave * (k2Cols / kWaves) + i * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz_b(b);
+    bsrc[i] = p.w2 + (static_cast<int64_t>(e) * H + hb + b) * p.ldw + c * 16;
+  }
+  auto issue = [&](int s, int slot) {
+    uint8_t* base = smem + slot * k2StageBytes;
+#pragma unroll
+    for (int i = 0; i < k2ADma; ++i)
+      dma16(asrc[i] + static_cast<int64_t>(s) * kBK, base + (wave * (2 * k2Rows / kWaves) + i * 8) * kARow);
+#pragma unroll
+    for (int i = 0; i < k2BDma; ++i)
+      dma16(bsrc[i] + static_cast<int64_t>(s) * kBK, base + k2AStage + (wave * (k2Cols / kWaves) + i * 16) * kBRow);
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = wn * 64 + 16 * j + col;
+    boff[j] = k2AStage + b * kBRow + 16 * (kg ^ swz_b(b));
+  }
+  int aoff[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int r = wm * 64 + mt * 16 + col;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) aoff[mt][ks] = r * kARow + 16 * ((2 * kg + ks) ^ swz_a(r));
+  }
+
+  auto run = [&](auto tiles) {
+    constexpr int MT = decltype(tiles)::value;
+    issue(0, 0);
+    if (nst > 1) issue(1, 1);
+    int slot = 0;
+    for (int s = 0; s < nst; ++s) {
+      if (s + 1 < nst) wait_vmcnt<k2ADma + k2BDma>();
+      else wait_vmcnt<0>();
+      stage_barrier();
+      if (s + 2 < nst) issue(s + 2, slot == 0 ? 2 : slot - 1);
+      const uint8_t* st = smem + slot * k2StageBytes;
+
+      u32x4 b[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(st + boff[j]);
+        i8x16_to_operands<false>(q, b[j][0], b[j][1]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 ah = *reinterpret_cast<const u32x4*>(st + aoff[mt][ks]);
+          const u32x4 al = *reinterpret_cast<const u32x4*>(st + k2Rows * kARow + aoff[mt][ks]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[mt][j] = mfma16_bf16(ah, b[j][ks], acc[mt][j]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[mt][j] = mfma16_bf16(al, b[j][ks], acc[mt][j]);
+        }
+      }
+      slot = slot == kStages - 1 ? 0 : slot + 1;
+    }
+  };
+  if (ntw > 3) run(std::integral_constant<int, 4>{});
+  else if (ntw > 2) run(std::integral_constant<int, 3>{});
+  else if (ntw > 1) run(std::integral_constant<int, 2>{});
+  else if (ntw > 0) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
+
+  float sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sc[j] = p.s2[static_cast<int64_t>(e) * H + hb + wn * 64 + 16 * j + col];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    if (mt < ntw) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = p.sorted_ids[row0 + wm * 64 + mt * 16 + kg * 4 + i];
+        if (f < Tk) {
+          float* yr = p.y + static_cast<int64_t>(f) * H + hb + wn * 64 + col;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yr[16 * j] = acc[mt][j][i] * sc[j];
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gemm2_w8_big(const Gemm2Args& p, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(p.H / k2Cols), static_cast<unsigned>(p.cap / k2Rows));
+  hipLaunchKernelGGL(gemm2_big_kernel, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm1_w8_big(const Gemm1Args& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.I / kOut), static_cast<unsigned>(p.cap / kRows));

@@ -66,10 +66,10 @@ hipError_t launch_gemm2_w8_stream(const Gemm2Args& p, int kw, hipStream_t stream
 // LDS-staged variants: GEMM1 for blocks of 32 or 64 rows (kw <= 2 at 32, 1 at 64); GEMM2 for
 // blocks of 16, 32 or 64 rows (kw <= 2 at 16, else 1), nt = 16-column tiles per wave (2 or 4).
 hipError_t launch_gemm1_w8_lds(const Gemm1Args& p, int kw, int ng, hipStream_t stream);
-// Large-block GEMM2 (block_m == 256): LDS-staged activations, register-held weights.
-hipError_t launch_gemm2_w8_prefill(const Gemm2Args& p, hipStream_t stream);
-// block_m == 256 GEMM1 with both operands copied straight into a 3-stage LDS ring.
+// block_m == 256 GEMMs with both operands copied straight into a 3-stage LDS ring
+// (GEMM2 needs H to be a multiple of 256).
 hipError_t launch_gemm1_w8_big(const Gemm1Args& p, hipStream_t stream);
+hipError_t launch_gemm2_w8_big(const Gemm2Args& p, hipStream_t stream);
 hipError_t launch_gemm2_w8_lds(const Gemm2Args& p, int kw, int nt, hipStream_t stream);
 
 struct Gemm1W4Args {
