@@ -20,7 +20,9 @@
 //   * the 16-byte chunks of every LDS row are XOR-swizzled by row so that the
 //     16 rows one MFMA operand read touches fall in distinct bank groups;
 //   * each wave converts its 4 weight fragments (int8 -> bf16/fp16, exact)
-//     once per stage and reuses each for its 8 row tiles.
+//     once per stage and reuses each for its 8 row tiles; all activation
+//     fragments of a stage are read first, then the column tiles are walked
+//     one by one so the conversion of one overlaps the MFMAs of the last.
 // Inside a stage, lane (col, kg) feeds K [16kg, 16kg+8) to the first MFMA and
 // [16kg+8, 16kg+16) to the second, for both operands (a dot product does not
 // depend on the order of its terms).
@@ -165,21 +167,25 @@ __global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) 
       if (s + 2 < nst) issue(s + 2, slot == 0 ? 2 : slot - 1);
       const uint8_t* st = smem + slot * kStageBytes;
 
-      u32x4 b[4][2];
+      // all activation fragments of the stage first, then column tile by
+      // column tile: converting tile j+1 overlaps the MFMAs of tile j
+      u32x4 q[4], af[MT > 0 ? MT : 1][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(st + boff[j]);
-        i8x16_to_operands<F16>(q, b[j][0], b[j][1]);
-      }
+      for (int j = 0; j < 4; ++j) q[j] = *reinterpret_cast<const u32x4*>(st + boff[j]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const uint8_t* ar = st + mt / 4 * 64 * kARow;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ar + aoff[mt & 3][0]);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ar + aoff[mt & 3][1]);
+        af[mt][0] = *reinterpret_cast<const u32x4*>(ar + aoff[mt & 3][0]);
+        af[mt][1] = *reinterpret_cast<const u32x4*>(ar + aoff[mt & 3][1]);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mt][j] = mfma16<F16>(a0, b[j][0], acc[mt][j]);
+      for (int j = 0; j < 4; ++j) {
+        u32x4 b[2];
+        i8x16_to_operands<F16>(q[j], b[0], b[1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mt][j] = mfma16<F16>(a1, b[j][1], acc[mt][j]);
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16<F16>(af[mt][ks], b[ks], acc[mt][j]);
       }
       slot = slot == kStages - 1 ? 0 : slot + 1;
     }
@@ -318,22 +324,26 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_kernel(const Gemm2Args p) 
       if (s + 2 < nst) issue(s + 2, slot == 0 ? 2 : slot - 1);
       const uint8_t* st = smem + slot * k2StageBytes;
 
-      u32x4 b[4][2];
+      u32x4 q[4], ah[MT > 0 ? MT : 1][2], al[MT > 0 ? MT : 1][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(st + boff[j]);
-        i8x16_to_operands<false>(q, b[j][0], b[j][1]);
-      }
+      for (int j = 0; j < 4; ++j) q[j] = *reinterpret_cast<const u32x4*>(st + boff[j]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 ah = *reinterpret_cast<const u32x4*>(st + aoff[mt][ks]);
-          const u32x4 al = *reinterpret_cast<const u32x4*>(st + k2Rows * kARow + aoff[mt][ks]);
+          ah[mt][ks] = *reinterpret_cast<const u32x4*>(st + aoff[mt][ks]);
+          al[mt][ks] = *reinterpret_cast<const u32x4*>(st + k2Rows * kARow + aoff[mt][ks]);
+        }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[mt][j] = mfma16_bf16(ah, b[j][ks], acc[mt][j]);
+      for (int j = 0; j < 4; ++j) {
+        u32x4 b[2];
+        i8x16_to_operands<false>(q[j], b[0], b[1]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[mt][j] = mfma16_bf16(al, b[j][ks], acc[mt][j]);
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16_bf16(ah[mt][ks], b[ks], acc[mt][j]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16_bf16(al[mt][ks], b[ks], acc[mt][j]);
         }
       }
       slot = slot == kStages - 1 ? 0 : slot + 1;
