@@ -66,10 +66,14 @@ bool use_prefill(int64_t bm) { return bm == 256; }
 
 bool use_stream(int64_t bm) { return bm <= 64; }
 
-// Rough count of align blocks that hold rows (the exact count stays on the device).
+// Rough count of align blocks that hold rows (the exact count stays on the
+// device): the blocks the assignments fill, plus half a block of padding for
+// each expert expected to be hit when T tokens pick k of E at random.
 int64_t blocks_estimate(int64_t T, int64_t E, int64_t k, int64_t bm) {
   const int64_t tk = T * k;
-  const int64_t ne = E < tk ? E : tk;
+  const double miss = std::pow(1.0 - static_cast<double>(k) / static_cast<double>(E), static_cast<double>(T));
+  const int64_t hit = static_cast<int64_t>(std::ceil(static_cast<double>(E) * (1.0 - miss)));
+  const int64_t ne = hit < tk ? hit : tk;
   return (tk + bm - 1) / bm + ne / 2;
 }
 
@@ -96,7 +100,7 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
 
 // ---- GEMM2 ----
 // LDS kernel (blocks of 16, 32 or 64 rows): 4 or 2 column tiles per wave and
-// K cut into `splits` parts so that about 768 workgroups are in flight.
+// K cut into `splits` parts so that about 512 workgroups are in flight.
 bool gemm2_lds(int64_t bm) { return bm == 16 || bm == 32 || bm == 64; }
 
 int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
@@ -127,7 +131,7 @@ Gemm2Plan gemm2_plan(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int6
   if (gemm2_lds(bm)) {
     const int64_t groups = (H / (64 * gemm2_nt(T, H, E, k, bm))) * blocks;
     int64_t sp = 1;
-    while (sp * 2 <= 16 && sp * 2 <= steps && groups * sp * 2 <= 768) sp *= 2;
+    while (sp * 2 <= 16 && sp * 2 <= steps && groups * sp * 2 <= 512) sp *= 2;
     return {sp, 1};
   }
   // register-streaming kernel (blocks of 48 rows)
@@ -143,7 +147,7 @@ int64_t splits_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_
 }
 
 // uint4 GEMM2 splits: the streaming kernel (blocks of 16/32/64 rows) takes any
-// count up to I/128 (about 768 workgroups in flight); the tiled kernel needs
+// count up to I/128 (about 512 workgroups in flight); the tiled kernel needs
 // equal parts of whole 128-wide steps.
 bool w4_stream(int64_t bm) { return bm == 16 || bm == 32 || bm == 64; }
 
@@ -151,7 +155,7 @@ int64_t w4_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t
   if (!w4_stream(bm)) return gemm2_plan(T, H, I, E, k, bm, true).splits;
   const int64_t groups = (H / 128) * blocks_estimate(T, E, k, bm);
   int64_t sp = 1;
-  while (sp * 2 <= 16 && sp * 2 <= I / 128 && groups * sp * 2 <= 768) sp *= 2;
+  while (sp * 2 <= 16 && sp * 2 <= I / 128 && groups * sp * 2 <= 512) sp *= 2;
   return sp;
 }
 

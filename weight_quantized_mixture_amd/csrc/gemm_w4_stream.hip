@@ -13,7 +13,8 @@
 // group scale of the lane's column before it joins the running total, so the
 // scale never rounds a weight.  The weights of the next three steps are in
 // flight while a step is converted and multiplied (packed rows are short, so a
-// wave needs several steps of loads outstanding to cover HBM latency).
+// wave needs several steps of loads outstanding to cover HBM latency); the
+// group scales and zero words travel with them.
 //
 // fp16 activations: 0x6400 | q is the half 1024 + q and one packed subtraction
 // of 1024 + z leaves q - z exactly; decoding nibble pairs (q_i, q_{i+4}) puts
@@ -195,40 +196,53 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weights of the next kPF steps are in flight while a step is multiplied
+  // weights, group scales and zero words of the next kPF steps are in flight
+  // while a step is multiplied (a scale or zero fetched in its own step would
+  // put a full memory latency on every step)
   constexpr int kPF = 3;
-  auto wload = [&](int s, u32x4 (&v)[NT]) {
-    const int64_t kq = sbeg + (s < nsteps ? s : nsteps - 1);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) v[j] = ld16(wp[j] + kq * (kStep / 8));
+  struct Pre {
+    u32x4 w[NT];
+    uint32_t sz[NT];   // fp16 scale bits (low half) | zero code << 16
   };
-  u32x4 areg[NPLANE][CPT];
-  u32x4 wv[NT], w1[NT], w2[NT];
+  auto wload = [&](int s, Pre& v) {
+    const int64_t kq = sbeg + (s < nsteps ? s : nsteps - 1);
+    const int64_t grp = kq * kStep / g;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      v.w[j] = ld16(wp[j] + kq * (kStep / 8));
+      v.sz[j] = static_cast<uint32_t>(sp[j][grp]) | (zero_code(qz_e, G, grp, nrow[j]) << 16);
+    }
+  };
+  // activation rows of the next kPF steps wait in registers (a0 = step s+1)
+  u32x4 a0[NPLANE][CPT], a1[NPLANE][CPT], a2[NPLANE][CPT];
+  Pre q0, q1, q2;
   if (nsteps > 0) {
-    load_a(0, areg);
-    wload(0, wv);
-    wload(1, w1);
-    wload(2, w2);
-    store_a(0, areg);
+    load_a(0, a0);
+    wload(0, q0);
+    wload(1, q1);
+    wload(2, q2);
+    store_a(0, a0);
+    if (nsteps > 1) load_a(1, a0);
+    if (nsteps > 2) load_a(2, a1);
+    if (nsteps > 3) load_a(3, a2);
   }
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
     const bool more = s + 1 < nsteps;
-    if (more) load_a(s + 1, areg);
-    const int64_t ks = sbeg + s;
-    u32x4 nv[NT];
-    wload(s + kPF, nv);
-    const int64_t grp = ks * kStep / g;
+    u32x4 an[NPLANE][CPT];
+    if (s + kPF + 1 < nsteps) load_a(s + kPF + 1, an);
+    Pre pn;
+    wload(s + kPF, pn);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const uint32_t z = zero_code(qz_e, G, grp, nrow[j]);
-      const float scale = f16_to_f32(sp[j][grp]);
+      const uint32_t z = q0.sz[j] >> 16;
+      const float scale = f16_to_f32(static_cast<uint16_t>(q0.sz[j] & 0xffffu));
       u32x4 b[4];
-      b[0] = w4_op<F16>(wv[j].x, z);
-      b[1] = w4_op<F16>(wv[j].y, z);
-      b[2] = w4_op<F16>(wv[j].z, z);
-      b[3] = w4_op<F16>(wv[j].w, z);
+      b[0] = w4_op<F16>(q0.w[j].x, z);
+      b[1] = w4_op<F16>(q0.w[j].y, z);
+      b[2] = w4_op<F16>(q0.w[j].z, z);
+      b[3] = w4_op<F16>(q0.w[j].w, z);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt < ntiles) {
@@ -247,13 +261,18 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
         }
       }
     }
+    q0 = q1;
+    q1 = q2;
+    q2 = pn;
+    if (more) store_a(buf ^ 1, a0);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      wv[j] = w1[j];
-      w1[j] = w2[j];
-      w2[j] = nv[j];
-    }
-    if (more) store_a(buf ^ 1, areg);
+    for (int pl = 0; pl < NPLANE; ++pl)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        a0[pl][c] = a1[pl][c];
+        a1[pl][c] = a2[pl][c];
+        a2[pl][c] = an[pl][c];
+      }
     __syncthreads();
   }
 
