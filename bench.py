@@ -383,7 +383,7 @@ def gemm1_kernel_name(block_m, H):
     """Name prefix of the GEMM1 kernel the library launches for this block size."""
     if block_m == 256:
         return "gemm1_big_kernel"
-    if block_m in (32, 64) and (block_m == 64 or H % 256 == 0):
+    if block_m in (32, 64):
         return "gemm1_lds_kernel"
     if block_m <= 64:
         return "gemm1_stream_kernel"

@@ -93,7 +93,7 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
   if (use_prefill(p.block_m)) return moe::launch_gemm1_w8_big(p, stream);
   if (!use_stream(p.block_m)) return moe::launch_gemm1_w8(p, stream);
   const int mt = p.block_m / 16;
-  if (mt == 2 && p.H % 256 == 0) return moe::launch_gemm1_w8_lds(p, 2, 1, stream);
+  if (mt == 2) return moe::launch_gemm1_w8_lds(p, 1, 1, stream);
   if (mt == 4) return moe::launch_gemm1_w8_lds(p, 1, 1, stream);
   return moe::launch_gemm1_w8_stream(p, gemm1_kways(T, p.H, p.I, E, p.k, p.block_m), stream);
 }
