@@ -299,15 +299,16 @@ def main():
         s_ids = torch.empty(cap, dtype=torch.int32, device=dev)
         b_exp = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
         npad = torch.empty(1, dtype=torch.int32, device=dev)
-        a_buf = torch.empty(cap, I, dtype=torch.float32, device=dev)
+        a_buf = torch.empty(pkg.moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m) // 4 + 64, dtype=torch.float32,
+                            device=dev)
         y_buf = torch.empty(splits, T * k, H, dtype=torch.float32, device=dev)
-        names = ["route", "align", "gemm1", "gemm2", "combine"]
+        names = ["route", "align", "gemm1", "requant", "gemm2", "combine"]
         acc = {n: [] for n in names}
         reps = max(5, min(args.steps, 20))
         for i in range(reps + 2):
             if flush is not None:
                 evict()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
             ev[0].record(stream)
             pkg.moe_route_topk(logits, k, wl.renormalize, tw, ti, stream)
             ev[1].record(stream)
@@ -315,11 +316,13 @@ def main():
             ev[2].record(stream)
             pkg.moe_w8a16_gemm1(x, layer.w13_weight, layer.w13_scale, s_ids, b_exp, npad, block_m, k, a_buf, stream)
             ev[3].record(stream)
+            pkg.moe_w8a16_requant(a_buf, T, I, E, k, s_ids, npad, block_m, stream)
+            ev[4].record(stream)
             pkg.moe_w8a16_gemm2(a_buf, T, k, layer.w2_weight, layer.w2_scale, s_ids, b_exp, npad, block_m, splits,
                                 y_buf, stream)
-            ev[4].record(stream)
-            pkg.moe_combine_topk(y_buf, splits, tw, ti, E, out, stream)
             ev[5].record(stream)
+            pkg.moe_combine_topk(y_buf, splits, tw, ti, E, out, stream)
+            ev[6].record(stream)
             torch.cuda.synchronize()
             if i >= 2:
                 for j, n in enumerate(names):

@@ -160,34 +160,49 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
 /* ------------------------------------------------------------------------
  * Stages of the forward, exported so that each kernel can be checked and
  * timed alone.  moe_w8a16_forward is exactly moe_align_block followed by
- * these three calls on the workspace regions.
+ * these four calls on the workspace regions.
  *
  * moe_w8a16_gemm1: for every padded row r < *num_padded with
  * f = sorted_ids[r] < T*k, t = f / k, e = block_expert[r / block_m]:
  *   v[r, i] = silu(h_i) * h_{I+i},  h_n = w13_scale[e,n] * sum_c x[t,c] w13[e,n,c]
- * stored as two bf16 planes, hi = rne(v) and lo = rne(v - hi) (16
- * significant bits): `a` is device bf16 [2, cap, I] (hi plane first) with
- * cap = moe_align_capacity; passed as float* for 4-byte alignment.  Padding
+ * `a` is the intermediate, device memory of moe_w8a16_intermediate_bytes
+ * bytes (16-byte aligned; passed as float*).  gemm1 writes its first part,
+ * two bf16 planes [2, cap, I] (hi plane first), hi = rne(v) and
+ * lo = rne(v - hi) (16 significant bits), cap = moe_align_capacity.  Padding
  * rows of a block that holds rows get v = 0; 16-row groups made only of
  * padding may be left unwritten (GEMM2 never reads them).
  *
+ * moe_w8a16_requant: for block_m <= 64 (a no-op otherwise) turns the planes
+ * into the 16-bit fixed-point form the integer GEMM2 reads, stored right
+ * after them (at byte offset round_up(4*cap*I, 256)): int8 hi codes
+ * [cap, I], then int8 lo codes [cap, I] (each region rounded up to 256
+ * bytes), then fp32 scales [cap, I/128], with
+ * v ~= s[r, i/128] * (256 * hi + lo), s = max |v| over the 128-column group
+ * / 32639 and |error| <= s/2 (the same rows as gemm1).
+ *
  * moe_w8a16_gemm2: for every valid padded row r (f = sorted_ids[r] < T*k),
  * split s < splits, h < H:
- *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} (hi + lo)[r, i] w2[e,h,i]
- * The K range [0, I) is cut into `splits` parts of whole 128-wide steps
- * (1 <= splits <= I/128; equal parts, so splits must divide I/128, when
- * block_m > 64).  y is device fp32 [splits, T*k, H]; rows of dropped ids are
- * not written.  moe_w8a16_splits gives the split count the forward uses.
+ *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} v[r, i] w2[e,h,i]
+ * with v as moe_w8a16_gemm1 and moe_w8a16_requant left it in `a` (the
+ * fixed-point form for block_m <= 64, the hi + lo planes otherwise).  The K range [0, I) is cut
+ * into `splits` parts of whole 128-wide steps (1 <= splits <= I/128; equal
+ * parts, so splits must divide I/128, when block_m > 64; 1 when block_m is
+ * 256).  y is device fp32 [splits, T*k, H]; rows of dropped ids are not
+ * written.  moe_w8a16_splits gives the split count the forward uses.
  *
  * moe_combine_topk: out[t, h] = sum_j topk_w[t,j] * sum_s y[s, t*k+j, h]
  * over the j with topk_ids in [0, E), in fp32 with j and s ascending, cast
  * to act_dtype (round to nearest even).
  * ---------------------------------------------------------------------- */
 int64_t moe_w8a16_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m);
+/* Bytes of the intermediate buffer `a` of the stage calls (0 for T <= 0). */
+size_t moe_w8a16_intermediate_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m);
 int moe_w8a16_gemm1(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
                     int64_t k, const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
                     const int32_t* sorted_ids, const int32_t* block_expert,
                     const int32_t* num_padded, int64_t block_m, float* a, hipStream_t stream);
+int moe_w8a16_requant(float* a, int64_t T, int64_t I, int64_t E, int64_t k, const int32_t* sorted_ids,
+                      const int32_t* num_padded, int64_t block_m, hipStream_t stream);
 int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                     const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
                     const int32_t* sorted_ids, const int32_t* block_expert,

@@ -113,6 +113,24 @@ def test_other_argument_errors():
     assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 128, 3,
                              p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # tiled kernels need equal splits
     assert L.moe_combine_topk(p(FAKE), 1, 4, 2, 256, 8, p(FAKE), p(FAKE), 5, p(FAKE), None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_w8a16_requant(p(FAKE), 4, 500, 8, 2, p(FAKE), p(FAKE), 32, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT                         # I not a multiple of 128
+    assert L.moe_w8a16_requant(p(FAKE), 4, 512, 8, 2, p(FAKE), p(FAKE), 40, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 32, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 128, None) == B.MOE_OK   # nothing to do at 128
+    assert L.moe_w8a16_requant(None, 0, 512, 8, 2, None, None, 32, None) == B.MOE_OK
+
+
+def test_intermediate_bytes():
+    """bf16 planes, plus the fixed-point codes and scales for blocks of at most 64 rows."""
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    for T, E, k, bm, I in [(4, 8, 2, 16, 512), (64, 8, 2, 32, 14336), (300, 8, 2, 128, 1024), (9, 64, 6, 64, 1408)]:
+        cap = B.moe_align_capacity(T, k, E, bm)
+        want = up(4 * cap * I)
+        if bm <= 64:
+            want += 2 * up(cap * I) + up(cap * (I // 128) * 4)
+        assert B.moe_w8a16_intermediate_bytes(T, 4096, I, E, k, bm) == want
+    assert B.moe_w8a16_intermediate_bytes(0, 4096, 512, 8, 2, 16) == 0
 
 
 def test_binding_raises_python_errors():

@@ -168,13 +168,35 @@ def test_gemm1_intermediate(act, bm):
     b = torch.empty(cap // bm, dtype=torch.int32, device=DEV)
     n = torch.empty(1, dtype=torch.int32, device=DEV)
     pkg.moe_align_block(ti, E, bm, s, b, n)
-    a = torch.full((2 * cap * I,), 0x7FC0, dtype=torch.int16, device=DEV)   # bf16 NaN fill
+    nbytes = pkg.moe_w8a16_intermediate_bytes(T, H, I, E, k, bm)
+    a = torch.full(((nbytes + 1) // 2,), 0x7FC0, dtype=torch.int16, device=DEV)   # bf16 NaN fill
     x = to_dev_act(xb, act)
     pkg.moe_w8a16_gemm1(x, W.w13, W.s13, s, b, n, bm, k, a)
+    pkg.moe_w8a16_requant(a, T, I, E, k, s, n, bm)
     torch.cuda.synchronize()
     sr, br, nr = oracle.align_block(ids_ref, E, bm)
-    planes = a.cpu().numpy().view(np.uint16).reshape(2, cap, I)
+    raw = a.cpu().numpy().view(np.uint8)
+    planes = raw[:4 * cap * I].view(np.uint16).reshape(2, cap, I)
     a_g = oracle.bf16_bits_to_f64(planes[0]) + oracle.bf16_bits_to_f64(planes[1])
+    if bm <= 64:
+        # the 16-bit fixed-point form after the planes: v ~= s * (256 hi + lo) per (row, 128 columns)
+        up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+        o = up(4 * cap * I)
+        qh = raw[o:o + cap * I].view(np.int8).reshape(cap, I).astype(np.int64)
+        o += up(cap * I)
+        ql = raw[o:o + cap * I].view(np.int8).reshape(cap, I).astype(np.int64)
+        o += up(cap * I)
+        qs = raw[o:o + cap * (I // 128) * 4].view(np.float32).reshape(cap, I // 128).astype(np.float64)
+        assert qh.min() >= -127 and qh.max() <= 127
+        for blk in range(nr // bm):
+            rows = sr[blk * bm:(blk + 1) * bm]
+            for r_local in range(16 * ((np.sum(rows < T * k) + 15) // 16)):
+                r = blk * bm + r_local
+                sc = np.repeat(qs[r], 128)
+                gmax = np.abs(a_g[r]).reshape(-1, 128).max(axis=1)
+                assert np.allclose(qs[r], gmax / 32639.0, rtol=1e-6, atol=0.0), (blk, r_local)
+                vq = sc * (256.0 * qh[r] + ql[r])
+                assert np.all(np.abs(vq - a_g[r]) <= 0.51 * sc + 1e-30), (blk, r_local)
     xf = oracle.act_bits_to_f64(xb, act)
     for blk in range(nr // bm):
         e = br[blk]

@@ -24,6 +24,8 @@ from .binding import (  # noqa: F401
     moe_w8a16_gemm1,
     moe_w8a16_gemm2,
     moe_w8a16_splits,
+    moe_w8a16_intermediate_bytes,
+    moe_w8a16_requant,
     moe_w8a16_workspace_bytes,
 )
 from .layer import W4A16MoE, W8A16MoE  # noqa: F401

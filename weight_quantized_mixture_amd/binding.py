@@ -47,6 +47,8 @@ SIGNATURES = {
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_w8a16_splits": (_c_i64, [_c_i64] * 6),
+    "moe_w8a16_intermediate_bytes": (_c_size, [_c_i64] * 6),
+    "moe_w8a16_requant": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p]),
     "moe_w8a16_gemm1": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p]),
     "moe_w8a16_gemm2": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
@@ -188,6 +190,15 @@ def moe_w8a16_splits(T, H, I, E, k, block_m=0) -> int:
     return int(lib().moe_w8a16_splits(T, H, I, E, k, block_m))
 
 
+def moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m=0) -> int:
+    return int(lib().moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m))
+
+
+def _need_bytes(t: torch.Tensor, nbytes: int, name: str):
+    if not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: needs a contiguous buffer of at least {nbytes} bytes")
+
+
 def moe_w8a16_workspace_bytes(T, H, I, E, k, block_m=0) -> int:
     return int(lib().moe_w8a16_workspace_bytes(T, H, I, E, k, block_m))
 
@@ -227,15 +238,23 @@ def moe_w8a16_gemm1(x, w13, w13_scale, sorted_ids, block_expert, num_padded, blo
     E, N2, _ = w13.shape
     I = N2 // 2
     ld13 = _row_stride(w13, torch.int8, (E, N2, H), "w13")
+    _need_bytes(a, moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m), "a")
     _check(lib().moe_w8a16_gemm1(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13,
                                  _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), block_m, _ptr(a),
                                  _stream(stream)), "moe_w8a16_gemm1")
+
+
+def moe_w8a16_requant(a, T, I, E, k, sorted_ids, num_padded, block_m, stream=None):
+    _need_bytes(a, moe_w8a16_intermediate_bytes(T, 128, I, E, k, block_m), "a")
+    _check(lib().moe_w8a16_requant(_ptr(a), T, I, E, k, _ptr(sorted_ids), _ptr(num_padded), block_m,
+                                   _stream(stream)), "moe_w8a16_requant")
 
 
 def moe_w8a16_gemm2(a, T, k, w2, w2_scale, sorted_ids, block_expert, num_padded, block_m, splits, y,
                     stream=None):
     E, H, I = w2.shape
     ld2 = _row_stride(w2, torch.int8, (E, H, I), "w2")
+    _need_bytes(a, moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m), "a")
     _check(lib().moe_w8a16_gemm2(_ptr(a), T, H, I, E, k, _ptr(w2), _ptr(w2_scale), ld2, _ptr(sorted_ids),
                                  _ptr(block_expert), _ptr(num_padded), block_m, splits, _ptr(y),
                                  _stream(stream)), "moe_w8a16_gemm2")

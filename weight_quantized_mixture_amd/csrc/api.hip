@@ -99,26 +99,27 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
 }
 
 // ---- GEMM2 ----
-// LDS kernel (blocks of 16, 32 or 64 rows): 4 or 2 column tiles per wave and
-// K cut into `splits` parts so that about 512 workgroups are in flight.
-bool gemm2_lds(int64_t bm) { return bm == 16 || bm == 32 || bm == 64; }
+// Blocks of at most 64 rows: integer-MFMA kernel on the 16-bit fixed-point
+// form of a (requantized after GEMM1), 4 or 2 column tiles per wave and K cut
+// into `splits` parts so that about 512 workgroups are in flight.  256-row
+// blocks: the LDS-ring kernel on the bf16 planes.  Other block sizes: the
+// generic tiled kernel (equal splits of whole 128-wide steps).
+bool gemm2_int8(int64_t bm) { return bm <= 64; }
 
-int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
-  if (bm == 64) return 2;   // 4 x 4 accumulator tiles would leave one wave per SIMD
-  return (H / 256) * blocks_estimate(T, E, k, bm) >= 64 ? 4 : 2;
+// Expected rows per active expert above half a tile: more MFMA work per
+// weight byte, so narrower waves (more workgroups) stream better.
+int gemm2_nt(int64_t T, int64_t E, int64_t k, int64_t bm) {
+  if (bm == 64) return 2;
+  const double miss = std::pow(1.0 - static_cast<double>(k) / static_cast<double>(E), static_cast<double>(T));
+  const double hit = static_cast<double>(E) * (1.0 - miss);
+  return static_cast<double>(T * k) / (hit > 1.0 ? hit : 1.0) > 8.0 ? 2 : 4;
 }
 
-struct Gemm2Plan {
-  int64_t splits;
-  int kw;
-};
-
-Gemm2Plan gemm2_plan(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm,
-                     bool tiled = false) {
+int64_t gemm2_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, bool tiled = false) {
   const int64_t steps = I / 128;
   const int64_t blocks = blocks_estimate(T, E, k, bm);
-  if (!tiled && use_prefill(bm)) return {1, 1};
-  if (tiled || !use_stream(bm)) {
+  if (!tiled && use_prefill(bm)) return 1;
+  if (tiled || !gemm2_int8(bm)) {
     // tiled kernel: 128 columns x one split per workgroup, equal splits
     const int64_t ntiles = H / 128;
     int64_t want = 1;
@@ -126,24 +127,16 @@ Gemm2Plan gemm2_plan(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int6
     int64_t best = 1;
     for (int64_t sp = 1; sp <= want && sp <= steps; ++sp)
       if (steps % sp == 0) best = sp;
-    return {best, 1};
+    return best;
   }
-  if (gemm2_lds(bm)) {
-    const int64_t groups = (H / (64 * gemm2_nt(T, H, E, k, bm))) * blocks;
-    int64_t sp = 1;
-    while (sp * 2 <= 16 && sp * 2 <= steps && groups * sp * 2 <= 512) sp *= 2;
-    return {sp, 1};
-  }
-  // register-streaming kernel (blocks of 48 rows)
-  const int64_t waves1 = (H / 32) * blocks;
-  int64_t ways = 1;
-  while (ways < 32 && waves1 * ways < kTargetWaves && steps >= 2 * ways) ways *= 2;
-  const int kw = ways >= 4 ? 4 : static_cast<int>(ways);
-  return {ways / kw, kw};
+  const int64_t groups = (H / (64 * gemm2_nt(T, E, k, bm))) * blocks;
+  int64_t sp = 1;
+  while (sp * 2 <= 16 && sp * 2 <= steps && groups * sp * 2 <= 512) sp *= 2;
+  return sp;
 }
 
 int64_t splits_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
-  return gemm2_plan(T, H, I, E, k, bm).splits;
+  return gemm2_splits(T, H, I, E, k, bm);
 }
 
 // uint4 GEMM2 splits: the streaming kernel (blocks of 16/32/64 rows) takes any
@@ -152,29 +145,52 @@ int64_t splits_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_
 bool w4_stream(int64_t bm) { return bm == 16 || bm == 32 || bm == 64; }
 
 int64_t w4_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
-  if (!w4_stream(bm)) return gemm2_plan(T, H, I, E, k, bm, true).splits;
+  if (!w4_stream(bm)) return gemm2_splits(T, H, I, E, k, bm, true);
   const int64_t groups = (H / 128) * blocks_estimate(T, E, k, bm);
   int64_t sp = 1;
   while (sp * 2 <= 16 && sp * 2 <= I / 128 && groups * sp * 2 <= 512) sp *= 2;
   return sp;
 }
 
-// In-workgroup K ways of the register-streaming GEMM2 for a given split count.
-int gemm2_kw_for(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, int64_t splits) {
-  const Gemm2Plan pl = gemm2_plan(T, H, I, E, k, bm);
-  if (pl.splits == splits) return pl.kw;
-  const int64_t steps = I / 128;
-  int kw = 1;
-  while (kw < 4 && splits * kw * 2 <= steps) kw *= 2;
-  return kw;
+// The intermediate: bf16 hi/lo planes [2, cap, I]; for blocks of at most 64
+// rows followed by the int8 hi codes [cap, I], lo codes [cap, I] and fp32
+// scales [cap, I/128] the integer GEMM2 reads.
+struct Q16 {
+  int8_t* hi;
+  int8_t* lo;
+  float* scale;
+};
+
+size_t planes_bytes(int64_t cap, int64_t I) { return align_up(static_cast<size_t>(cap) * static_cast<size_t>(I) * 4); }
+
+size_t intermediate_bytes(int64_t cap, int64_t I, int64_t bm, bool w8) {
+  size_t b = planes_bytes(cap, I);
+  if (w8 && gemm2_int8(bm)) {
+    b += 2 * align_up(static_cast<size_t>(cap) * static_cast<size_t>(I));
+    b += align_up(static_cast<size_t>(cap) * static_cast<size_t>(I / 128) * 4);
+  }
+  return b;
+}
+
+Q16 q16_of(const float* a, int64_t cap, int64_t I) {
+  char* base = const_cast<char*>(reinterpret_cast<const char*>(a)) + planes_bytes(cap, I);
+  const size_t codes = align_up(static_cast<size_t>(cap) * static_cast<size_t>(I));
+  return Q16{reinterpret_cast<int8_t*>(base), reinterpret_cast<int8_t*>(base + codes),
+             reinterpret_cast<float*>(base + 2 * codes)};
+}
+
+hipError_t run_gemm1_and_requant(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t stream) {
+  hipError_t e = run_gemm1(p, T, E, stream);
+  if (e != hipSuccess || !gemm2_int8(p.block_m)) return e;
+  const Q16 q = q16_of(p.a, p.cap, p.I);
+  return moe::launch_requant_q16(p.a, p.cap, p.I, p.sorted_ids, p.num_padded, p.Tk, q.hi, q.lo, q.scale, stream);
 }
 
 hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, hipStream_t stream) {
   if (use_prefill(p.block_m) && p.H % 256 == 0) return moe::launch_gemm2_w8_big(p, stream);
-  if (!use_stream(p.block_m)) return moe::launch_gemm2_w8(p, stream);
-  if (gemm2_lds(p.block_m))
-    return moe::launch_gemm2_w8_lds(p, 1, gemm2_nt(T, p.H, E, k, p.block_m), stream);
-  return moe::launch_gemm2_w8_stream(p, gemm2_kw_for(T, p.H, p.I, E, k, p.block_m, p.splits), stream);
+  if (!gemm2_int8(p.block_m)) return moe::launch_gemm2_w8(p, stream);
+  const Q16 q = q16_of(p.a, p.cap, p.I);
+  return moe::launch_gemm2_q16(p, gemm2_nt(T, E, k, p.block_m), q.hi, q.lo, q.scale, stream);
 }
 
 struct Layout {
@@ -182,7 +198,7 @@ struct Layout {
   size_t off_sorted, off_block, off_npad, off_a, off_y, total;
 };
 
-Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, int64_t splits) {
+Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, int64_t splits, bool w8) {
   Layout L{};
   L.cap = capacity(T, k, E, bm);
   L.nblocks = bm > 0 ? L.cap / bm : 0;
@@ -191,7 +207,7 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm,
   L.off_sorted = o; o += align_up(static_cast<size_t>(L.cap) * 4);
   L.off_block = o;  o += align_up(static_cast<size_t>(L.nblocks) * 4);
   L.off_npad = o;   o += align_up(4);
-  L.off_a = o;      o += align_up(static_cast<size_t>(L.cap) * static_cast<size_t>(I) * 4);
+  L.off_a = o;      o += intermediate_bytes(L.cap, I, bm, w8);
   L.off_y = o;      o += align_up(static_cast<size_t>(splits) * static_cast<size_t>(T * k) *
                                   static_cast<size_t>(H) * 4);
   L.total = o;
@@ -321,7 +337,15 @@ size_t moe_w8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int
                                  int64_t block_m) {
   if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
   if (block_m == 0) block_m = auto_block_m(T, E, k);
-  return layout(T, H, I, E, k, block_m, splits_for(T, H, I, E, k, block_m)).total;
+  return layout(T, H, I, E, k, block_m, splits_for(T, H, I, E, k, block_m), true).total;
+}
+
+size_t moe_w8a16_intermediate_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m) {
+  (void)H;
+  if (T <= 0 || I < 1 || E < 1 || k < 1) return 0;
+  if (block_m == 0) block_m = auto_block_m(T, E, k);
+  if (block_m < 16 || block_m > 256 || block_m % 16) return 0;
+  return intermediate_bytes(capacity(T, k, E, block_m), I, block_m, true);
 }
 
 int moe_w8a16_gemm1(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
@@ -347,6 +371,21 @@ int moe_w8a16_gemm1(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
   return hip_status(run_gemm1(p, T, E, stream), "gemm1_w8");
 }
 
+int moe_w8a16_requant(float* a, int64_t T, int64_t I, int64_t E, int64_t k, const int32_t* sorted_ids,
+                      const int32_t* num_padded, int64_t block_m, hipStream_t stream) {
+  int st;
+  if (T < 0 || E < 1 || k < 1 || k > E) return fail(MOE_ERR_INVALID_ARGUMENT, "need T >= 0, 1 <= k <= E");
+  if (I < 128 || I % 128) return fail(MOE_ERR_INVALID_ARGUMENT, "I must be a positive multiple of 128");
+  if ((st = check_block_m(block_m)) != MOE_OK) return st;
+  if (T == 0 || !gemm2_int8(block_m)) return ok();
+  if (!a || !sorted_ids || !num_padded) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(a, 16)) return fail(MOE_ERR_INVALID_ARGUMENT, "a must be 16-byte aligned");
+  const int64_t cap = capacity(T, k, E, block_m);
+  const Q16 q = q16_of(a, cap, I);
+  return hip_status(moe::launch_requant_q16(a, cap, I, sorted_ids, num_padded, T * k, q.hi, q.lo, q.scale, stream),
+                    "requant");
+}
+
 int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                     const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
                     const int32_t* sorted_ids, const int32_t* block_expert,
@@ -357,7 +396,7 @@ int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, 
   if ((st = check_block_m(block_m)) != MOE_OK) return st;
   const int64_t ldw = w2_row_stride ? w2_row_stride : I;
   if (ldw < I || ldw % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "w2_row_stride must be >= I and a multiple of 16");
-  if (splits < 1 || splits > I / 128 || (!use_stream(block_m) && (I / 128) % splits != 0) ||
+  if (splits < 1 || splits > I / 128 || (!gemm2_int8(block_m) && (I / 128) % splits != 0) ||
       (use_prefill(block_m) && splits != 1))
     return fail(MOE_ERR_INVALID_ARGUMENT,
                 "splits must be in [1, I/128], divide I/128 when block_m > 64, and be 1 when block_m is 256");
@@ -419,7 +458,7 @@ int forward_w8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, in
       !aligned(workspace, kAlign))
     return fail(MOE_ERR_INVALID_ARGUMENT, "x, w13, w2 16-byte, out 8-byte, workspace 256-byte alignment required");
   const int64_t splits = splits_for(T, H, I, E, k, block_m);
-  const Layout L = layout(T, H, I, E, k, block_m, splits);
+  const Layout L = layout(T, H, I, E, k, block_m, splits, true);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
   char* ws = static_cast<char*>(workspace);
@@ -439,7 +478,7 @@ int forward_w8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, in
   p1.x = x; p1.f16 = act_dtype == MOE_FP16; p1.T = T; p1.H = H; p1.I = I; p1.k = k; p1.Tk = T * k;
   p1.w13 = w13; p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = sorted; p1.block_expert = blocks;
   p1.num_padded = npad; p1.block_m = static_cast<int>(block_m); p1.cap = L.cap; p1.a = a;
-  if ((e = run_gemm1(p1, T, E, stream)) != hipSuccess) return hip_status(e, "gemm1_w8");
+  if ((e = run_gemm1_and_requant(p1, T, E, stream)) != hipSuccess) return hip_status(e, "gemm1_w8");
   moe::Gemm2Args p2{};
   p2.a = a; p2.H = H; p2.I = I; p2.Tk = T * k; p2.w2 = w2; p2.s2 = w2_scale; p2.ldw = ld2;
   p2.sorted_ids = sorted; p2.block_expert = blocks; p2.num_padded = npad;
@@ -496,7 +535,7 @@ size_t moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int
                                  int64_t block_m) {
   if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
   if (block_m == 0) block_m = auto_block_m(T, E, k);
-  return layout(T, H, I, E, k, block_m, w4_splits(T, H, I, E, k, block_m)).total;
+  return layout(T, H, I, E, k, block_m, w4_splits(T, H, I, E, k, block_m), false).total;
 }
 
 }  // extern "C"
@@ -528,7 +567,7 @@ int forward_w4(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, in
       !aligned(workspace, kAlign))
     return fail(MOE_ERR_INVALID_ARGUMENT, "alignment: x and qweights 16 bytes, out 8, workspace 256");
   const int64_t splits = w4_splits(T, H, I, E, k, block_m);
-  const Layout L = layout(T, H, I, E, k, block_m, splits);
+  const Layout L = layout(T, H, I, E, k, block_m, splits, false);
   if (workspace_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
   char* ws = static_cast<char*>(workspace);

@@ -1,11 +1,10 @@
-// Weight-streaming grouped GEMMs with the activation tile staged in LDS
+// Weight-streaming grouped GEMM1 with the activation tile staged in LDS
 // (align blocks of 32 or 64 rows: the gathered activations are shared by the
 // four waves of a workgroup instead of being fetched once per wave).
 //
 // experts_int8 page, ExpertsInt8MoEMethod.create_weights / apply ->
 // fused_experts(use_int8_w8a16): GEMM1 h = x dequant(w13[e])^T (scale on the
-// fp32 accumulator), a = silu(h_gate) * h_up written as bf16 hi/lo planes;
-// GEMM2 y = (hi + lo) dequant(w2[e])^T.
+// fp32 accumulator), a = silu(h_gate) * h_up written as bf16 hi/lo planes.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -198,165 +197,6 @@ __global__ __launch_bounds__(kThreads) void gemm1_lds_kernel(const Gemm1Args p) 
   }
 }
 
-// GEMM2: same structure; the staged tile holds the hi and lo planes of a.
-template <int MT, int KW, int NT>
-__global__ __launch_bounds__(kThreads) void gemm2_lds_kernel(const Gemm2Args p) {
-  constexpr int CW = 4 / KW;
-  constexpr int KT = KW * kStep;
-  constexpr int PITCH = KT + 8;
-  constexpr int ROWS = 16 * MT;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][2][ROWS * PITCH];   // [buf][hi/lo]
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int cw = wave % CW;
-  const int kw = wave / CW;
-  const int col = lane & 15;
-  const int kg = lane >> 4;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * ROWS;
-  if (row0 >= *p.num_padded) return;
-  const int e = p.block_expert[blockIdx.y];
-  int ntiles = 0;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    if (p.sorted_ids[row0 + mt * 16] < p.Tk) ntiles = mt + 1;
-  const int nrows = ntiles * 16;
-
-  const int64_t I = p.I, H = p.H;
-  const int64_t h0 = static_cast<int64_t>(blockIdx.x) * (16 * NT * CW) + cw * 16 * NT;
-  const int total_iters = static_cast<int>(I / KT);
-  const int ib = static_cast<int>(blockIdx.z) * total_iters / p.splits;
-  const int iters = (static_cast<int>(blockIdx.z) + 1) * total_iters / p.splits - ib;
-  const int64_t kbase = static_cast<int64_t>(ib) * KT;
-  const int8_t* wbase = p.w2 + (static_cast<int64_t>(e) * H + h0 + col) * p.ldw + kbase + kw * kStep + kg * 16;
-  const int64_t tstride = 16 * p.ldw;
-  const uint16_t* a_hi = reinterpret_cast<const uint16_t*>(p.a);
-  const uint16_t* a_lo = a_hi + p.cap * I;
-
-  constexpr int QPR = KT / 8;
-  constexpr int CPT = (ROWS * QPR + kThreads - 1) / kThreads;
-  int64_t srco[CPT];
-  int dsto[CPT];
-  bool cvalid[CPT];
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int ci = tid + c * kThreads;
-    const int r = ci / QPR, q = ci % QPR;
-    cvalid[c] = r < nrows;
-    srco[c] = (row0 + r) * I + kbase + q * 8;
-    dsto[c] = r * PITCH + q * 8;
-  }
-  auto load_a = [&](int it, u32x4* rh, u32x4* rl) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      if (cvalid[c]) {
-        rh[c] = ld16(a_hi + srco[c] + static_cast<int64_t>(it) * KT);
-        rl[c] = ld16(a_lo + srco[c] + static_cast<int64_t>(it) * KT);
-      }
-    }
-  };
-  auto store_a = [&](int buf, const u32x4* rh, const u32x4* rl) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (cvalid[c]) {
-        *reinterpret_cast<u32x4*>(&As[buf][0][dsto[c]]) = rh[c];
-        *reinterpret_cast<u32x4*>(&As[buf][1][dsto[c]]) = rl[c];
-      }
-  };
-
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 rh[CPT], rl[CPT];
-  if (iters > 0) {
-    load_a(0, rh, rl);
-  }
-  u32x4 w0[NT], w1[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    // a split without iterations (never planned) reads nothing and writes zeros
-    w0[j] = iters > 0 ? ld16(wbase + j * tstride) : u32x4{0u, 0u, 0u, 0u};
-    w1[j] = iters > 0 ? ld16(wbase + j * tstride + 64) : u32x4{0u, 0u, 0u, 0u};
-  }
-  if (iters > 0) store_a(0, rh, rl);
-  __syncthreads();
-  for (int it = 0; it < iters; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < iters;
-    if (more) load_a(it + 1, rh, rl);
-    const int64_t kn = static_cast<int64_t>(more ? it + 1 : it) * KT;
-    u32x4 n0[NT], n1[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      n0[j] = ld16(wbase + j * tstride + kn);
-      n1[j] = ld16(wbase + j * tstride + kn + 64);
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      u32x4 b[4];
-      i8x16_to_operands<false>(w0[j], b[0], b[1]);
-      i8x16_to_operands<false>(w1[j], b[2], b[3]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (mt < ntiles) {
-          const int o = (mt * 16 + col) * PITCH + kw * kStep + kg * 16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int oi = o + (i >> 1) * 64 + (i & 1) * 8;
-            const u32x4 ah = *reinterpret_cast<const u32x4*>(&As[buf][0][oi]);
-            const u32x4 al = *reinterpret_cast<const u32x4*>(&As[buf][1][oi]);
-            acc[mt][j] = mfma16_bf16(ah, b[i], acc[mt][j]);
-            acc[mt][j] = mfma16_bf16(al, b[i], acc[mt][j]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      w0[j] = n0[j];
-      w1[j] = n1[j];
-    }
-    if (more) store_a(buf ^ 1, rh, rl);
-    __syncthreads();
-  }
-
-  if constexpr (KW > 1) {
-    f32x4* red = reinterpret_cast<f32x4*>(&As[0][0][0]);
-    if (kw > 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) red[((((kw - 1) * CW + cw) * MT + mt) * NT + j) * kWave + lane] = acc[mt][j];
-    }
-    __syncthreads();
-    if (kw > 0) return;
-#pragma unroll
-    for (int q = 0; q < KW - 1; ++q)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[mt][j] += red[(((q * CW + cw) * MT + mt) * NT + j) * kWave + lane];
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt < ntiles) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = p.sorted_ids[row0 + mt * 16 + kg * 4 + i];
-        if (f < p.Tk) {
-          float* yr = p.y + (static_cast<int64_t>(blockIdx.z) * p.Tk + f) * H + h0 + col;
-#pragma unroll
-          for (int j = 0; j < NT; ++j) yr[16 * j] = acc[mt][j][i] * p.s2[static_cast<int64_t>(e) * H + h0 + 16 * j + col];
-        }
-      }
-    }
-  }
-}
-
 #define G1L(MT, KW, NG, F16)                                                                        \
   hipLaunchKernelGGL((gemm1_lds_kernel<MT, KW, NG, F16>),                                         \
                      dim3(static_cast<unsigned>(p.I / (16 * NG * (4 / KW))),                      \
@@ -381,38 +221,11 @@ hipError_t g1l(const Gemm1Args& p, int mt, int kw, int ng, hipStream_t stream) {
 }
 #undef G1L
 
-#define G2L(MT, KW, NT)                                                                             \
-  hipLaunchKernelGGL((gemm2_lds_kernel<MT, KW, NT>),                                               \
-                     dim3(static_cast<unsigned>(p.H / (16 * NT * (4 / KW))),                       \
-                          static_cast<unsigned>(p.cap / p.block_m), static_cast<unsigned>(p.splits)), \
-                     dim3(kThreads), 0, stream, p)
-
-hipError_t g2l(const Gemm2Args& p, int mt, int kw, int nt, hipStream_t stream) {
-  // LDS: 2 x 2 x 16*MT x (KW*128 + 8) bf16 -> (MT, KW) in {(1,1..2), (2,1), (4,1)}
-  if (mt >= 2) kw = 1;
-  if (kw > 2) kw = 2;
-  if (nt == 4) {
-    if (mt == 4) G2L(4, 1, 4);
-    else if (mt == 2) G2L(2, 1, 4);
-    else { if (kw == 2) G2L(1, 2, 4); else G2L(1, 1, 4); }
-  } else {
-    if (mt == 4) G2L(4, 1, 2);
-    else if (mt == 2) G2L(2, 1, 2);
-    else { if (kw == 2) G2L(1, 2, 2); else G2L(1, 1, 2); }
-  }
-  return hipGetLastError();
-}
-#undef G2L
-
 }  // namespace
 
 hipError_t launch_gemm1_w8_lds(const Gemm1Args& p, int kw, int ng, hipStream_t stream) {
   const int mt = p.block_m / 16;
   return p.f16 ? g1l<true>(p, mt, kw, ng, stream) : g1l<false>(p, mt, kw, ng, stream);
-}
-
-hipError_t launch_gemm2_w8_lds(const Gemm2Args& p, int kw, int nt, hipStream_t stream) {
-  return g2l(p, p.block_m / 16, kw, nt, stream);
 }
 
 }  // namespace moe

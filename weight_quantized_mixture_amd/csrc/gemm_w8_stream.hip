@@ -1,9 +1,9 @@
-// Weight-streaming grouped GEMMs for int8 experts when each align block holds
-// at most 64 rows (decode-sized batches: the weights dominate the bytes).
+// Weight-streaming grouped GEMM1 for int8 experts when each align block holds
+// 16 or 48 rows (decode-sized batches: the weights dominate the bytes).
 //
 // experts_int8 page, ExpertsInt8MoEMethod.create_weights / apply ->
-// fused_experts(use_int8_w8a16): GEMM1 h = x dequant(w13[e])^T with the scale
-// on the fp32 accumulator and a = silu(h_gate) * h_up; GEMM2 y = a dequant(w2[e])^T.
+// fused_experts(use_int8_w8a16): h = x dequant(w13[e])^T with the scale on
+// the fp32 accumulator and a = silu(h_gate) * h_up.
 //
 // Design for HBM-bound streaming on gfx950:
 //   * every lane owns one weight row (the MFMA column l%16) and 32 consecutive
@@ -18,9 +18,8 @@
 //   * the 4 waves of a workgroup split K (KW ways) and/or columns (4/KW);
 //     K partial sums are added in a fixed order through LDS, so small batches
 //     still fill 256 CUs without atomics.
-//   * GEMM1 writes a as two bf16 planes, hi = rne(a) and lo = rne(a - hi)
-//     (16 significant bits); GEMM2 feeds both through the MFMA with the same
-//     dequantized weights and needs no conversion of its own.
+//   * a is written as two bf16 planes, hi = rne(a) and lo = rne(a - hi)
+//     (16 significant bits).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -148,130 +147,6 @@ __global__ __launch_bounds__(kThreads) void gemm1_stream_kernel(const Gemm1Args 
   }
 }
 
-template <int MT, int KW, int NT>
-__global__ __launch_bounds__(kThreads) void gemm2_stream_kernel(const Gemm2Args p) {
-  constexpr int CW = 4 / KW;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int cw = wave % CW;
-  const int kw = wave / CW;
-  const int col = lane & 15;
-  const int kg = lane >> 4;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
-  if (row0 >= *p.num_padded) return;
-  const int e = p.block_expert[blockIdx.y];
-  int ntiles = 0;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    if (p.sorted_ids[row0 + mt * 16] < p.Tk) ntiles = mt + 1;
-
-  const int64_t I = p.I, H = p.H;
-  const int64_t h0 = static_cast<int64_t>(blockIdx.x) * (16 * NT * CW) + cw * 16 * NT;
-  const int total_steps = static_cast<int>(I / kStep);
-  const int kways = p.splits * KW;
-  const int kidx = static_cast<int>(blockIdx.z) * KW + kw;
-  const int sbeg = kidx * total_steps / kways;
-  const int nsteps = (kidx + 1) * total_steps / kways - sbeg;
-  const int64_t kbeg = static_cast<int64_t>(sbeg) * kStep;
-  const int8_t* wr = p.w2 + (static_cast<int64_t>(e) * H + h0 + col) * p.ldw + kbeg + kg * 32;
-  const int64_t wstride = 16 * p.ldw;      // next 16-row tile
-  const uint16_t* a_hi = reinterpret_cast<const uint16_t*>(p.a);
-  const uint16_t* a_lo = a_hi + p.cap * I;
-  const int64_t aoff = (row0 + col) * I + kbeg + kg * 32;
-
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 w0[NT], w1[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    w0[j] = ld16(wr + j * wstride);
-    w1[j] = ld16(wr + j * wstride + 16);
-  }
-  for (int s = 0; s < nsteps; ++s) {
-    const int64_t ko = static_cast<int64_t>(s) * kStep;
-    u32x4 ah[MT][4], al[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt < ntiles) {
-        const int64_t o = aoff + static_cast<int64_t>(mt) * 16 * I + ko;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ah[mt][i] = ld16(a_hi + o + 8 * i);
-          al[mt][i] = ld16(a_lo + o + 8 * i);
-        }
-      }
-    }
-    const int64_t kn = (s + 1 < nsteps) ? ko + kStep : ko;
-    u32x4 n0[NT], n1[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      n0[j] = ld16(wr + j * wstride + kn);
-      n1[j] = ld16(wr + j * wstride + kn + 16);
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      u32x4 b[4];
-      i8x16_to_operands<false>(w0[j], b[0], b[1]);
-      i8x16_to_operands<false>(w1[j], b[2], b[3]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (mt < ntiles) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[mt][j] = mfma16_bf16(ah[mt][i], b[i], acc[mt][j]);
-            acc[mt][j] = mfma16_bf16(al[mt][i], b[i], acc[mt][j]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      w0[j] = n0[j];
-      w1[j] = n1[j];
-    }
-  }
-
-  if constexpr (KW > 1) {
-    __shared__ f32x4 red[KW - 1][CW][MT][NT][kWave];
-    if (kw > 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) red[kw - 1][cw][mt][j][lane] = acc[mt][j];
-    }
-    __syncthreads();
-    if (kw > 0) return;
-#pragma unroll
-    for (int q = 0; q < KW - 1; ++q)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[mt][j] += red[q][cw][mt][j][lane];
-  }
-
-  float sc[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) sc[j] = p.s2[static_cast<int64_t>(e) * H + h0 + 16 * j + col];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt < ntiles) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = p.sorted_ids[row0 + mt * 16 + kg * 4 + i];
-        if (f < p.Tk) {
-          float* yr = p.y + (static_cast<int64_t>(blockIdx.z) * p.Tk + f) * H + h0 + col;
-#pragma unroll
-          for (int j = 0; j < NT; ++j) yr[16 * j] = acc[mt][j][i] * sc[j];
-        }
-      }
-    }
-  }
-}
-
 template <int MT, bool F16>
 hipError_t g1_kw(const Gemm1Args& p, int kw, hipStream_t stream) {
   const unsigned by = static_cast<unsigned>(p.cap / p.block_m);
@@ -291,27 +166,6 @@ hipError_t g1_kw(const Gemm1Args& p, int kw, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT>
-hipError_t g2_kw(const Gemm2Args& p, int kw, hipStream_t stream) {
-  constexpr int NT = 2;
-  const unsigned by = static_cast<unsigned>(p.cap / p.block_m);
-  const unsigned bz = static_cast<unsigned>(p.splits);
-  switch (kw) {
-    case 4:
-      hipLaunchKernelGGL((gemm2_stream_kernel<MT, 4, NT>), dim3(static_cast<unsigned>(p.H / (16 * NT)), by, bz),
-                         dim3(kThreads), 0, stream, p);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemm2_stream_kernel<MT, 2, NT>), dim3(static_cast<unsigned>(p.H / (32 * NT)), by, bz),
-                         dim3(kThreads), 0, stream, p);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm2_stream_kernel<MT, 1, NT>), dim3(static_cast<unsigned>(p.H / (64 * NT)), by, bz),
-                         dim3(kThreads), 0, stream, p);
-  }
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_gemm1_w8_stream(const Gemm1Args& p, int kw, hipStream_t stream) {
@@ -326,14 +180,6 @@ hipError_t launch_gemm1_w8_stream(const Gemm1Args& p, int kw, hipStream_t stream
   if (mt == 3) return g1_kw<3, false>(p, kw, stream);
   if (mt == 2) return g1_kw<2, false>(p, kw, stream);
   return g1_kw<1, false>(p, kw, stream);
-}
-
-hipError_t launch_gemm2_w8_stream(const Gemm2Args& p, int kw, hipStream_t stream) {
-  const int mt = p.block_m / 16;
-  if (mt == 4) return g2_kw<4>(p, kw, stream);
-  if (mt == 3) return g2_kw<3>(p, kw, stream);
-  if (mt == 2) return g2_kw<2>(p, kw, stream);
-  return g2_kw<1>(p, kw, stream);
 }
 
 }  // namespace moe
