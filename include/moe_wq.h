@@ -172,9 +172,9 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * rows of a block that holds rows get v = 0; 16-row groups made only of
  * padding may be left unwritten (GEMM2 never reads them).
  *
- * moe_w8a16_requant: for block_m <= 64 (a no-op otherwise) turns the planes
- * into the 16-bit fixed-point form the integer GEMM2 reads, stored right
- * after them (at byte offset round_up(4*cap*I, 256)): int8 hi codes
+ * moe_w8a16_requant: for block_m in [32, 64] (a no-op otherwise) turns the
+ * planes into the 16-bit fixed-point form the integer GEMM2 reads, stored
+ * right after them (at byte offset round_up(4*cap*I, 256)): int8 hi codes
  * [cap, I], then int8 lo codes [cap, I] (each region rounded up to 256
  * bytes), then fp32 scales [cap, I/128], with
  * v ~= s[r, i/128] * (256 * hi + lo), s = max |v| over the 128-column group
@@ -184,7 +184,8 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * split s < splits, h < H:
  *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} v[r, i] w2[e,h,i]
  * with v as moe_w8a16_gemm1 and moe_w8a16_requant left it in `a` (the
- * fixed-point form for block_m <= 64, the hi + lo planes otherwise).  The K range [0, I) is cut
+ * fixed-point form for block_m in [32, 64]; the hi + lo planes otherwise,
+ * which for block_m = 16 GEMM2 rounds to the same fixed-point form itself).  The K range [0, I) is cut
  * into `splits` parts of whole 128-wide steps (1 <= splits <= I/128; equal
  * parts, so splits must divide I/128, when block_m > 64; 1 when block_m is
  * 256).  y is device fp32 [splits, T*k, H]; rows of dropped ids are not

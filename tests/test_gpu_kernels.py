@@ -178,7 +178,7 @@ def test_gemm1_intermediate(act, bm):
     raw = a.cpu().numpy().view(np.uint8)
     planes = raw[:4 * cap * I].view(np.uint16).reshape(2, cap, I)
     a_g = oracle.bf16_bits_to_f64(planes[0]) + oracle.bf16_bits_to_f64(planes[1])
-    if bm <= 64:
+    if 32 <= bm <= 64:
         # the 16-bit fixed-point form after the planes: v ~= s * (256 hi + lo) per (row, 128 columns)
         up = lambda v: (v + 255) // 256 * 256  # noqa: E731
         o = up(4 * cap * I)

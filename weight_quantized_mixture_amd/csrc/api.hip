@@ -106,6 +106,9 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
 // generic tiled kernel (equal splits of whole 128-wide steps).
 bool gemm2_int8(int64_t bm) { return bm <= 64; }
 
+// 16-row blocks quantize inside GEMM2; 32 to 64 rows read the requantized form.
+bool needs_requant(int64_t bm) { return bm >= 32 && bm <= 64; }
+
 // Expected rows per active expert above half a tile: more MFMA work per
 // weight byte, so narrower waves (more workgroups) stream better.
 int gemm2_nt(int64_t T, int64_t E, int64_t k, int64_t bm) {
@@ -152,7 +155,7 @@ int64_t w4_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t
   return sp;
 }
 
-// The intermediate: bf16 hi/lo planes [2, cap, I]; for blocks of at most 64
+// The intermediate: bf16 hi/lo planes [2, cap, I]; for blocks of 32 to 64
 // rows followed by the int8 hi codes [cap, I], lo codes [cap, I] and fp32
 // scales [cap, I/128] the integer GEMM2 reads.
 struct Q16 {
@@ -165,7 +168,7 @@ size_t planes_bytes(int64_t cap, int64_t I) { return align_up(static_cast<size_t
 
 size_t intermediate_bytes(int64_t cap, int64_t I, int64_t bm, bool w8) {
   size_t b = planes_bytes(cap, I);
-  if (w8 && gemm2_int8(bm)) {
+  if (w8 && needs_requant(bm)) {
     b += 2 * align_up(static_cast<size_t>(cap) * static_cast<size_t>(I));
     b += align_up(static_cast<size_t>(cap) * static_cast<size_t>(I / 128) * 4);
   }
@@ -181,7 +184,7 @@ Q16 q16_of(const float* a, int64_t cap, int64_t I) {
 
 hipError_t run_gemm1_and_requant(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t stream) {
   hipError_t e = run_gemm1(p, T, E, stream);
-  if (e != hipSuccess || !gemm2_int8(p.block_m)) return e;
+  if (e != hipSuccess || !needs_requant(p.block_m)) return e;
   const Q16 q = q16_of(p.a, p.cap, p.I);
   return moe::launch_requant_q16(p.a, p.cap, p.I, p.sorted_ids, p.num_padded, p.Tk, q.hi, q.lo, q.scale, stream);
 }
@@ -377,7 +380,7 @@ int moe_w8a16_requant(float* a, int64_t T, int64_t I, int64_t E, int64_t k, cons
   if (T < 0 || E < 1 || k < 1 || k > E) return fail(MOE_ERR_INVALID_ARGUMENT, "need T >= 0, 1 <= k <= E");
   if (I < 128 || I % 128) return fail(MOE_ERR_INVALID_ARGUMENT, "I must be a positive multiple of 128");
   if ((st = check_block_m(block_m)) != MOE_OK) return st;
-  if (T == 0 || !gemm2_int8(block_m)) return ok();
+  if (T == 0 || !needs_requant(block_m)) return ok();
   if (!a || !sorted_ids || !num_padded) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
   if (!aligned(a, 16)) return fail(MOE_ERR_INVALID_ARGUMENT, "a must be 16-byte aligned");
   const int64_t cap = capacity(T, k, E, block_m);

@@ -16,7 +16,9 @@
 //
 // requant_q16_kernel turns the bf16 hi/lo planes GEMM1 writes into this form
 // (16 lanes per (row, group)); rows of 16-row tiles made only of padding are
-// skipped, like everywhere else.
+// skipped, like everywhere else.  Blocks of 16 rows skip that pass: their
+// GEMM2 quantizes the (one tile of) planes while staging them in LDS, which
+// costs less than a launch when a block holds so few rows.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -92,14 +94,13 @@ __global__ __launch_bounds__(kThreads) void requant_q16_kernel(const uint16_t* _
 // scales for one step are staged in LDS (double-buffered, one barrier per
 // step); lane (col, kg) feeds K [16kg, 16kg+16) and [64+16kg, 64+16kg+16) of
 // the step to the two MFMAs of each plane, for both operands.
-template <int MT, int NT>
+template <int MT, int NT, bool FQ>
 __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, const int8_t* __restrict__ qhi,
                                                              const int8_t* __restrict__ qlo,
                                                              const float* __restrict__ qscale) {
   constexpr int ROWS = 16 * MT;
   constexpr int PITCH = kStep + 16;                  // bytes per LDS row (16-byte pad)
   constexpr int CPR = kStep / 16;                    // 16-byte chunks per row and plane
-  constexpr int CPT = (2 * ROWS * CPR + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) int8_t As[2][2][ROWS * PITCH];
   __shared__ __attribute__((aligned(16))) float Ss[2][ROWS];
 
@@ -125,32 +126,88 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
   const int8_t* wbase = p.w2 + (static_cast<int64_t>(e) * H + h0 + col) * p.ldw + static_cast<int64_t>(ib) * kStep + kg * 16;
   const int64_t tstride = 16 * p.ldw;
 
-  // cooperative copy: chunk c = (plane, row, 16-byte column)
+  // cooperative copy of one step of the block's rows into LDS.
+  //   FQ = false: chunk c = (plane, row, 16 codes) of the fixed-point form;
+  //   FQ = true:  chunk c = (row, 8 values) of the bf16 planes, quantized on
+  //   the way (the 16 lanes of a row find its group maximum by shuffles).
+  constexpr int NCH = FQ ? ROWS * 16 : 2 * ROWS * CPR;
+  constexpr int CPT = (NCH + kThreads - 1) / kThreads;
   int64_t srco[CPT];
   int dsto[CPT];
   bool cv[CPT];
   const int8_t* srcp[CPT];
+  const uint16_t* planes = reinterpret_cast<const uint16_t*>(p.a);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ci = tid + c * kThreads;
-    const int pl = ci / (ROWS * CPR), rem = ci % (ROWS * CPR);
-    const int r = rem / CPR, q = rem % CPR;
-    cv[c] = ci < 2 * ROWS * CPR && r < nrows;
-    srcp[c] = pl == 0 ? qhi : qlo;
-    srco[c] = (row0 + r) * I + static_cast<int64_t>(ib) * kStep + q * 16;
-    dsto[c] = (pl * ROWS + r) * PITCH + q * 16;
+    if constexpr (FQ) {
+      const int r = ci / 16, q = ci % 16;
+      cv[c] = ci < NCH && r < nrows;
+      srcp[c] = nullptr;
+      srco[c] = (row0 + r) * I + static_cast<int64_t>(ib) * kStep + q * 8;
+      dsto[c] = r * PITCH + q * 8;
+    } else {
+      const int pl = ci / (ROWS * CPR), rem = ci % (ROWS * CPR);
+      const int r = rem / CPR, q = rem % CPR;
+      cv[c] = ci < NCH && r < nrows;
+      srcp[c] = pl == 0 ? qhi : qlo;
+      srco[c] = (row0 + r) * I + static_cast<int64_t>(ib) * kStep + q * 16;
+      dsto[c] = (pl * ROWS + r) * PITCH + q * 16;
+    }
   }
+  constexpr int NREG = FQ ? 2 * CPT : CPT;
   auto load_a = [&](int it, u32x4* regs, float& sreg) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (cv[c]) regs[c] = ld16(srcp[c] + srco[c] + static_cast<int64_t>(it) * kStep);
-    if (tid < nrows) sreg = qscale[(row0 + tid) * G + ib + it];
+    for (int c = 0; c < CPT; ++c) {
+      if constexpr (FQ) {
+        regs[2 * c] = u32x4{0u, 0u, 0u, 0u};
+        regs[2 * c + 1] = u32x4{0u, 0u, 0u, 0u};
+        if (cv[c]) {
+          regs[2 * c] = ld16(planes + srco[c] + static_cast<int64_t>(it) * kStep);
+          regs[2 * c + 1] = ld16(planes + p.cap * I + srco[c] + static_cast<int64_t>(it) * kStep);
+        }
+      } else {
+        if (cv[c]) regs[c] = ld16(srcp[c] + srco[c] + static_cast<int64_t>(it) * kStep);
+      }
+    }
+    if (!FQ && tid < nrows) sreg = qscale[(row0 + tid) * G + ib + it];
   };
   auto store_a = [&](int buf, const u32x4* regs, float sreg) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (cv[c]) *reinterpret_cast<u32x4*>(&As[buf][0][dsto[c]]) = regs[c];
-    if (tid < nrows) Ss[buf][tid] = sreg;
+    for (int c = 0; c < CPT; ++c) {
+      if constexpr (FQ) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t hw = regs[2 * c][i], lw = regs[2 * c + 1][i];
+          v[2 * i] = __uint_as_float(hw << 16) + __uint_as_float(lw << 16);
+          v[2 * i + 1] = __uint_as_float(hw & 0xffff0000u) + __uint_as_float(lw & 0xffff0000u);
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+        const float inv = m > 0.0f ? static_cast<float>(kQMax) / m : 0.0f;
+        uint32_t hb[2] = {0u, 0u}, lb[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          int q = static_cast<int>(__builtin_rintf(v[i] * inv));
+          q = q < -kQMax ? -kQMax : (q > kQMax ? kQMax : q);
+          const int h = (q + 128) >> 8;
+          hb[i / 4] |= static_cast<uint32_t>(h & 0xff) << (8 * (i % 4));
+          lb[i / 4] |= static_cast<uint32_t>((q - 256 * h) & 0xff) << (8 * (i % 4));
+        }
+        if (cv[c]) {
+          *reinterpret_cast<u32x2*>(&As[buf][0][dsto[c]]) = u32x2{hb[0], hb[1]};
+          *reinterpret_cast<u32x2*>(&As[buf][1][dsto[c]]) = u32x2{lb[0], lb[1]};
+          if ((tid & 15) == 0) Ss[buf][(tid + c * kThreads) / 16] = m / static_cast<float>(kQMax);
+        }
+      } else {
+        if (cv[c]) *reinterpret_cast<u32x4*>(&As[buf][0][dsto[c]]) = regs[c];
+      }
+    }
+    if (!FQ && tid < nrows) Ss[buf][tid] = sreg;
   };
 
   f32x4 acc[MT][NT];
@@ -159,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 areg[CPT];
+  u32x4 areg[NREG];
   float sreg = 0.0f;
   if (iters > 0) load_a(0, areg, sreg);
   u32x4 w0[NT], w1[NT];
@@ -245,13 +302,15 @@ hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, const int8_t* qhi, const
                             hipStream_t stream) {
   const int mt = p.block_m / 16;
   const unsigned by = static_cast<unsigned>(p.cap / p.block_m), bz = static_cast<unsigned>(p.splits);
-#define Q16(MT, NT)                                                                                   \
-  hipLaunchKernelGGL((gemm2_q16_kernel<MT, NT>), dim3(static_cast<unsigned>(p.H / (64 * NT)), by, bz), \
+#define Q16(MT, NT, FQ)                                                                                   \
+  hipLaunchKernelGGL((gemm2_q16_kernel<MT, NT, FQ>), dim3(static_cast<unsigned>(p.H / (64 * NT)), by, bz), \
                      dim3(kThreads), 0, stream, p, qhi, qlo, qscale)
   if (nt == 4) {
-    if (mt == 4) Q16(4, 4); else if (mt == 3) Q16(3, 4); else if (mt == 2) Q16(2, 4); else Q16(1, 4);
+    if (mt == 4) Q16(4, 4, false); else if (mt == 3) Q16(3, 4, false); else if (mt == 2) Q16(2, 4, false);
+    else Q16(1, 4, true);
   } else {
-    if (mt == 4) Q16(4, 2); else if (mt == 3) Q16(3, 2); else if (mt == 2) Q16(2, 2); else Q16(1, 2);
+    if (mt == 4) Q16(4, 2, false); else if (mt == 3) Q16(3, 2, false); else if (mt == 2) Q16(2, 2, false);
+    else Q16(1, 2, true);
   }
 #undef Q16
   return hipGetLastError();
