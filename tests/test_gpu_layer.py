@@ -189,7 +189,8 @@ def test_fine_grained(T):
 
 
 @pytest.mark.parametrize("T,E,k,act", [(1, 8, 2, "bf16"), (8, 64, 6, "fp16"), (37, 8, 2, "fp16"),
-                                       (300, 16, 4, "bf16")])
+                                       (300, 16, 4, "bf16"), (600, 8, 2, "bf16"), (5, 128, 8, "fp16"),
+                                       (20, 96, 4, "bf16")])
 def test_apply_from_logits_matches_route_then_forward(T, E, k, act):
     """moe_w8a16_apply (routing fused with align up to 8 tokens) equals route + forward bit for bit."""
     H, I = 256, 384
