@@ -386,9 +386,11 @@ def gemm1_kernel_name(block_m, H):
     """Name prefix of the GEMM1 kernel the library launches for this block size."""
     if block_m == 256:
         return "gemm1_big_kernel"
-    if block_m in (32, 64):
+    if block_m in (16, 32):
+        return "gemm1_dma_kernel"
+    if block_m == 64:
         return "gemm1_lds_kernel"
-    if block_m <= 64:
+    if block_m == 48:
         return "gemm1_stream_kernel"
     return "gemm1_w8_kernel"
 

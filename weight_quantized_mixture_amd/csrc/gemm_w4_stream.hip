@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
       for (int pl = 0; pl < NPLANE; ++pl) {
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
         if (cv[c] && src[c] >= 0) v = ld16(xa + pl * plane + src[c] + ko);
-        regs[pl][c] = F16 ? perm0415(v) : v;
+        regs[pl][c] = v;
       }
   };
   auto store_a = [&](int buf, const u32x4 (&regs)[NPLANE][CPT]) {
@@ -186,7 +186,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
     for (int c = 0; c < CPT; ++c)
       if (cv[c]) {
 #pragma unroll
-        for (int pl = 0; pl < NPLANE; ++pl) *reinterpret_cast<u32x4*>(&As[buf][pl][dst[c]]) = regs[pl][c];
+        for (int pl = 0; pl < NPLANE; ++pl)
+          *reinterpret_cast<u32x4*>(&As[buf][pl][dst[c]]) = F16 ? perm0415(regs[pl][c]) : regs[pl][c];
       }
   };
 

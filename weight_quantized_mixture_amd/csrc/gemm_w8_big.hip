@@ -29,14 +29,12 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 namespace {
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
@@ -51,30 +49,6 @@ constexpr int kBStage = 2 * kOut * kBRow;     // 16 KB
 constexpr int kStageBytes = kAStage + kBStage;
 constexpr int kADma = kAStage / (kThreads * 16);   // 16-byte copies per thread per stage
 constexpr int kBDma = kBStage / (kThreads * 16);
-
-// 16 bytes from global memory to LDS; lane l of the wave lands at lds + 16 l.
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_ptr_t)const_cast<void*>(src), (lds_ptr_t)lds_wave_base, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) (other counters left alone).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that waits for nothing but keeps the compiler from moving
-// memory accesses across it (the LDS copies are waited for explicitly).
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Chunk swizzles: activation rows hold 8 chunks of 16 bytes, weight rows 4.
-__device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int swz_b(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 
 template <bool F16>
 __global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) {

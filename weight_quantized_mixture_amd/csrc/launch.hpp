@@ -64,6 +64,8 @@ struct Gemm2Args {
 hipError_t launch_gemm2_w8(const Gemm2Args& p, hipStream_t stream);
 // LDS-staged GEMM1 for blocks of 32 or 64 rows (kw <= 2 at 32, 1 at 64; ng = 16-column groups per wave).
 hipError_t launch_gemm1_w8_lds(const Gemm1Args& p, int kw, int ng, hipStream_t stream);
+// GEMM1 for blocks of 16 or 32 rows on a 3-step LDS ring of direct global -> LDS copies.
+hipError_t launch_gemm1_w8_dma(const Gemm1Args& p, hipStream_t stream);
 // Intermediate as 16-bit fixed point per (row, 128 columns) for the integer-MFMA GEMM2 (blocks of
 // at most 64 rows): requant turns GEMM1's bf16 hi/lo planes into hi/lo int8 codes and scales;
 // nt = 16-column tiles per wave (2 or 4).
