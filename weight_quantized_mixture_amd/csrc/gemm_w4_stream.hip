@@ -14,7 +14,7 @@
 // scale never rounds a weight.  The weights of the next three steps are in
 // flight while a step is converted and multiplied (packed rows are short, so a
 // wave needs several steps of loads outstanding to cover HBM latency); the
-// group scales and zero words travel with them.
+// group scales, zero words and activation rows travel with them.
 //
 // fp16 activations: 0x6400 | q is the half 1024 + q and one packed subtraction
 // of 1024 + z leaves q - z exactly; decoding nibble pairs (q_i, q_{i+4}) puts
@@ -197,53 +197,43 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // weights, group scales and zero words of the next kPF steps are in flight
-  // while a step is multiplied (a scale or zero fetched in its own step would
-  // put a full memory latency on every step)
-  constexpr int kPF = 3;
+  // Weights, group scales and zero words of step s+3, and the activation rows
+  // of step s+3, are requested while step s is multiplied (a scale or zero
+  // fetched in its own step would put a full memory latency on every step).
+  // They live in rings of four register sets and the loop is unrolled by
+  // four, so the rings turn by renaming: copying a register that a load is
+  // still filling would wait for that load.
   struct Pre {
     u32x4 w[NT];
-    uint32_t sz[NT];   // fp16 scale bits (low half) | zero code << 16
+    uint16_t s[NT];    // fp16 group scale
+    uint32_t z[NT];    // zero word (8 rows' codes), decoded when used
   };
   auto wload = [&](int s, Pre& v) {
-    const int64_t kq = sbeg + (s < nsteps ? s : nsteps - 1);
-    const int64_t grp = kq * kStep / g;
+    const int kq = sbeg + s;
+    const int grp = kq * kStep / g;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       v.w[j] = ld16(wp[j] + kq * (kStep / 8));
-      v.sz[j] = static_cast<uint32_t>(sp[j][grp]) | (zero_code(qz_e, G, grp, nrow[j]) << 16);
+      v.s[j] = sp[j][grp];
+      v.z[j] = static_cast<uint32_t>(qz_e[(nrow[j] >> 3) * G + grp]);
     }
   };
-  // activation rows of the next kPF steps wait in registers (a0 = step s+1)
-  u32x4 a0[NPLANE][CPT], a1[NPLANE][CPT], a2[NPLANE][CPT];
-  Pre q0, q1, q2;
-  if (nsteps > 0) {
-    load_a(0, a0);
-    wload(0, q0);
-    wload(1, q1);
-    wload(2, q2);
-    store_a(0, a0);
-    if (nsteps > 1) load_a(1, a0);
-    if (nsteps > 2) load_a(2, a1);
-    if (nsteps > 3) load_a(3, a2);
-  }
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
+  typedef u32x4 ARegs[NPLANE][CPT];
+  auto step = [&](int s, const Pre& cur, Pre& ahead, const ARegs& anext, ARegs& aahead) {
     const int buf = s & 1;
-    const bool more = s + 1 < nsteps;
-    u32x4 an[NPLANE][CPT];
-    if (s + kPF + 1 < nsteps) load_a(s + kPF + 1, an);
-    Pre pn;
-    wload(s + kPF, pn);
+    if (s + 3 < nsteps) {
+      load_a(s + 3, aahead);
+      wload(s + 3, ahead);
+    }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const uint32_t z = q0.sz[j] >> 16;
-      const float scale = f16_to_f32(static_cast<uint16_t>(q0.sz[j] & 0xffffu));
+      const uint32_t z = (cur.z[j] >> (4 * (nrow[j] & 7))) & 0xFu;
+      const float scale = f16_to_f32(cur.s[j]);
       u32x4 b[4];
-      b[0] = w4_op<F16>(q0.w[j].x, z);
-      b[1] = w4_op<F16>(q0.w[j].y, z);
-      b[2] = w4_op<F16>(q0.w[j].z, z);
-      b[3] = w4_op<F16>(q0.w[j].w, z);
+      b[0] = w4_op<F16>(cur.w[j].x, z);
+      b[1] = w4_op<F16>(cur.w[j].y, z);
+      b[2] = w4_op<F16>(cur.w[j].z, z);
+      b[3] = w4_op<F16>(cur.w[j].w, z);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt < ntiles) {
@@ -251,30 +241,37 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
           f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(&As[buf][0][o + 8 * i]);
-            part = mfma16<F16>(a0, b[i], part);
+            const u32x4 x0 = *reinterpret_cast<const u32x4*>(&As[buf][0][o + 8 * i]);
+            part = mfma16<F16>(x0, b[i], part);
             if constexpr (ROLE == 2) {
-              const u32x4 a1 = *reinterpret_cast<const u32x4*>(&As[buf][1][o + 8 * i]);
-              part = mfma16<F16>(a1, b[i], part);
+              const u32x4 x1 = *reinterpret_cast<const u32x4*>(&As[buf][1][o + 8 * i]);
+              part = mfma16<F16>(x1, b[i], part);
             }
           }
           acc[mt][j] += part * scale;
         }
       }
     }
-    q0 = q1;
-    q1 = q2;
-    q2 = pn;
-    if (more) store_a(buf ^ 1, a0);
-#pragma unroll
-    for (int pl = 0; pl < NPLANE; ++pl)
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        a0[pl][c] = a1[pl][c];
-        a1[pl][c] = a2[pl][c];
-        a2[pl][c] = an[pl][c];
-      }
+    if (s + 1 < nsteps) store_a(buf ^ 1, anext);
     __syncthreads();
+  };
+  Pre q[4];
+  ARegs ar[4];
+  if (nsteps > 0) {
+    load_a(0, ar[0]);
+    wload(0, q[0]);
+    if (nsteps > 1) wload(1, q[1]);
+    if (nsteps > 2) wload(2, q[2]);
+    store_a(0, ar[0]);
+    if (nsteps > 1) load_a(1, ar[1]);
+    if (nsteps > 2) load_a(2, ar[2]);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 4) {
+    step(s, q[0], q[3], ar[1], ar[3]);
+    if (s + 1 < nsteps) step(s + 1, q[1], q[0], ar[2], ar[0]);
+    if (s + 2 < nsteps) step(s + 2, q[2], q[1], ar[3], ar[1]);
+    if (s + 3 < nsteps) step(s + 3, q[3], q[2], ar[0], ar[2]);
   }
 
   if constexpr (ROLE == 1) {
