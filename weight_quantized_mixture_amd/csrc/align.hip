@@ -24,6 +24,12 @@ constexpr int kAlignWaves = 8;
 constexpr int kAlignThreads = kAlignWaves * kWave;
 constexpr int kMaxExperts = 1024;
 
+// The ids of the flat indices a thread handles are loaded once, all before
+// the first use, when T*k <= kIdsInRegs * 512 (a loop that loads, waits and
+// uses would pay one memory latency per 512 ids, twice).
+constexpr int kIdsInRegs = 16;
+
+template <bool REGS>
 __device__ __forceinline__ void align_body(
     const int32_t* __restrict__ ids, int64_t Tk, int E, int bm, int64_t cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
@@ -39,6 +45,22 @@ __device__ __forceinline__ void align_body(
   const int wave = tid / kWave;
   const int sentinel = static_cast<int>(Tk);
 
+  int reg_ids[REGS ? kIdsInRegs : 1];
+  auto id_of = [&](int u, int64_t f) -> int {
+    int e;
+    if constexpr (REGS) e = reg_ids[u];
+    else e = f < Tk ? ids[f] : -1;
+    return (e >= 0 && e < E) ? e : -1;
+  };
+  if constexpr (REGS) {
+#pragma unroll
+    for (int u = 0; u < kIdsInRegs; ++u) {
+      const int64_t f = static_cast<int64_t>(u) * kAlignThreads + tid;
+      reg_ids[u] = f < Tk ? ids[f] : -1;
+    }
+  }
+  const int nchunks = static_cast<int>((Tk + kAlignThreads - 1) / kAlignThreads);
+
   for (int e = tid; e < E; e += kAlignThreads) {
     cnt[e] = 0;
     done[e] = 0;
@@ -46,9 +68,17 @@ __device__ __forceinline__ void align_body(
   __syncthreads();
 
   // 1. histogram
-  for (int64_t f = tid; f < Tk; f += kAlignThreads) {
-    const int e = ids[f];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  if constexpr (REGS) {
+#pragma unroll
+    for (int u = 0; u < kIdsInRegs; ++u) {
+      const int e = id_of(u, 0);
+      if (e >= 0) atomicAdd(&cnt[e], 1);
+    }
+  } else {
+    for (int64_t f = tid; f < Tk; f += kAlignThreads) {
+      const int e = id_of(0, f);
+      if (e >= 0) atomicAdd(&cnt[e], 1);
+    }
   }
   __syncthreads();
 
@@ -90,15 +120,11 @@ __device__ __forceinline__ void align_body(
   // 3. stable scatter
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  for (int64_t c0 = 0; c0 < Tk; c0 += kAlignThreads) {
+  auto chunk = [&](int u) {
     for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wc[i / E][i % E] = 0;
     __syncthreads();
-    const int64_t f = c0 + tid;
-    int e = -1;
-    if (f < Tk) {
-      e = ids[f];
-      if (e < 0 || e >= E) e = -1;
-    }
+    const int64_t f = static_cast<int64_t>(u) * kAlignThreads + tid;
+    const int e = id_of(u, f);
     const bool active = (e >= 0);
     uint64_t mask = __ballot(active);
     for (int b = 0; b < nbits; ++b) {
@@ -122,6 +148,13 @@ __device__ __forceinline__ void align_body(
       done[x] += s;
     }
     __syncthreads();
+  };
+  if constexpr (REGS) {
+#pragma unroll
+    for (int u = 0; u < kIdsInRegs; ++u)
+      if (u < nchunks) chunk(u);
+  } else {
+    for (int u = 0; u < nchunks; ++u) chunk(u);
   }
 }
 
@@ -129,7 +162,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int64_t Tk, int E, int bm, int64_t cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded) {
-  align_body(ids, Tk, E, bm, cap, sorted_ids, block_expert, num_padded);
+  if (Tk <= static_cast<int64_t>(kIdsInRegs) * kAlignThreads)
+    align_body<true>(ids, Tk, E, bm, cap, sorted_ids, block_expert, num_padded);
+  else
+    align_body<false>(ids, Tk, E, bm, cap, sorted_ids, block_expert, num_padded);
 }
 
 // Routing and align in one launch (small batches): the 8 waves route the
@@ -143,7 +179,7 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
   for (int64_t t = wave; t < T; t += kAlignWaves)
     route_token(logits + t * E, E, k, renormalize, topk_w + t * k, topk_ids + t * k);
   __syncthreads();
-  align_body(topk_ids, T * k, E, bm, cap, sorted_ids, block_expert, num_padded);
+  align_body<true>(topk_ids, T * k, E, bm, cap, sorted_ids, block_expert, num_padded);
 }
 
 }  // namespace

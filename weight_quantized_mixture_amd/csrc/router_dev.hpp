@@ -40,6 +40,8 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lr, int E,
   z = wave_sum(z);
   uint32_t taken = 0;   // bit i: slot i of this lane already chosen
   float psum = 0.0f;
+  float my_p = 0.0f;    // lane j keeps the j-th winner (k <= 64)
+  int my_id = 0;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int bid = 0x7fffffff;
@@ -63,13 +65,24 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lr, int E,
     if ((bid & (kWave - 1)) == lane) taken |= 1u << (bid / kWave);
     const float p = expf(bv - m) / z;
     psum += p;
-    if (lane == 0) {
+    if (j < kWave) {
+      if (lane == j) {
+        my_p = p;
+        my_id = bid;
+      }
+    } else if (lane == 0) {
       ti[j] = bid;
       tw[j] = p;
     }
   }
+  // the first 64 winners are written by the lanes that hold them (no store is
+  // read back); renormalisation divides by the sum taken in j order
+  if (lane < k) {
+    ti[lane] = my_id;
+    tw[lane] = renormalize ? my_p / psum : my_p;
+  }
   if (renormalize && lane == 0) {
-    for (int j = 0; j < k; ++j) tw[j] = tw[j] / psum;
+    for (int j = kWave; j < k; ++j) tw[j] = tw[j] / psum;
   }
 }
 
