@@ -54,6 +54,9 @@ def parse():
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of a bench run, then of "
                          "--calibrate-copy-mb 1024) into the traffic summary under profiles/ and exit")
     ap.add_argument("--pmc-command", default="", help="command line recorded in the traffic summary")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="turn a rocprofv3 --pmc output folder with SQ/GRBM counters into the per-kernel busy "
+                         "summary under profiles/ and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace --stats output folder into the kernel-time summary "
                          "under profiles/ and exit")
@@ -155,6 +158,36 @@ def summarize_trace(args):
     print("\n".join(lines), flush=True)
 
 
+def summarize_counters(args):
+    """Per-kernel busy fractions from SQ counters (summed over the SIMDs / XCDs of the chip)."""
+    rows = _pmc_rows(args.summarize_counters)
+    T = args.tokens or HEADLINE_T[args.workload]
+    kernels = {}
+    for (name, c), xs in rows.items():
+        if "moe::" not in name:
+            continue
+        short = name.replace("moe::(anonymous namespace)::", "").replace("void ", "").split("(moe::")[0]
+        short = short.split("(float const")[0].split("(int const")[0][:70]
+        kernels.setdefault(short, {})[c] = sum(xs) / len(xs)
+    lines = [f"# SQ counters per launch: {args.workload}, T={T}", "", f"Command: `{args.pmc_command}`", "",
+             "GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the kernel's GPU cycles are GRBM_GUI_ACTIVE / 8; "
+             "SQ_VALU_MFMA_BUSY_CYCLES is summed over the 1024 SIMDs.", "",
+             "| kernel | GPU cycles | MFMA busy (per SIMD) | VALU active / wave cycles | waiting / wave cycles | "
+             "LDS bank conflicts |", "|---|---|---|---|---|---|"]
+    for name, m in sorted(kernels.items()):
+        cyc = m.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        wave = m.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+        busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024.0 / cyc if cyc else 0.0
+        lines.append(f"| `{name}` | {cyc:.0f} | {100 * busy:.1f}% | "
+                     f"{100 * m.get('SQ_ACTIVE_INST_VALU', 0.0) / wave:.1f}% | "
+                     f"{100 * m.get('SQ_WAIT_INST_ANY', 0.0) / wave:.1f}% | {m.get('SQ_LDS_BANK_CONFLICT', 0.0):.3g} |")
+    lines += ["", f"Kernel sources sha256[:16]: `{sources_sha()}`"]
+    stem = f"counters_{args.workload}_T{T}"
+    os.makedirs(PROFILES, exist_ok=True)
+    open(os.path.join(PROFILES, stem + ".md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
 def recorded_traffic(workload, T, kernel_prefix):
     """Scaled HBM bytes of the dominant kernel from the committed summary, if the kernels are unchanged."""
     path = os.path.join(PROFILES, f"traffic_{workload}_T{T}.json")
@@ -176,6 +209,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this library runs on a "
