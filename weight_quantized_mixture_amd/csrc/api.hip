@@ -90,7 +90,7 @@ int gemm1_kways(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t b
 }
 
 hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t stream) {
-  if (use_prefill(p.block_m)) return moe::launch_gemm1_w8_big(p, stream);
+  if (use_prefill(p.block_m) && moe::gemm1_w8_big_fits(p)) return moe::launch_gemm1_w8_big(p, stream);
   if (!use_stream(p.block_m)) return moe::launch_gemm1_w8(p, stream);
   if (p.block_m == 16 || p.block_m == 32) return moe::launch_gemm1_w8_dma(p, stream);
   if (p.block_m == 64) return moe::launch_gemm1_w8_lds(p, 1, 1, stream);

@@ -1,28 +1,28 @@
 // Grouped int8-weight GEMMs for 256-row align blocks (prefill-sized expert
-// loads, where the bf16 MFMA work dominates), gfx950.
+// loads, where the MFMA work dominates), gfx950.
 //
 // experts_int8 page, ExpertsInt8MoEMethod.create_weights / apply ->
 // fused_experts(use_int8_w8a16): h = x dequant(w13[e])^T with the per-row
 // scale on the fp32 accumulator, a = silu(h_gate) * h_up, written as bf16
 // hi/lo planes (hi = rne(a), lo = rne(a - hi)).
 //
-// Tiling: a workgroup owns one align block (256 rows) and 128 output columns,
-// i.e. 128 gate + the matching 128 up rows of w13.  Its 8 waves (two per
-// SIMD, so one can issue MFMAs while the other waits for LDS) form a 2 x 4
-// grid; a wave owns 128 rows x (32 gate + 32 up) columns = 8 x 4 accumulator
-// tiles of v_mfma_f32_16x16x32 (128 accumulator registers).
+// GEMM1 tiling: a workgroup owns one align block (256 rows) and 128 output
+// columns, i.e. 128 gate + the matching 128 up rows of w13.  Its 4 waves (one
+// per SIMD) form a 2 x 2 grid; a wave owns 128 rows x (64 gate + 64 up)
+// columns = 8 x 8 accumulator tiles of v_mfma_f32_16x16x32 (256 accumulator
+// registers, which live in the AGPR half of the register file).
 // K advances in stages of 64 through a 3-deep LDS ring:
 //   * both operands go HBM/L2 -> LDS with global_load_lds_dwordx4 (no
 //     staging registers, no LDS store instructions): per stage 32 KB of
 //     gathered bf16 activation rows and 16 KB of int8 weight rows;
-//   * stage s+2 is requested while stage s is multiplied; one barrier per
-//     stage, preceded by a wait for this thread's own copies of stage s;
+//   * the operand fragments of stage s+1 are read from LDS while the MFMAs
+//     of stage s run, and the int8 weights (-> bf16/fp16, exact) are
+//     converted one K half ahead of their MFMAs, so LDS latency and the
+//     conversion hide behind 128 MFMAs per wave and stage;
+//   * one barrier per stage, after which the copy of stage s+3 goes into the
+//     slot stage s was read from;
 //   * the 16-byte chunks of every LDS row are XOR-swizzled by row so that the
 //     16 rows one MFMA operand read touches fall in distinct bank groups;
-//   * each wave converts its 4 weight fragments (int8 -> bf16/fp16, exact)
-//     once per stage and reuses each for its 8 row tiles; all activation
-//     fragments of a stage are read first, then the column tiles are walked
-//     one by one so the conversion of one overlaps the MFMAs of the last.
 // Inside a stage, lane (col, kg) feeds K [16kg, 16kg+8) to the first MFMA and
 // [16kg+8, 16kg+16) to the second, for both operands (a dot product does not
 // depend on the order of its terms).
@@ -36,8 +36,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * kWave;
 constexpr int kRows = 256;                    // rows per workgroup (= block_m)
 constexpr int kOut = 128;                     // output columns per workgroup
 constexpr int kBK = 64;                       // K per stage
@@ -47,11 +45,15 @@ constexpr int kBRow = kBK;                    // bytes per weight row per stage
 constexpr int kAStage = kRows * kARow;        // 32 KB
 constexpr int kBStage = 2 * kOut * kBRow;     // 16 KB
 constexpr int kStageBytes = kAStage + kBStage;
-constexpr int kADma = kAStage / (kThreads * 16);   // 16-byte copies per thread per stage
-constexpr int kBDma = kBStage / (kThreads * 16);
+
+constexpr int k1Waves = 4;
+constexpr int k1Threads = k1Waves * kWave;
+constexpr int k1ADma = kAStage / (k1Threads * 16);  // 16-byte copies per thread per stage
+constexpr int k1BDma = kBStage / (k1Threads * 16);
+constexpr int k1Dma = k1ADma + k1BDma;
 
 template <bool F16>
-__global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) {
+__global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
 
   const int tid = threadIdx.x;
@@ -74,49 +76,56 @@ __global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) 
   ntw = ntw < 0 ? 0 : (ntw > 8 ? 8 : ntw);
   const int nst = static_cast<int>(H / kBK);
 
-  // copy sources.  Rows that hold no token read token 0's row (never used):
-  // every lane issues every copy, so the per-thread copy count is fixed.
-  const uint16_t* x = static_cast<const uint16_t*>(p.x);
-  const uint16_t* asrc[kADma];
+  // copy sources, as 32-bit byte offsets into two buffer resources (x, and
+  // the w13 rows of expert e; both under 2^31 bytes, which the launcher
+  // checks).  Rows that hold no token read token 0's row (never used): every
+  // lane issues every copy, so the per-thread copy count is fixed.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, static_cast<uint32_t>(p.T * H * 2));
+  uint32_t aoffs[k1ADma];
 #pragma unroll
-  for (int i = 0; i < kADma; ++i) {
-    const int r = wave * (kRows / kWaves) + i * 8 + (lane >> 3);
+  for (int i = 0; i < k1ADma; ++i) {
+    const int r = wave * (kRows / k1Waves) + i * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz_a(r);
     const int f = r < nrows ? p.sorted_ids[row0 + r] : static_cast<int>(Tk);
-    const int64_t t = f < Tk ? f / static_cast<int>(p.k) : 0;
-    asrc[i] = x + t * H + c * 8;
+    const uint32_t t = f < Tk ? static_cast<uint32_t>(f / static_cast<int>(p.k)) : 0u;
+    aoffs[i] = (t * static_cast<uint32_t>(H) + static_cast<uint32_t>(c * 8)) * 2u;
   }
+  // a wave copies 64 weight rows of one half (gate for waves 0-1, up for
+  // 2-3): row b + 16 i has the swizzle of row b, so one lane offset serves
+  // all four copies and the row step goes into the uniform offset
   const int64_t nb = static_cast<int64_t>(blockIdx.x) * kOut;
-  const int8_t* bsrc[kBDma];
-#pragma unroll
-  for (int i = 0; i < kBDma; ++i) {
-    const int b = wave * (2 * kOut / kWaves) + i * 16 + (lane >> 2);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(p.w13 + static_cast<int64_t>(e) * 2 * I * p.ldw, static_cast<uint32_t>(2 * I * p.ldw));
+  uint32_t boffv;
+  {
+    const int b = wave * (2 * kOut / k1Waves) + (lane >> 2);
     const int c = (lane & 3) ^ swz_b(b);
     const int64_t n = b < kOut ? nb + b : I + nb + (b - kOut);
-    bsrc[i] = p.w13 + (static_cast<int64_t>(e) * 2 * I + n) * p.ldw + c * 16;
+    boffv = static_cast<uint32_t>(n * p.ldw + c * 16);
   }
-  auto issue = [&](int s, int slot) {
+  const uint32_t bstep = static_cast<uint32_t>(16 * p.ldw);
+  // copy number i (of k1Dma) of stage s into LDS slot `slot`
+  auto issue_one = [&](int s, int slot, int i) {
     uint8_t* base = smem + slot * kStageBytes;
-#pragma unroll
-    for (int i = 0; i < kADma; ++i)
-      dma16(asrc[i] + static_cast<int64_t>(s) * kBK, base + (wave * (kRows / kWaves) + i * 8) * kARow);
-#pragma unroll
-    for (int i = 0; i < kBDma; ++i)
-      dma16(bsrc[i] + static_cast<int64_t>(s) * kBK, base + kAStage + (wave * (2 * kOut / kWaves) + i * 16) * kBRow);
+    if (i < k1ADma)
+      dma16_buf(xr, aoffs[i], static_cast<uint32_t>(s * kBK * 2), base + (wave * (kRows / k1Waves) + i * 8) * kARow);
+    else
+      dma16_buf(wr, boffv, static_cast<uint32_t>(s * kBK) + (i - k1ADma) * bstep,
+                base + kAStage + (wave * (2 * kOut / k1Waves) + (i - k1ADma) * 16) * kBRow);
   };
 
-  f32x4 acc[8][4];
+  f32x4 acc[8][8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this lane's weight rows inside the stage tile (gate j < 2, up j >= 2)
-  int boff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int b = (j < 2 ? wn * 32 + 16 * j : kOut + wn * 32 + 16 * (j - 2)) + col;
-    boff[j] = kAStage + b * kBRow + 16 * (kg ^ swz_b(b));
+  // this lane's weight rows inside the stage tile (gate j < 4, up j >= 4):
+  // row b0 + 16 j (+ kOut for up), all with the swizzle of b0
+  int boff0;
+  {
+    const int b = wn * 64 + col;
+    boff0 = kAStage + b * kBRow + 16 * (kg ^ swz_b(b));
   }
   // activation fragment offsets: the swizzle of row 16 mt + col depends on mt mod 4
   int aoff[4][2];
@@ -131,38 +140,127 @@ __global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) 
   // wave so that partly filled blocks skip their empty tiles without branches
   auto run = [&](auto tiles) {
     constexpr int MT = decltype(tiles)::value;
-    issue(0, 0);
-    if (nst > 1) issue(1, 1);
-    int slot = 0;
-    for (int s = 0; s < nst; ++s) {
-      if (s + 1 < nst) wait_vmcnt<kADma + kBDma>();
-      else wait_vmcnt<0>();
-      stage_barrier();
-      if (s + 2 < nst) issue(s + 2, slot == 0 ? 2 : slot - 1);
-      const uint8_t* st = smem + slot * kStageBytes;
-
-      // all activation fragments of the stage first, then column tile by
-      // column tile: converting tile j+1 overlaps the MFMAs of tile j
-      u32x4 q[4], af[MT > 0 ? MT : 1][2];
+    // Registers: af[mt][h] = activation fragment of row tile mt for K half
+    // h; rw[j][h] = the 8 int8 weight codes of column tile j for K half h;
+    // cw[h][j] = those codes as a 16-bit MFMA operand.  Half 0 of a stage
+    // multiplies with cw[0] while converting the stage's half-1 codes into
+    // cw[1]; half 1 multiplies with cw[1] while converting the next stage's
+    // half-0 codes into cw[0].  Every register a half has finished with is
+    // refilled from the next stage's LDS slot right away.
+    u32x4 af[MT > 0 ? MT : 1][2];
+    u32x2 rw[8][2];
+    u32x4 cw[2][8];
+    auto read_a = [&](const uint8_t* st, int mt, int h) {
+      af[mt][h] = *reinterpret_cast<const u32x4*>(st + mt / 4 * 64 * kARow + aoff[mt & 3][h]);
+    };
+    auto read_w = [&](const uint8_t* st, int j, int h) {
+      rw[j][h] = *reinterpret_cast<const u32x2*>(st + boff0 + (j & 3) * 16 * kBRow + (j >> 2) * kOut * kBRow + 8 * h);
+    };
+    auto conv = [&](int j, int h) {
+      const u32x2 p0 = F16 ? i8x4_to_f16x4(rw[j][h].x) : i8x4_to_bf16x4(rw[j][h].x);
+      const u32x2 p1 = F16 ? i8x4_to_f16x4(rw[j][h].y) : i8x4_to_bf16x4(rw[j][h].y);
+      cw[h][j] = u32x4{p0.x, p0.y, p1.x, p1.y};
+    };
+    // column tiles handled in row-tile slot m: [jlo(m), jlo(m + 1))
+    constexpr int MT1 = MT > 0 ? MT : 1;
+    auto jlo = [](int m) { return m * 8 / MT1; };
+    // scheduling of one slot (8 MFMAs, nconv conversions of 12 VALU each, a
+    // few LDS reads): MFMA and VALU alternate so that the conversions and
+    // address arithmetic issue while the matrix core works
+    auto interleave = []() {
+      constexpr int per = (12 * ((8 + MT1 - 1) / MT1) + 7) / 8 + 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) q[j] = *reinterpret_cast<const u32x4*>(st + boff[j]);
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, per, 0);   // VALU
+        if (i < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+        if (i == 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy to LDS
+      }
+    };
+
+    // one stage: make stage s+1 visible (every thread's copies of it have
+    // landed and every wave has read stage s out of its slot), then multiply
+    // stage s while reading stage s+1 and refilling stage s's slot with
+    // stage s+3 (the last stage's index past the end: those copies are never
+    // read).  The copies are spread over the row-tile slots so that no wave
+    // stalls on a burst of them.  The last stage (MORE = false) only
+    // multiplies.
+    constexpr int kSlots = 2 * MT1;
+    auto copies = [&](int s, int m) {
+      const int sc = s + 3 < nst ? s + 3 : nst - 1;
+#pragma unroll
+      for (int i = m * k1Dma / kSlots; i < (m + 1) * k1Dma / kSlots; ++i) issue_one(sc, s % kStages, i);
+    };
+    auto step = [&](int s, auto more_tag) {
+      constexpr bool MORE = decltype(more_tag)::value;
+      if constexpr (MORE) {
+        wait_vmcnt_lgkm0<k1Dma>();
+        stage_barrier();
+      }
+      if constexpr (MT == 0) {
+        if constexpr (MORE) {
+#pragma unroll
+          for (int m = 0; m < kSlots; ++m) copies(s, m);
+        }
+      } else {
+        const uint8_t* nx = smem + ((s + 1) % kStages) * kStageBytes;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[mt][j] = mfma16<F16>(af[mt][0], cw[0][j], acc[mt][j]);
+          if constexpr (MORE) {
+            read_a(nx, mt, 0);
+            copies(s, mt);
+          }
+#pragma unroll
+          for (int j = jlo(mt); j < jlo(mt + 1); ++j) {
+            conv(j, 1);
+            if constexpr (MORE) read_w(nx, j, 0);
+          }
+          interleave();
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[mt][j] = mfma16<F16>(af[mt][1], cw[1][j], acc[mt][j]);
+          if constexpr (MORE) {
+            read_a(nx, mt, 1);
+            copies(s, MT + mt);
+#pragma unroll
+            for (int j = jlo(mt); j < jlo(mt + 1); ++j) {
+              conv(j, 0);
+              read_w(nx, j, 1);
+            }
+            interleave();
+          }
+        }
+      }
+    };
+
+    // stages 0, 1, 2 into slots 0, 1, 2 (indices past the end repeat the
+    // last stage), then wait for stage 0
+#pragma unroll
+    for (int q = 0; q < kStages; ++q)
+#pragma unroll
+      for (int i = 0; i < k1Dma; ++i) issue_one(q < nst ? q : nst - 1, q, i);
+    wait_vmcnt<2 * k1Dma>();
+    stage_barrier();
+    if constexpr (MT > 0) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint8_t* ar = st + mt / 4 * 64 * kARow;
-        af[mt][0] = *reinterpret_cast<const u32x4*>(ar + aoff[mt & 3][0]);
-        af[mt][1] = *reinterpret_cast<const u32x4*>(ar + aoff[mt & 3][1]);
+        read_a(smem, mt, 0);
+        read_a(smem, mt, 1);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 b[2];
-        i8x16_to_operands<F16>(q[j], b[0], b[1]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16<F16>(af[mt][ks], b[ks], acc[mt][j]);
+      for (int j = 0; j < 8; ++j) {
+        read_w(smem, j, 0);
+        read_w(smem, j, 1);
       }
-      slot = slot == kStages - 1 ? 0 : slot + 1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) conv(j, 0);
     }
+    for (int s = 0; s + 1 < nst; ++s) step(s, std::true_type{});
+    step(nst - 1, std::false_type{});
   };
   if (ntw > 6) run(std::integral_constant<int, 8>{});
   else if (ntw > 4) run(std::integral_constant<int, 6>{});
@@ -173,10 +271,10 @@ __global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) 
   // epilogue: scales, SiLU(gate) * up, hi/lo planes; padding rows get 0
   uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.a);
   uint16_t* a_lo = a_hi + p.cap * I;
-  float sg[2], su[2];
+  float sg[4], su[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = nb + wn * 32 + 16 * j + col;
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = nb + wn * 64 + 16 * j + col;
     sg[j] = p.s13[static_cast<int64_t>(e) * 2 * I + n];
     su[j] = p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
   }
@@ -188,11 +286,11 @@ __global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) 
         const int64_t r = row0 + wm * 128 + mt * 16 + kg * 4 + i;
         const bool valid = p.sorted_ids[r] < Tk;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float v = valid ? silu_mul(acc[mt][j][i] * sg[j], acc[mt][j + 2][i] * su[j]) : 0.0f;
+        for (int j = 0; j < 4; ++j) {
+          const float v = valid ? silu_mul(acc[mt][j][i] * sg[j], acc[mt][j + 4][i] * su[j]) : 0.0f;
           const uint32_t hi = pack_bf16_rne(v, 0.0f) & 0xffffu;
           const uint32_t lo = pack_bf16_rne(v - __uint_as_float(hi << 16), 0.0f) & 0xffffu;
-          const int64_t o = r * I + nb + wn * 32 + 16 * j + col;
+          const int64_t o = r * I + nb + wn * 64 + 16 * j + col;
           a_hi[o] = static_cast<uint16_t>(hi);
           a_lo[o] = static_cast<uint16_t>(lo);
         }
@@ -207,6 +305,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_big_kernel(const Gemm1Args p) 
 // tiles, both planes of a through the MFMA with the same converted weight
 // fragment).  Stages of 64 K in the same 3-deep LDS ring: 2 x 16 KB of the
 // hi/lo planes and 16 KB of int8 w2 rows per stage.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
 constexpr int k2Rows = 128;
 constexpr int k2Cols = 256;
 constexpr int k2AStage = 2 * k2Rows * kARow;          // 32 KB
@@ -356,12 +456,17 @@ hipError_t launch_gemm2_w8_big(const Gemm2Args& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+bool gemm1_w8_big_fits(const Gemm1Args& p) {
+  return p.T * p.H * 2 < (int64_t{1} << 31) && 2 * p.I * p.ldw < (int64_t{1} << 31);
+}
+
 hipError_t launch_gemm1_w8_big(const Gemm1Args& p, hipStream_t stream) {
+  if (!gemm1_w8_big_fits(p)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.I / kOut), static_cast<unsigned>(p.cap / kRows));
   if (p.f16)
-    hipLaunchKernelGGL((gemm1_big_kernel<true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm1_big_kernel<true>), grid, dim3(k1Threads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm1_big_kernel<false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm1_big_kernel<false>), grid, dim3(k1Threads), 0, stream, p);
   return hipGetLastError();
 }
 

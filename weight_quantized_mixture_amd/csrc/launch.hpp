@@ -76,6 +76,8 @@ hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, const int8_t* qhi, const
                             hipStream_t stream);
 // block_m == 256 GEMMs with both operands copied straight into a 3-stage LDS ring
 // (GEMM2 needs H to be a multiple of 256).
+// the 256-row GEMM1 addresses x and one expert's w13 with 32-bit offsets
+bool gemm1_w8_big_fits(const Gemm1Args& p);
 hipError_t launch_gemm1_w8_big(const Gemm1Args& p, hipStream_t stream);
 hipError_t launch_gemm2_w8_big(const Gemm2Args& p, hipStream_t stream);
 
