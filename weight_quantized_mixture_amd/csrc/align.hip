@@ -175,9 +175,10 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
     float* __restrict__ topk_w, int32_t* __restrict__ topk_ids, int bm, int64_t cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded) {
+  __shared__ __attribute__((aligned(16))) uint64_t keys[kAlignWaves][kRankMaxExperts];
   const int wave = threadIdx.x / kWave;
   for (int64_t t = wave; t < T; t += kAlignWaves)
-    route_token(logits + t * E, E, k, renormalize, topk_w + t * k, topk_ids + t * k);
+    route_token(logits + t * E, E, k, renormalize, topk_w + t * k, topk_ids + t * k, keys[wave]);
   __syncthreads();
   align_body<true>(topk_ids, T * k, E, bm, cap, sorted_ids, block_expert, num_padded);
 }

@@ -13,9 +13,10 @@ constexpr int kRouteWaves = 4;
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_topk_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int renormalize,
     float* __restrict__ topk_w, int32_t* __restrict__ topk_ids) {
+  __shared__ __attribute__((aligned(16))) uint64_t keys[kRouteWaves][kRankMaxExperts];
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteWaves + (threadIdx.x / kWave);
   if (t >= T) return;
-  route_token(logits + t * E, E, k, renormalize, topk_w + t * k, topk_ids + t * k);
+  route_token(logits + t * E, E, k, renormalize, topk_w + t * k, topk_ids + t * k, keys[threadIdx.x / kWave]);
 }
 
 }  // namespace
