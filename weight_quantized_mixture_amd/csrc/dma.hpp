@@ -43,6 +43,9 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
+// s_waitcnt lgkmcnt(0): this thread's LDS accesses (and scalar loads) are done.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
+
 // Workgroup barrier that waits for nothing but keeps the compiler from moving
 // memory accesses across it (the LDS copies are waited for explicitly).
 __device__ __forceinline__ void stage_barrier() {

@@ -14,7 +14,8 @@
 // scale never rounds a weight.  The weights of the next three steps are in
 // flight while a step is converted and multiplied (packed rows are short, so a
 // wave needs several steps of loads outstanding to cover HBM latency); the
-// group scales, zero words and activation rows travel with them.
+// group scales, zero words and activation rows travel with them, and the
+// barrier that ends a step waits for LDS only, so they stay in flight.
 //
 // fp16 activations: 0x6400 | q is the half 1024 + q and one packed subtraction
 // of 1024 + z leaves q - z exactly; decoding nibble pairs (q_i, q_{i+4}) puts
@@ -25,6 +26,7 @@
 // bf16 activations: codes go through fp32 into bf16 (natural order) and the
 // planes are bf16.
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace moe {
@@ -170,24 +172,32 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
   }
   const uint16_t* xa = ROLE == 1 ? static_cast<const uint16_t*>(p1.x) : reinterpret_cast<const uint16_t*>(p2.a);
   const int64_t plane = ROLE == 1 ? 0 : p2.cap * I;
+  // every lane issues every load (rows without a token read offset 0 and
+  // are zeroed afterwards), so the number of loads in flight is the same on
+  // every path and the compiler's waits stay exact
+  int64_t srcs[CPT];
+  bool use[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    use[c] = cv[c] && src[c] >= 0;
+    srcs[c] = use[c] ? src[c] : 0;
+  }
   auto load_a = [&](int s, u32x4 (&regs)[NPLANE][CPT]) {
     const int64_t ko = static_cast<int64_t>(sbeg + s) * kStep;
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
 #pragma unroll
-      for (int pl = 0; pl < NPLANE; ++pl) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (cv[c] && src[c] >= 0) v = ld16(xa + pl * plane + src[c] + ko);
-        regs[pl][c] = v;
-      }
+      for (int pl = 0; pl < NPLANE; ++pl) regs[pl][c] = ld16(xa + pl * plane + srcs[c] + (use[c] ? ko : 0));
   };
   auto store_a = [&](int buf, const u32x4 (&regs)[NPLANE][CPT]) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
       if (cv[c]) {
 #pragma unroll
-        for (int pl = 0; pl < NPLANE; ++pl)
-          *reinterpret_cast<u32x4*>(&As[buf][pl][dst[c]]) = F16 ? perm0415(regs[pl][c]) : regs[pl][c];
+        for (int pl = 0; pl < NPLANE; ++pl) {
+          const u32x4 v = use[c] ? regs[pl][c] : u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&As[buf][pl][dst[c]]) = F16 ? perm0415(v) : v;
+        }
       }
   };
 
@@ -221,10 +231,11 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
   typedef u32x4 ARegs[NPLANE][CPT];
   auto step = [&](int s, const Pre& cur, Pre& ahead, const ARegs& anext, ARegs& aahead) {
     const int buf = s & 1;
-    if (s + 3 < nsteps) {
-      load_a(s + 3, aahead);
-      wload(s + 3, ahead);
-    }
+    // step s+3, or the last step again near the end (same addresses, never
+    // used): an unconditional load count keeps the waits exact
+    const int sa = s + 3 < nsteps ? s + 3 : nsteps - 1;
+    load_a(sa, aahead);
+    wload(sa, ahead);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const uint32_t z = (cur.z[j] >> (4 * (nrow[j] & 7))) & 0xFu;
@@ -253,18 +264,21 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
       }
     }
     if (s + 1 < nsteps) store_a(buf ^ 1, anext);
-    __syncthreads();
+    // LDS writes done, then the barrier; the loads of later steps stay in
+    // flight across it (a full __syncthreads would wait for them too)
+    wait_lgkm0();
+    stage_barrier();
   };
   Pre q[4];
   ARegs ar[4];
   if (nsteps > 0) {
     load_a(0, ar[0]);
     wload(0, q[0]);
-    if (nsteps > 1) wload(1, q[1]);
-    if (nsteps > 2) wload(2, q[2]);
+    wload(nsteps > 1 ? 1 : 0, q[1]);
+    wload(nsteps > 2 ? 2 : nsteps - 1, q[2]);
     store_a(0, ar[0]);
-    if (nsteps > 1) load_a(1, ar[1]);
-    if (nsteps > 2) load_a(2, ar[2]);
+    load_a(nsteps > 1 ? 1 : 0, ar[1]);
+    load_a(nsteps > 2 ? 2 : nsteps - 1, ar[2]);
   }
   __syncthreads();
   for (int s = 0; s < nsteps; s += 4) {
