@@ -171,6 +171,10 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * lo = rne(v - hi) (16 significant bits), cap = moe_align_capacity.  Padding
  * rows of a block that holds rows get v = 0; 16-row groups made only of
  * padding may be left unwritten (GEMM2 never reads them).
+ * Exception: block_m = 256 with H a multiple of 256 and T*H*2 < 2^32
+ * (the prefill form): gemm1 writes the 16-bit fixed-point form described
+ * under moe_w8a16_requant directly, starting at byte offset 0 of `a`, and
+ * no planes.
  *
  * moe_w8a16_requant: for block_m in [32, 64] (a no-op otherwise) turns the
  * planes into the 16-bit fixed-point form the integer GEMM2 reads, stored
@@ -184,8 +188,9 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * split s < splits, h < H:
  *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} v[r, i] w2[e,h,i]
  * with v as moe_w8a16_gemm1 and moe_w8a16_requant left it in `a` (the
- * fixed-point form for block_m in [32, 64]; the hi + lo planes otherwise,
- * which for block_m = 16 GEMM2 rounds to the same fixed-point form itself).  The K range [0, I) is cut
+ * fixed-point form for block_m in [32, 64] and for the prefill form of
+ * block_m = 256; the hi + lo planes otherwise, which for block_m = 16 GEMM2
+ * rounds to the same fixed-point form itself).  The K range [0, I) is cut
  * into `splits` parts of whole 128-wide steps (1 <= splits <= I/128; equal
  * parts, so splits must divide I/128, when block_m > 64; 1 when block_m is
  * 256).  y is device fp32 [splits, T*k, H]; rows of dropped ids are not

@@ -88,12 +88,19 @@ def test_quantize_w4_random_and_golden(group):
 
 @pytest.mark.parametrize("T,E,k,renorm", [(37, 8, 2, True), (16, 64, 6, True), (33, 128, 8, True),
                                           (5, 1024, 8, True), (9, 5, 5, False), (64, 8, 1, True),
-                                          (3, 100, 7, False), (1, 1, 1, True)])
+                                          (3, 100, 7, False), (1, 1, 1, True), (12, 256, 16, True),
+                                          (7, 257, 3, True), (4, 65, 65, True)])
 def test_route(T, E, k, renorm):
+    # E <= 256 takes the rank path, larger E the arg-max rounds
     log(f"[route] T={T} E={E} k={k} renorm={renorm}")
     logits = synthetic.random_logits(T, E, seed=T * E + k)
     if E >= 4:
         logits[0, 1] = logits[0, 3] = np.float32(logits[0].max() + 1)   # a tie at the top
+    if E >= 8 and T >= 2:
+        # -0 and +0 compare equal: the lower id wins
+        logits[1] = -np.abs(logits[1]) - np.float32(1)
+        logits[1, 6] = np.float32(0.0)
+        logits[1, 2] = np.float32(-0.0)
     tw, ti, w_ref, ids_ref = route_both(logits, k, renorm)
     np.testing.assert_array_equal(ti.cpu().numpy(), ids_ref)
     np.testing.assert_allclose(tw.cpu().numpy(), w_ref, rtol=0, atol=1e-6)
@@ -152,6 +159,54 @@ def test_align_empty():
     pkg.moe_align_block(torch.empty(0, 2, dtype=torch.int32, device=DEV), 8, 16, e, e, n)
     torch.cuda.synchronize()
     assert int(n.item()) == 0
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_gemm1_q16_blocks_of_256(act):
+    # 256-row blocks with H a multiple of 256: GEMM1 writes the 16-bit
+    # fixed-point form itself, at the start of the intermediate
+    E, k, H, I, T, bm = 4, 2, 512, 384, 300, 256
+    log(f"[gemm1 q16] act={act} E={E} H={H} I={I} T={T}")
+    W = small_w8(E, H, I, seed=13)
+    xb = synthetic.random_activations(T, H, act, seed=14)
+    logits = synthetic.random_logits(T, E, seed=15)
+    tw, ti, w_ref, ids_ref = route_both(logits, k)
+    cap = pkg.moe_align_capacity(T, k, E, bm)
+    s = torch.empty(cap, dtype=torch.int32, device=DEV)
+    b = torch.empty(cap // bm, dtype=torch.int32, device=DEV)
+    n = torch.empty(1, dtype=torch.int32, device=DEV)
+    pkg.moe_align_block(ti, E, bm, s, b, n)
+    nbytes = pkg.moe_w8a16_intermediate_bytes(T, H, I, E, k, bm)
+    a = torch.full(((nbytes + 1) // 2,), 0x7FC0, dtype=torch.int16, device=DEV)
+    pkg.moe_w8a16_gemm1(to_dev_act(xb, act), W.w13, W.s13, s, b, n, bm, k, a)
+    torch.cuda.synchronize()
+    sr, br, nr = oracle.align_block(ids_ref, E, bm)
+    raw = a.cpu().numpy().view(np.uint8)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    qh = raw[:cap * I].view(np.int8).reshape(cap, I).astype(np.int64)
+    ql = raw[up(cap * I):up(cap * I) + cap * I].view(np.int8).reshape(cap, I).astype(np.int64)
+    o = 2 * up(cap * I)
+    qs = raw[o:o + cap * (I // 128) * 4].view(np.float32).reshape(cap, I // 128).astype(np.float64)
+    xf = oracle.act_bits_to_f64(xb, act)
+    checked = 0
+    for blk in range(nr // bm):
+        W13 = oracle.dequant_int8_rows(W.q13[br[blk]], W.hs13[br[blk]])
+        rows = sr[blk * bm:(blk + 1) * bm]
+        for r_local in range(16 * ((np.sum(rows < T * k) + 15) // 16)):
+            r = blk * bm + r_local
+            f = rows[r_local]
+            if f >= T * k:
+                assert np.all(qh[r] == 0) and np.all(ql[r] == 0) and np.all(qs[r] == 0.0)
+                continue
+            ref = oracle.moe_expert_intermediate(xf[f // k][None], W13, I)[0]
+            gmax = np.abs(ref).reshape(-1, 128).max(axis=1)
+            assert np.allclose(qs[r], gmax / 32639.0, rtol=1e-4, atol=0.0), (blk, r_local)
+            sc = np.repeat(qs[r], 128)
+            vq = sc * (256.0 * qh[r] + ql[r])
+            tol = 0.51 * sc + 2e-5 * np.abs(ref).max() + 1e-4 * np.abs(ref)
+            assert np.all(np.abs(vq - ref) <= tol), (blk, r_local, np.abs(vq - ref).max())
+            checked += 1
+    assert checked == T * k
 
 
 @pytest.mark.parametrize("act,bm", [("bf16", 16), ("fp16", 32), ("bf16", 64), ("bf16", 48)])

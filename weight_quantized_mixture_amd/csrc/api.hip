@@ -64,6 +64,45 @@ int64_t auto_block_m(int64_t T, int64_t E, int64_t k) {
 
 bool use_prefill(int64_t bm) { return bm == 256; }
 
+// 16-row blocks quantize inside GEMM2; 32 to 64 rows read the requantized form.
+bool needs_requant(int64_t bm) { return bm >= 32 && bm <= 64; }
+
+// The intermediate: bf16 hi/lo planes [2, cap, I]; for blocks of 32 to 64
+// rows followed by the int8 hi codes [cap, I], lo codes [cap, I] and fp32
+// scales [cap, I/128] the integer GEMM2 reads.  With prefill_q16 (256-row
+// blocks) that fixed-point form alone sits at offset 0, in the planes' space.
+struct Q16 {
+  int8_t* hi;
+  int8_t* lo;
+  float* scale;
+};
+
+size_t planes_bytes(int64_t cap, int64_t I) { return align_up(static_cast<size_t>(cap) * static_cast<size_t>(I) * 4); }
+
+size_t intermediate_bytes(int64_t cap, int64_t I, int64_t bm, bool w8) {
+  size_t b = planes_bytes(cap, I);
+  if (w8 && needs_requant(bm)) {
+    b += 2 * align_up(static_cast<size_t>(cap) * static_cast<size_t>(I));
+    b += align_up(static_cast<size_t>(cap) * static_cast<size_t>(I / 128) * 4);
+  }
+  return b;
+}
+
+Q16 q16_at(const float* a, int64_t cap, int64_t I, size_t offset) {
+  char* base = const_cast<char*>(reinterpret_cast<const char*>(a)) + offset;
+  const size_t codes = align_up(static_cast<size_t>(cap) * static_cast<size_t>(I));
+  return Q16{reinterpret_cast<int8_t*>(base), reinterpret_cast<int8_t*>(base + codes),
+             reinterpret_cast<float*>(base + 2 * codes)};
+}
+
+// 256-row blocks keep the intermediate as 16-bit fixed point (written by
+// GEMM1's epilogue, read by the integer-MFMA GEMM2) when both 256-row
+// kernels apply; otherwise as bf16 planes.  Decided from (T, H, block_m),
+// which every stage call knows, so GEMM1 and GEMM2 always agree.
+bool prefill_q16(int64_t T, int64_t H, int64_t bm) {
+  return use_prefill(bm) && H % 256 == 0 && T * H * 2 < (int64_t{1} << 32);
+}
+
 bool use_stream(int64_t bm) { return bm <= 64; }
 
 // Rough count of align blocks that hold rows (the exact count stays on the
@@ -90,7 +129,13 @@ int gemm1_kways(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t b
 }
 
 hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t stream) {
-  if (use_prefill(p.block_m) && moe::gemm1_w8_big_fits(p)) return moe::launch_gemm1_w8_big(p, stream);
+  if (use_prefill(p.block_m) && moe::gemm1_w8_big_fits(p)) {
+    if (prefill_q16(T, p.H, p.block_m)) {
+      const Q16 q = q16_at(p.a, p.cap, p.I, 0);
+      return moe::launch_gemm1_w8_big(p, q.hi, q.lo, q.scale, stream);
+    }
+    return moe::launch_gemm1_w8_big(p, nullptr, nullptr, nullptr, stream);
+  }
   if (!use_stream(p.block_m)) return moe::launch_gemm1_w8(p, stream);
   if (p.block_m == 16 || p.block_m == 32) return moe::launch_gemm1_w8_dma(p, stream);
   if (p.block_m == 64) return moe::launch_gemm1_w8_lds(p, 1, 1, stream);
@@ -105,8 +150,6 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
 // generic tiled kernel (equal splits of whole 128-wide steps).
 bool gemm2_int8(int64_t bm) { return bm <= 64; }
 
-// 16-row blocks quantize inside GEMM2; 32 to 64 rows read the requantized form.
-bool needs_requant(int64_t bm) { return bm >= 32 && bm <= 64; }
 
 // Expected rows per active expert above half a tile: more MFMA work per
 // weight byte, so narrower waves (more workgroups) stream better.
@@ -154,44 +197,20 @@ int64_t w4_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t
   return sp;
 }
 
-// The intermediate: bf16 hi/lo planes [2, cap, I]; for blocks of 32 to 64
-// rows followed by the int8 hi codes [cap, I], lo codes [cap, I] and fp32
-// scales [cap, I/128] the integer GEMM2 reads.
-struct Q16 {
-  int8_t* hi;
-  int8_t* lo;
-  float* scale;
-};
-
-size_t planes_bytes(int64_t cap, int64_t I) { return align_up(static_cast<size_t>(cap) * static_cast<size_t>(I) * 4); }
-
-size_t intermediate_bytes(int64_t cap, int64_t I, int64_t bm, bool w8) {
-  size_t b = planes_bytes(cap, I);
-  if (w8 && needs_requant(bm)) {
-    b += 2 * align_up(static_cast<size_t>(cap) * static_cast<size_t>(I));
-    b += align_up(static_cast<size_t>(cap) * static_cast<size_t>(I / 128) * 4);
-  }
-  return b;
-}
-
-Q16 q16_of(const float* a, int64_t cap, int64_t I) {
-  char* base = const_cast<char*>(reinterpret_cast<const char*>(a)) + planes_bytes(cap, I);
-  const size_t codes = align_up(static_cast<size_t>(cap) * static_cast<size_t>(I));
-  return Q16{reinterpret_cast<int8_t*>(base), reinterpret_cast<int8_t*>(base + codes),
-             reinterpret_cast<float*>(base + 2 * codes)};
-}
-
 hipError_t run_gemm1_and_requant(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t stream) {
   hipError_t e = run_gemm1(p, T, E, stream);
   if (e != hipSuccess || !needs_requant(p.block_m)) return e;
-  const Q16 q = q16_of(p.a, p.cap, p.I);
+  const Q16 q = q16_at(p.a, p.cap, p.I, planes_bytes(p.cap, p.I));
   return moe::launch_requant_q16(p.a, p.cap, p.I, p.sorted_ids, p.num_padded, p.Tk, q.hi, q.lo, q.scale, stream);
 }
 
 hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, hipStream_t stream) {
-  if (use_prefill(p.block_m) && p.H % 256 == 0) return moe::launch_gemm2_w8_big(p, stream);
+  if (prefill_q16(T, p.H, p.block_m)) {
+    const Q16 q = q16_at(p.a, p.cap, p.I, 0);
+    return moe::launch_gemm2_w8_big_q16(p, q.hi, q.lo, q.scale, stream);
+  }
   if (!gemm2_int8(p.block_m)) return moe::launch_gemm2_w8(p, stream);
-  const Q16 q = q16_of(p.a, p.cap, p.I);
+  const Q16 q = q16_at(p.a, p.cap, p.I, planes_bytes(p.cap, p.I));
   return moe::launch_gemm2_q16(p, gemm2_nt(T, E, k, p.block_m), q.hi, q.lo, q.scale, stream);
 }
 
@@ -383,7 +402,7 @@ int moe_w8a16_requant(float* a, int64_t T, int64_t I, int64_t E, int64_t k, cons
   if (!a || !sorted_ids || !num_padded) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
   if (!aligned(a, 16)) return fail(MOE_ERR_INVALID_ARGUMENT, "a must be 16-byte aligned");
   const int64_t cap = capacity(T, k, E, block_m);
-  const Q16 q = q16_of(a, cap, I);
+  const Q16 q = q16_at(a, cap, I, planes_bytes(cap, I));
   return hip_status(moe::launch_requant_q16(a, cap, I, sorted_ids, num_padded, T * k, q.hi, q.lo, q.scale, stream),
                     "requant");
 }

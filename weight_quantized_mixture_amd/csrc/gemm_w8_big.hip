@@ -3,8 +3,15 @@
 //
 // experts_int8 page, ExpertsInt8MoEMethod.create_weights / apply ->
 // fused_experts(use_int8_w8a16): h = x dequant(w13[e])^T with the per-row
-// scale on the fp32 accumulator, a = silu(h_gate) * h_up, written as bf16
-// hi/lo planes (hi = rne(a), lo = rne(a - hi)).
+// scale on the fp32 accumulator, a = silu(h_gate) * h_up, then
+// y = a dequant(w2[e])^T.  GEMM1 writes a either as bf16 hi/lo planes
+// (hi = rne(a), lo = rne(a - hi)) or, when GEMM2 below runs, directly as
+// 16-bit fixed point per (row, 128 columns): a ~= s (256 hi + lo) with
+// s = max|a| / 32639 over the group, which is exactly the 128 output columns
+// of one GEMM1 workgroup (the two waves sharing a row exchange their row
+// maxima through LDS).  GEMM2 then runs the int8 codes of w2 and of a
+// through v_mfma_i32_16x16x64_i8 (half the MFMA work of two bf16 planes,
+// and 32 instead of 48 KB per stage to copy).
 //
 // GEMM1 tiling: a workgroup owns one align block (256 rows) and 128 output
 // columns, i.e. 128 gate + the matching 128 up rows of w13.  Its 4 waves (one
@@ -46,19 +53,24 @@ constexpr int kAStage = kRows * kARow;        // 32 KB
 constexpr int kBStage = 2 * kOut * kBRow;     // 16 KB
 constexpr int kStageBytes = kAStage + kBStage;
 
+constexpr int kQMax = 32639;                  // 256 * 127 + 127
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int k1Waves = 4;
 constexpr int k1Threads = k1Waves * kWave;
 constexpr int k1ADma = kAStage / (k1Threads * 16);  // 16-byte copies per thread per stage
 constexpr int k1BDma = kBStage / (k1Threads * 16);
 constexpr int k1Dma = k1ADma + k1BDma;
 
-template <bool F16>
-__global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p) {
+template <bool F16, bool Q16>
+__global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p, int8_t* __restrict__ qhi,
+                                                              int8_t* __restrict__ qlo, float* __restrict__ qscale) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar registers
   const int wm = wave & 1, wn = wave >> 1;
   const int col = lane & 15;
   const int kg = lane >> 4;
@@ -76,10 +88,11 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p)
   ntw = ntw < 0 ? 0 : (ntw > 8 ? 8 : ntw);
   const int nst = static_cast<int>(H / kBK);
 
-  // copy sources, as 32-bit byte offsets into two buffer resources (x, and
-  // the w13 rows of expert e; both under 2^31 bytes, which the launcher
-  // checks).  Rows that hold no token read token 0's row (never used): every
-  // lane issues every copy, so the per-thread copy count is fixed.
+  // copy sources, as 32-bit byte offsets into buffer resources: x (under
+  // 2^32 bytes, which the launcher checks) and the 128 gate or up rows of
+  // w13 this wave copies.  Rows that hold no token read token 0's row (never
+  // used): every lane issues every copy, so the per-thread copy count is
+  // fixed.
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, static_cast<uint32_t>(p.T * H * 2));
   uint32_t aoffs[k1ADma];
 #pragma unroll
@@ -94,16 +107,22 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p)
   // 2-3): row b + 16 i has the swizzle of row b, so one lane offset serves
   // all four copies and the row step goes into the uniform offset
   const int64_t nb = static_cast<int64_t>(blockIdx.x) * kOut;
+  const bool up_half = wave >= k1Waves / 2;
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(p.w13 + static_cast<int64_t>(e) * 2 * I * p.ldw, static_cast<uint32_t>(2 * I * p.ldw));
+      make_rsrc(p.w13 + (static_cast<int64_t>(e) * 2 * I + (up_half ? I : 0) + nb) * p.ldw,
+                static_cast<uint32_t>(kOut * p.ldw));
+  // LDS row 16 q + r (q < 4, r < 16) of a wave's 64 holds source row 4 r + q,
+  // so that MFMA tile q, which takes rows 4 col + q, reads 16 consecutive
+  // LDS rows (conflict-free under the swizzle) and lane col ends up with the
+  // 4 adjacent output columns 4 col .. 4 col + 3.  Copy i of this lane:
+  // LDS row 16 i + lane/4, source row 4 (lane/4) + i.
   uint32_t boffv;
   {
-    const int b = wave * (2 * kOut / k1Waves) + (lane >> 2);
-    const int c = (lane & 3) ^ swz_b(b);
-    const int64_t n = b < kOut ? nb + b : I + nb + (b - kOut);
-    boffv = static_cast<uint32_t>(n * p.ldw + c * 16);
+    const int b = wave * (2 * kOut / k1Waves) + (lane >> 2);   // LDS row of copy 0
+    const int c = (lane & 3) ^ swz_b(b);                       // the same for every copy i
+    boffv = static_cast<uint32_t>(((wave & 1) * 64 + 4 * (lane >> 2)) * p.ldw + c * 16);
   }
-  const uint32_t bstep = static_cast<uint32_t>(16 * p.ldw);
+  const uint32_t bstep = static_cast<uint32_t>(p.ldw);
   // copy number i (of k1Dma) of stage s into LDS slot `slot`
   auto issue_one = [&](int s, int slot, int i) {
     uint8_t* base = smem + slot * kStageBytes;
@@ -120,8 +139,10 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this lane's weight rows inside the stage tile (gate j < 4, up j >= 4):
-  // row b0 + 16 j (+ kOut for up), all with the swizzle of b0
+  // this lane's weight rows inside the stage tile: tile j (gate j < 4, up
+  // j >= 4) reads LDS rows 16 (j & 3) + col of the wave's 64 (source rows
+  // 4 col + (j & 3)), all with the swizzle of LDS row col; the up rows sit
+  // kOut rows further
   int boff0;
   {
     const int b = wn * 64 + col;
@@ -267,60 +288,147 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p)
   else if (ntw > 2) run(std::integral_constant<int, 4>{});
   else if (ntw > 0) run(std::integral_constant<int, 2>{});
   else run(std::integral_constant<int, 0>{});
+  wait_vmcnt<0>();   // no copy into LDS outlives the main loop
 
-  // epilogue: scales, SiLU(gate) * up, hi/lo planes; padding rows get 0
-  uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.a);
-  uint16_t* a_lo = a_hi + p.cap * I;
+  // epilogue: scales, SiLU(gate) * up; padding rows get 0.  Lane col holds
+  // output columns n0 .. n0 + 3.  The ids of the lane's 32 rows (4
+  // consecutive rows per tile) are loaded together up front, so their
+  // latency is paid once.
+  const int64_t n0 = nb + wn * 64 + 4 * col;
+  bool valid[8][4];
+  {
+    i32x4 ids[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+      ids[mt] = *reinterpret_cast<const i32x4*>(p.sorted_ids + row0 + wm * 128 + mt * 16 + kg * 4);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) valid[mt][i] = mt < ntw && ids[mt][i] < Tk;
+  }
   float sg[4], su[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t n = nb + wn * 64 + 16 * j + col;
-    sg[j] = p.s13[static_cast<int64_t>(e) * 2 * I + n];
-    su[j] = p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
+    sg[j] = p.s13[static_cast<int64_t>(e) * 2 * I + n0 + j];
+    su[j] = p.s13[static_cast<int64_t>(e) * 2 * I + I + n0 + j];
   }
+  if constexpr (!Q16) {
+    // bf16 hi/lo planes
+    uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.a);
+    uint16_t* a_lo = a_hi + p.cap * I;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    if (mt < ntw) {
+    for (int mt = 0; mt < 8; ++mt) {
+      if (mt < ntw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t r = row0 + wm * 128 + mt * 16 + kg * 4 + i;
+          f32x4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[j] = valid[mt][i] ? silu_mul(acc[mt][j][i] * sg[j], acc[mt][j + 4][i] * su[j]) : 0.0f;
+          u32x2 hi, lo;
+          split_bf16x4(make_float4(v[0], v[1], v[2], v[3]), hi, lo);
+          *reinterpret_cast<u32x2*>(a_hi + r * I + n0) = hi;
+          *reinterpret_cast<u32x2*>(a_lo + r * I + n0) = lo;
+        }
+      }
+    }
+  } else {
+    // 16-bit fixed point per (row, the workgroup's 128 columns).  Row maxima:
+    // over this lane's 4 columns, the 16 lanes of the row (xor shuffles
+    // inside a 16-lane group), then the other wave of the row through LDS.
+    float* rmax = reinterpret_cast<float*>(smem);   // [2][256]; the ring is idle now
+    float m[8][4];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t r = row0 + wm * 128 + mt * 16 + kg * 4 + i;
-        const bool valid = p.sorted_ids[r] < Tk;
+        float mm = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = valid ? silu_mul(acc[mt][j][i] * sg[j], acc[mt][j + 4][i] * su[j]) : 0.0f;
-          const uint32_t hi = pack_bf16_rne(v, 0.0f) & 0xffffu;
-          const uint32_t lo = pack_bf16_rne(v - __uint_as_float(hi << 16), 0.0f) & 0xffffu;
-          const int64_t o = r * I + nb + wn * 64 + 16 * j + col;
-          a_hi[o] = static_cast<uint16_t>(hi);
-          a_lo[o] = static_cast<uint16_t>(lo);
+          const float v = valid[mt][i] ? silu_mul(acc[mt][j][i] * sg[j], acc[mt][j + 4][i] * su[j]) : 0.0f;
+          acc[mt][j][i] = v;
+          mm = fmaxf(mm, fabsf(v));
+        }
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) mm = fmaxf(mm, __shfl_xor(mm, d, kWave));
+        m[mt][i] = mm;
+      }
+    wait_vmcnt_lgkm0<0>();
+    stage_barrier();   // every wave is past its last copy and LDS read of the ring
+    if (col == 0) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rmax[wn * kRows + wm * 128 + mt * 16 + kg * 4 + i] = m[mt][i];
+    }
+    wait_lgkm0();
+    stage_barrier();
+    const int64_t G = I / kOut;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      if (mt < ntw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = wm * 128 + mt * 16 + kg * 4 + i;
+          const float mm = fmaxf(m[mt][i], rmax[(1 - wn) * kRows + rl]);
+          const float inv = mm > 0.0f ? static_cast<float>(kQMax) / mm : 0.0f;
+          const int64_t r = row0 + rl;
+          uint32_t hw = 0u, lw = 0u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            int q = static_cast<int>(__builtin_rintf(acc[mt][j][i] * inv));
+            q = q < -kQMax ? -kQMax : (q > kQMax ? kQMax : q);
+            const int h = (q + 128) >> 8;
+            hw |= static_cast<uint32_t>(h & 0xff) << (8 * j);
+            lw |= static_cast<uint32_t>((q - 256 * h) & 0xff) << (8 * j);
+          }
+          *reinterpret_cast<uint32_t*>(qhi + r * I + n0) = hw;
+          *reinterpret_cast<uint32_t*>(qlo + r * I + n0) = lw;
+          if (wn == 0 && col == 0) qscale[r * G + blockIdx.x] = mm / static_cast<float>(kQMax);
         }
       }
     }
   }
 }
 
-// GEMM2 for 256-row blocks: y = (hi + lo) dequant(w2[e])^T, scale on the
-// accumulator.  A workgroup owns 128 rows (half an align block) and 256
-// output columns; 8 waves in a 2 x 4 grid, each 64 rows x 64 columns (4 x 4
-// tiles, both planes of a through the MFMA with the same converted weight
-// fragment).  Stages of 64 K in the same 3-deep LDS ring: 2 x 16 KB of the
-// hi/lo planes and 16 KB of int8 w2 rows per stage.
+// GEMM2 for 256-row blocks on the fixed-point form of a: y = a dequant(w2[e])^T,
+// scale on the accumulator.  A workgroup owns 128 rows (half an align block)
+// and 256 output columns; 8 waves (2 per SIMD) in a 2 x 4 grid, each 64 rows
+// x 64 columns (4 x 4 tiles of v_mfma_i32_16x16x64_i8, hi and lo codes of a
+// against the same w2 fragment).  Stages of 64 K through a 4-deep LDS ring
+// filled with global_load_lds: 8 KB of hi codes, 8 KB of lo codes, 16 KB of
+// w2 codes and each wave's 64 row scales of the stage's group.  The copies
+// of stage s+3 are requested after the barrier of stage s (past the end the
+// last stage's index repeats, into a slot nobody reads), so the copy count
+// per stage is fixed.  Per stage and tile the two int32 results are folded
+// into fp32 as s_row * (256 hi + lo) (exact in int32: |.| < 2^29).
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int k2Rows = 128;
 constexpr int k2Cols = 256;
-constexpr int k2AStage = 2 * k2Rows * kARow;          // 32 KB
-constexpr int k2BStage = k2Cols * kBRow;              // 16 KB
-constexpr int k2StageBytes = k2AStage + k2BStage;
-constexpr int k2ADma = k2AStage / (kThreads * 16);
-constexpr int k2BDma = k2BStage / (kThreads * 16);
+constexpr int k2Ring = 4;
+constexpr int k2APlane = k2Rows * kBK;                // 8 KB
+constexpr int k2BBytes = k2Cols * kBK;                // 16 KB
+constexpr int k2SBytes = kWaves * 256;                // 64 scales per wave
+constexpr int k2StageBytes = 2 * k2APlane + k2BBytes + k2SBytes;
+constexpr int k2ADma = 2 * k2APlane / (kThreads * 16);
+constexpr int k2BDma = k2BBytes / (kThreads * 16);
+constexpr int k2Dma = k2ADma + k2BDma + 1;
 
-__global__ __launch_bounds__(kThreads) void gemm2_big_kernel(const Gemm2Args p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * k2StageBytes];
+__device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0,
+                                               0);
+}
+
+__global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args p, const int8_t* __restrict__ qhi,
+                                                                 const int8_t* __restrict__ qlo,
+                                                                 const float* __restrict__ qscale) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[k2Ring * k2StageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: scalar registers
   const int wm = wave & 1, wn = wave >> 1;
   const int col = lane & 15;
   const int kg = lane >> 4;
@@ -328,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_kernel(const Gemm2Args p) 
   const int64_t row0 = static_cast<int64_t>(blockIdx.y) * k2Rows;
   if (row0 >= *p.num_padded) return;
   const int e = p.block_expert[row0 / kRows];
-  const int64_t Tk = p.Tk, H = p.H, I = p.I;
+  const int64_t Tk = p.Tk, H = p.H, I = p.I, G = I / 128;
 
   int nrows = 0;
   for (int r = 0; r < k2Rows; r += 16)
@@ -338,32 +446,36 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_kernel(const Gemm2Args p) 
   ntw = ntw < 0 ? 0 : (ntw > 4 ? 4 : ntw);
   const int nst = static_cast<int>(I / kBK);
 
-  // A copies: (plane, row) pairs q = 0..255, 8 per copy instruction
-  const uint16_t* a16 = reinterpret_cast<const uint16_t*>(p.a);
-  const uint16_t* asrc[k2ADma];
+  // copies: code chunk g = (plane, row, 16-byte position) of the stage's
+  // hi/lo codes (LDS position g holds source chunk (g%4) ^ swz_b(row)), w2
+  // rows b, and this wave's 64 row scales
+  const int8_t* asrc[k2ADma];
 #pragma unroll
   for (int i = 0; i < k2ADma; ++i) {
-    const int q = wave * (2 * k2Rows / kWaves) + i * 8 + (lane >> 3);
-    const int pl = q / k2Rows, r = q % k2Rows;
-    const int c = (lane & 7) ^ swz_a(r);
-    asrc[i] = a16 + pl * p.cap * I + (row0 + r) * I + c * 8;
+    const int g = (wave * k2ADma + i) * kWave + lane;
+    const int pl = g / (k2Rows * 4), r = (g % (k2Rows * 4)) / 4;
+    const int c = (g & 3) ^ swz_b(r);
+    asrc[i] = (pl == 0 ? qhi : qlo) + (row0 + r) * I + c * 16;
   }
   const int64_t hb = static_cast<int64_t>(blockIdx.x) * k2Cols;
   const int8_t* bsrc[k2BDma];
 #pragma unroll
   for (int i = 0; i < k2BDma; ++i) {
-    const int b = wave * (k2Cols / kWaves) + i * 16 + (lane >> 2);
+    const int b = (wave * k2BDma + i) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ swz_b(b);
     bsrc[i] = p.w2 + (static_cast<int64_t>(e) * H + hb + b) * p.ldw + c * 16;
   }
-  auto issue = [&](int s, int slot) {
+  const float* ssrc = qscale + (row0 + wm * 64 + lane) * G;
+  auto issue = [&](int s, int slot) __attribute__((always_inline)) {
     uint8_t* base = smem + slot * k2StageBytes;
 #pragma unroll
     for (int i = 0; i < k2ADma; ++i)
-      dma16(asrc[i] + static_cast<int64_t>(s) * kBK, base + (wave * (2 * k2Rows / kWaves) + i * 8) * kARow);
+      dma16(asrc[i] + static_cast<int64_t>(s) * kBK, base + (wave * k2ADma + i) * 1024);
 #pragma unroll
     for (int i = 0; i < k2BDma; ++i)
-      dma16(bsrc[i] + static_cast<int64_t>(s) * kBK, base + k2AStage + (wave * (k2Cols / kWaves) + i * 16) * kBRow);
+      dma16(bsrc[i] + static_cast<int64_t>(s) * kBK, base + 2 * k2APlane + (wave * k2BDma + i) * 1024);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)const_cast<float*>(ssrc + s / 2),
+                                     (lds_ptr_t)(base + 2 * k2APlane + k2BBytes + wave * 256), 4, 0, 0);
   };
 
   f32x4 acc[4][4];
@@ -376,51 +488,49 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_kernel(const Gemm2Args p) 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int b = wn * 64 + 16 * j + col;
-    boff[j] = k2AStage + b * kBRow + 16 * (kg ^ swz_b(b));
+    boff[j] = 2 * k2APlane + b * kBK + 16 * (kg ^ swz_b(b));
   }
-  int aoff[4][2];
+  int aoff[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int r = wm * 64 + mt * 16 + col;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) aoff[mt][ks] = r * kARow + 16 * ((2 * kg + ks) ^ swz_a(r));
+    aoff[mt] = r * kBK + 16 * (kg ^ swz_b(r));
   }
 
-  auto run = [&](auto tiles) {
+  auto run = [&](auto tiles) __attribute__((always_inline)) {
     constexpr int MT = decltype(tiles)::value;
-    issue(0, 0);
-    if (nst > 1) issue(1, 1);
-    int slot = 0;
+#pragma unroll
+    for (int q = 0; q < k2Ring - 1; ++q) issue(q < nst ? q : nst - 1, q);
     for (int s = 0; s < nst; ++s) {
-      if (s + 1 < nst) wait_vmcnt<k2ADma + k2BDma>();
-      else wait_vmcnt<0>();
+      // this thread's copies of stage s landed (those of s+1, s+2 may still
+      // fly) and its LDS reads of stage s-1 done; then the slot of s-1 takes
+      // stage s+3
+      wait_vmcnt_lgkm0<2 * k2Dma>();
       stage_barrier();
-      if (s + 2 < nst) issue(s + 2, slot == 0 ? 2 : slot - 1);
-      const uint8_t* st = smem + slot * k2StageBytes;
-
-      u32x4 q[4], ah[MT > 0 ? MT : 1][2], al[MT > 0 ? MT : 1][2];
+      issue(s + 3 < nst ? s + 3 : nst - 1, (s + 3) % k2Ring);
+      const uint8_t* st = smem + (s % k2Ring) * k2StageBytes;
+      u32x4 bq[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) q[j] = *reinterpret_cast<const u32x4*>(st + boff[j]);
+      for (int j = 0; j < 4; ++j) bq[j] = *reinterpret_cast<const u32x4*>(st + boff[j]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(st + aoff[mt]);
+        const u32x4 al = *reinterpret_cast<const u32x4*>(st + k2APlane + aoff[mt]);
+        const f32x4 sr =
+            *reinterpret_cast<const f32x4*>(st + 2 * k2APlane + k2BBytes + wave * 256 + 4 * (mt * 16 + kg * 4));
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          ah[mt][ks] = *reinterpret_cast<const u32x4*>(st + aoff[mt][ks]);
-          al[mt][ks] = *reinterpret_cast<const u32x4*>(st + k2Rows * kARow + aoff[mt][ks]);
+        for (int j = 0; j < 4; ++j) {
+          const i32x4 z = {0, 0, 0, 0};
+          const i32x4 ih = mfma_i8(ah, bq[j], z);
+          const i32x4 il = mfma_i8(al, bq[j], z);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][j][i] += sr[i] * static_cast<float>(ih[i] * 256 + il[i]);
         }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 b[2];
-        i8x16_to_operands<false>(q[j], b[0], b[1]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16_bf16(ah[mt][ks], b[ks], acc[mt][j]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16_bf16(al[mt][ks], b[ks], acc[mt][j]);
-        }
+        // one row tile at a time: keeps the int32 results of at most one
+        // tile row live (the scheduler would otherwise start every MFMA of
+        // the stage first and run out of registers)
+        __builtin_amdgcn_sched_barrier(0);
       }
-      slot = slot == kStages - 1 ? 0 : slot + 1;
     }
   };
   if (ntw > 3) run(std::integral_constant<int, 4>{});
@@ -428,6 +538,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_kernel(const Gemm2Args p) 
   else if (ntw > 1) run(std::integral_constant<int, 2>{});
   else if (ntw > 0) run(std::integral_constant<int, 1>{});
   else run(std::integral_constant<int, 0>{});
+  wait_vmcnt<0>();   // no copy into LDS outlives the workgroup
 
   float sc[4];
 #pragma unroll
@@ -450,23 +561,28 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_kernel(const Gemm2Args p) 
 
 }  // namespace
 
-hipError_t launch_gemm2_w8_big(const Gemm2Args& p, hipStream_t stream) {
+bool gemm1_w8_big_fits(const Gemm1Args& p) { return p.T * p.H * 2 < (int64_t{1} << 32); }
+
+hipError_t launch_gemm2_w8_big_q16(const Gemm2Args& p, const int8_t* qhi, const int8_t* qlo, const float* qscale,
+                                   hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.H / k2Cols), static_cast<unsigned>(p.cap / k2Rows));
-  hipLaunchKernelGGL(gemm2_big_kernel, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(gemm2_big_q16_kernel, grid, dim3(kThreads), 0, stream, p, qhi, qlo, qscale);
   return hipGetLastError();
 }
 
-bool gemm1_w8_big_fits(const Gemm1Args& p) {
-  return p.T * p.H * 2 < (int64_t{1} << 31) && 2 * p.I * p.ldw < (int64_t{1} << 31);
-}
-
-hipError_t launch_gemm1_w8_big(const Gemm1Args& p, hipStream_t stream) {
+hipError_t launch_gemm1_w8_big(const Gemm1Args& p, int8_t* qhi, int8_t* qlo, float* qscale, hipStream_t stream) {
   if (!gemm1_w8_big_fits(p)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.I / kOut), static_cast<unsigned>(p.cap / kRows));
-  if (p.f16)
-    hipLaunchKernelGGL((gemm1_big_kernel<true>), grid, dim3(k1Threads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm1_big_kernel<false>), grid, dim3(k1Threads), 0, stream, p);
+  const bool q16 = qhi != nullptr;
+#define G1(F, Q) hipLaunchKernelGGL((gemm1_big_kernel<F, Q>), grid, dim3(k1Threads), 0, stream, p, qhi, qlo, qscale)
+  if (p.f16) {
+    if (q16) G1(true, true);
+    else G1(true, false);
+  } else {
+    if (q16) G1(false, true);
+    else G1(false, false);
+  }
+#undef G1
   return hipGetLastError();
 }
 

@@ -76,10 +76,14 @@ hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, const int8_t* qhi, const
                             hipStream_t stream);
 // block_m == 256 GEMMs with both operands copied straight into a 3-stage LDS ring
 // (GEMM2 needs H to be a multiple of 256).
-// the 256-row GEMM1 addresses x and one expert's w13 with 32-bit offsets
+// the 256-row GEMM1 addresses x with 32-bit byte offsets (T * H * 2 < 2^32)
 bool gemm1_w8_big_fits(const Gemm1Args& p);
-hipError_t launch_gemm1_w8_big(const Gemm1Args& p, hipStream_t stream);
-hipError_t launch_gemm2_w8_big(const Gemm2Args& p, hipStream_t stream);
+// qhi == nullptr: bf16 planes into p.a; else the 16-bit fixed-point form
+// (hi, lo codes [cap, I], scales [cap, I/128]) that launch_gemm2_w8_big_q16 reads.
+hipError_t launch_gemm1_w8_big(const Gemm1Args& p, int8_t* qhi, int8_t* qlo, float* qscale, hipStream_t stream);
+// 256-row blocks, H a multiple of 256.
+hipError_t launch_gemm2_w8_big_q16(const Gemm2Args& p, const int8_t* qhi, const int8_t* qlo, const float* qscale,
+                                   hipStream_t stream);
 
 struct Gemm1W4Args {
   const void* x;
