@@ -171,7 +171,7 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * lo = rne(v - hi) (16 significant bits), cap = moe_align_capacity.  Padding
  * rows of a block that holds rows get v = 0; 16-row groups made only of
  * padding may be left unwritten (GEMM2 never reads them).
- * Exception: block_m = 256 with H a multiple of 256 and T*H*2 < 2^32
+ * Exception: block_m = 256 with H a multiple of 256 and (T+1)*H*2 < 2^32
  * (the prefill form): gemm1 writes the 16-bit fixed-point form described
  * under moe_w8a16_requant directly, starting at byte offset 0 of `a`, and
  * no planes.
@@ -191,9 +191,11 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * fixed-point form for block_m in [32, 64] and for the prefill form of
  * block_m = 256; the hi + lo planes otherwise, which for block_m = 16 GEMM2
  * rounds to the same fixed-point form itself).  The K range [0, I) is cut
- * into `splits` parts of whole 128-wide steps (1 <= splits <= I/128; equal
- * parts, so splits must divide I/128, when block_m > 64; 1 when block_m is
- * 256).  y is device fp32 [splits, T*k, H]; rows of dropped ids are not
+ * into `splits` parts of whole 128-wide steps (1 <= splits <= I/128; part z
+ * covers steps [z*(I/128)/splits, (z+1)*(I/128)/splits) in integer division;
+ * block_m > 64 needs equal parts, so splits must divide I/128, except for
+ * the prefill form of block_m = 256).  y is device fp32 [splits, T*k, H];
+ * rows of dropped ids are not
  * written.  moe_w8a16_splits gives the split count the forward uses.
  *
  * moe_combine_topk: out[t, h] = sum_j topk_w[t,j] * sum_s y[s, t*k+j, h]

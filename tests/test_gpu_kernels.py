@@ -266,3 +266,34 @@ def test_gemm1_intermediate(act, bm):
             ref = oracle.moe_expert_intermediate(xf[f // k][None], W13, I)[0]
             err = np.abs(a_g[r] - ref)
             assert np.all(err <= 2e-5 * np.abs(ref).max() + 1e-4 * np.abs(ref)), (blk, f, err.max())
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3])
+def test_gemm2_blocks_of_256_splits(splits):
+    # the stage calls at 256-row blocks (fixed-point intermediate, integer
+    # GEMM2) with K cut into 1, 2 or 3 parts of whole 128-wide groups (I/128 =
+    # 3, so two parts are uneven); the combined output against the oracle layer
+    E, k, H, I, T, bm = 4, 2, 512, 384, 300, 256
+    log(f"[gemm2 256 splits] splits={splits} E={E} H={H} I={I} T={T}")
+    W = small_w8(E, H, I, seed=21)
+    xb = synthetic.random_activations(T, H, "bf16", seed=22)
+    logits = synthetic.random_logits(T, E, seed=23)
+    tw, ti, w_ref, ids_ref = route_both(logits, k)
+    cap = pkg.moe_align_capacity(T, k, E, bm)
+    s = torch.empty(cap, dtype=torch.int32, device=DEV)
+    b = torch.empty(cap // bm, dtype=torch.int32, device=DEV)
+    n = torch.empty(1, dtype=torch.int32, device=DEV)
+    pkg.moe_align_block(ti, E, bm, s, b, n)
+    nbytes = pkg.moe_w8a16_intermediate_bytes(T, H, I, E, k, bm)
+    a = torch.zeros(((nbytes + 1) // 2,), dtype=torch.int16, device=DEV)
+    pkg.moe_w8a16_gemm1(to_dev_act(xb, "bf16"), W.w13, W.s13, s, b, n, bm, k, a)
+    y = torch.full((splits, T * k, H), float("nan"), dtype=torch.float32, device=DEV)
+    pkg.moe_w8a16_gemm2(a, T, k, W.w2, W.s2, s, b, n, bm, splits, y)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    pkg.moe_combine_topk(y, splits, tw, ti, E, out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any(), "every part writes every valid row"
+    got = out.float().cpu().numpy().astype(np.float64)
+    ok, detail = oracle.layer_within_tolerance(got, oracle.moe_forward_w8(
+        oracle.bf16_bits_to_f64(xb), W.q13, W.hs13, W.q2, W.hs2, w_ref, ids_ref))
+    assert ok, f"splits={splits}: {detail}"

@@ -255,6 +255,7 @@ def moe_w8a16_gemm2(a, T, k, w2, w2_scale, sorted_ids, block_expert, num_padded,
     E, H, I = w2.shape
     ld2 = _row_stride(w2, torch.int8, (E, H, I), "w2")
     _need_bytes(a, moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m), "a")
+    _need(y, torch.float32, (splits, T * k, H), "y")
     _check(lib().moe_w8a16_gemm2(_ptr(a), T, H, I, E, k, _ptr(w2), _ptr(w2_scale), ld2, _ptr(sorted_ids),
                                  _ptr(block_expert), _ptr(num_padded), block_m, splits, _ptr(y),
                                  _stream(stream)), "moe_w8a16_gemm2")

@@ -100,7 +100,7 @@ Q16 q16_at(const float* a, int64_t cap, int64_t I, size_t offset) {
 // kernels apply; otherwise as bf16 planes.  Decided from (T, H, block_m),
 // which every stage call knows, so GEMM1 and GEMM2 always agree.
 bool prefill_q16(int64_t T, int64_t H, int64_t bm) {
-  return use_prefill(bm) && H % 256 == 0 && T * H * 2 < (int64_t{1} << 32);
+  return use_prefill(bm) && H % 256 == 0 && (T + 1) * H * 2 < (int64_t{1} << 32);
 }
 
 bool use_stream(int64_t bm) { return bm <= 64; }
@@ -163,7 +163,26 @@ int gemm2_nt(int64_t T, int64_t E, int64_t k, int64_t bm) {
 int64_t gemm2_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, bool tiled = false) {
   const int64_t steps = I / 128;
   const int64_t blocks = blocks_estimate(T, E, k, bm);
-  if (!tiled && use_prefill(bm)) return 1;
+  if (!tiled && use_prefill(bm)) {
+    if (!prefill_q16(T, H, bm)) return 1;
+    // 128-row halves x 256 columns per workgroup, one workgroup per CU.  When
+    // they fill at most two rounds of 256 CUs, the split count (1, 2 or 4
+    // parts of whole 128-wide groups) with the shortest run in rounds, each
+    // extra part charged 5% for its partials' round trip through the combine
+    const int64_t wgs = 2 * blocks * (H / 256);
+    if (wgs > 512) return 1;
+    int64_t best = 1;
+    double best_t = 1e30;
+    for (int64_t sp = 1; sp <= 4 && sp <= steps; sp *= 2) {
+      const double t = std::ceil(static_cast<double>(wgs * sp) / 256.0) / static_cast<double>(sp) *
+                       (1.0 + 0.05 * static_cast<double>(sp - 1));
+      if (t < best_t) {
+        best_t = t;
+        best = sp;
+      }
+    }
+    return best;
+  }
   if (tiled || !gemm2_int8(bm)) {
     // tiled kernel: 128 columns x one split per workgroup, equal splits
     const int64_t ntiles = H / 128;
@@ -248,6 +267,8 @@ int check_layer_dims(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "H, I, E and k must be >= 1");
   if (k > E) return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) > E (%lld)", (long long)k, (long long)E);
   if (E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E > %lld", (long long)kMaxExperts);
+  if (H > (int64_t{1} << 24) || I > (int64_t{1} << 24))
+    return fail(MOE_ERR_UNSUPPORTED, "H and I above 2^24 are not supported");
   if (H % 128 != 0 || I % 128 != 0)
     return fail(MOE_ERR_INVALID_ARGUMENT, "H (%lld) and I (%lld) must be multiples of 128",
                 (long long)H, (long long)I);
@@ -417,10 +438,11 @@ int moe_w8a16_gemm2(const float* a, int64_t T, int64_t H, int64_t I, int64_t E, 
   if ((st = check_block_m(block_m)) != MOE_OK) return st;
   const int64_t ldw = w2_row_stride ? w2_row_stride : I;
   if (ldw < I || ldw % 16) return fail(MOE_ERR_INVALID_ARGUMENT, "w2_row_stride must be >= I and a multiple of 16");
-  if (splits < 1 || splits > I / 128 || (!gemm2_int8(block_m) && (I / 128) % splits != 0) ||
-      (use_prefill(block_m) && splits != 1))
+  if (splits < 1 || splits > I / 128 ||
+      (!gemm2_int8(block_m) && !prefill_q16(T, H, block_m) && (I / 128) % splits != 0))
     return fail(MOE_ERR_INVALID_ARGUMENT,
-                "splits must be in [1, I/128], divide I/128 when block_m > 64, and be 1 when block_m is 256");
+                "splits must be in [1, I/128] and divide I/128 when block_m > 64 (except for 256-row blocks "
+                "with H a multiple of 256)");
   if (T == 0) return ok();
   if (!a || !w2 || !w2_scale || !sorted_ids || !block_expert || !num_padded || !y)
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");

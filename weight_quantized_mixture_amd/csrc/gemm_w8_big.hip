@@ -88,12 +88,14 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
   ntw = ntw < 0 ? 0 : (ntw > 8 ? 8 : ntw);
   const int nst = static_cast<int>(H / kBK);
 
-  // copy sources, as 32-bit byte offsets into buffer resources: x (under
-  // 2^32 bytes, which the launcher checks) and the 128 gate or up rows of
-  // w13 this wave copies.  Rows that hold no token read token 0's row (never
-  // used): every lane issues every copy, so the per-thread copy count is
-  // fixed.
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, static_cast<uint32_t>(p.T * H * 2));
+  // copy sources, as 32-bit byte offsets into buffer resources: x (the
+  // launcher checks that its size plus one row stays under 2^32 bytes) and
+  // the 128 gate or up rows of w13 this wave copies.  Every lane issues every
+  // copy, so the per-thread copy count is fixed; rows that hold no token take
+  // the offset one past the end of x, which the buffer's range check turns
+  // into a zero fill that reads no memory (those rows' results are dropped).
+  const uint32_t xbytes = static_cast<uint32_t>(p.T * H * 2);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, xbytes);
   uint32_t aoffs[k1ADma];
 #pragma unroll
   for (int i = 0; i < k1ADma; ++i) {
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
     const int c = (lane & 7) ^ swz_a(r);
     const int f = r < nrows ? p.sorted_ids[row0 + r] : static_cast<int>(Tk);
     const uint32_t t = f < Tk ? static_cast<uint32_t>(f / static_cast<int>(p.k)) : 0u;
-    aoffs[i] = (t * static_cast<uint32_t>(H) + static_cast<uint32_t>(c * 8)) * 2u;
+    aoffs[i] = f < Tk ? (t * static_cast<uint32_t>(H) + static_cast<uint32_t>(c * 8)) * 2u : xbytes;
   }
   // a wave copies 64 weight rows of one half (gate for waves 0-1, up for
   // 2-3): row b + 16 i has the swizzle of row b, so one lane offset serves
@@ -394,15 +396,18 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
 
 // GEMM2 for 256-row blocks on the fixed-point form of a: y = a dequant(w2[e])^T,
 // scale on the accumulator.  A workgroup owns 128 rows (half an align block)
-// and 256 output columns; 8 waves (2 per SIMD) in a 2 x 4 grid, each 64 rows
-// x 64 columns (4 x 4 tiles of v_mfma_i32_16x16x64_i8, hi and lo codes of a
-// against the same w2 fragment).  Stages of 64 K through a 4-deep LDS ring
-// filled with global_load_lds: 8 KB of hi codes, 8 KB of lo codes, 16 KB of
-// w2 codes and each wave's 64 row scales of the stage's group.  The copies
-// of stage s+3 are requested after the barrier of stage s (past the end the
+// and 256 output columns of one K part (grid z: K cut into `splits` parts of
+// whole 128-wide scale groups, partials to y[z]); 8 waves (2 per SIMD) in a
+// 2 x 4 grid, each 64 rows x 64 columns (4 x 4 tiles of
+// v_mfma_i32_16x16x64_i8, hi and lo codes of a against the same w2
+// fragment).  Stages of 64 K through a 4-deep LDS ring filled with
+// global_load_lds: 8 KB of hi codes, 8 KB of lo codes, 16 KB of w2 codes and
+// each wave's 64 row scales of the stage's group.  The copies of stage s+3
+// are requested after the barrier of stage s (past the end of the part the
 // last stage's index repeats, into a slot nobody reads), so the copy count
-// per stage is fixed.  Per stage and tile the two int32 results are folded
-// into fp32 as s_row * (256 hi + lo) (exact in int32: |.| < 2^29).
+// per stage is fixed.  The two stages of one scale group accumulate in int32
+// (|.| < 2^22 per plane), and at the group's end each tile is folded into
+// fp32 as s_row * (256 hi + lo) (exact in int32: |.| < 2^30).
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int k2Rows = 128;
@@ -413,6 +418,7 @@ constexpr int k2BBytes = k2Cols * kBK;                // 16 KB
 constexpr int k2SBytes = kWaves * 256;                // 64 scales per wave
 constexpr int k2StageBytes = 2 * k2APlane + k2BBytes + k2SBytes;
 constexpr int k2ADma = 2 * k2APlane / (kThreads * 16);
+static_assert((k2APlane / 16) % (k2ADma * kWave) == 0, "each wave copies codes of one plane");
 constexpr int k2BDma = k2BBytes / (kThreads * 16);
 constexpr int k2Dma = k2ADma + k2BDma + 1;
 
@@ -433,6 +439,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
   const int col = lane & 15;
   const int kg = lane >> 4;
 
+  const int z = static_cast<int>(blockIdx.z);
   const int64_t row0 = static_cast<int64_t>(blockIdx.y) * k2Rows;
   if (row0 >= *p.num_padded) return;
   const int e = p.block_expert[row0 / kRows];
@@ -444,18 +451,26 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
   if (nrows == 0) return;      // the second half of a block may be empty (uniform exit)
   int ntw = (nrows - wm * 64) / 16;
   ntw = ntw < 0 ? 0 : (ntw > 4 ? 4 : ntw);
-  const int nst = static_cast<int>(I / kBK);
+  // this part's stages: whole scale groups [g0, g1), two 64-K stages each
+  const int s0 = static_cast<int>(2 * (z * G / p.splits));
+  const int s1 = static_cast<int>(2 * ((z + 1) * G / p.splits));
 
   // copies: code chunk g = (plane, row, 16-byte position) of the stage's
   // hi/lo codes (LDS position g holds source chunk (g%4) ^ swz_b(row)), w2
-  // rows b, and this wave's 64 row scales
-  const int8_t* asrc[k2ADma];
+  // rows b, and this wave's 64 row scales.  The codes go through buffer
+  // resources over this half's rows that hold tokens (nrows * I < 2^31 bytes,
+  // as I <= 2^24): the copies of the rows past them fall outside the range,
+  // read no memory and fill zeros (those rows' results are dropped), while
+  // every lane still issues every copy.  Waves 0-3 copy hi codes, 4-7 lo.
+  const __amdgpu_buffer_rsrc_t ar =
+      make_rsrc((wave * k2ADma < 8 ? qhi : qlo) + row0 * I, static_cast<uint32_t>(nrows * I));
+  uint32_t aoffv[k2ADma];
 #pragma unroll
   for (int i = 0; i < k2ADma; ++i) {
     const int g = (wave * k2ADma + i) * kWave + lane;
-    const int pl = g / (k2Rows * 4), r = (g % (k2Rows * 4)) / 4;
+    const int r = (g % (k2Rows * 4)) / 4;
     const int c = (g & 3) ^ swz_b(r);
-    asrc[i] = (pl == 0 ? qhi : qlo) + (row0 + r) * I + c * 16;
+    aoffv[i] = static_cast<uint32_t>(r * I + c * 16);
   }
   const int64_t hb = static_cast<int64_t>(blockIdx.x) * k2Cols;
   const int8_t* bsrc[k2BDma];
@@ -470,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
     uint8_t* base = smem + slot * k2StageBytes;
 #pragma unroll
     for (int i = 0; i < k2ADma; ++i)
-      dma16(asrc[i] + static_cast<int64_t>(s) * kBK, base + (wave * k2ADma + i) * 1024);
+      dma16_buf(ar, aoffv[i], static_cast<uint32_t>(s * kBK), base + (wave * k2ADma + i) * 1024);
 #pragma unroll
     for (int i = 0; i < k2BDma; ++i)
       dma16(bsrc[i] + static_cast<int64_t>(s) * kBK, base + 2 * k2APlane + (wave * k2BDma + i) * 1024);
@@ -499,16 +514,20 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
 
   auto run = [&](auto tiles) __attribute__((always_inline)) {
     constexpr int MT = decltype(tiles)::value;
+    i32x4 ih[MT > 0 ? MT : 1][4], il[MT > 0 ? MT : 1][4];
 #pragma unroll
-    for (int q = 0; q < k2Ring - 1; ++q) issue(q < nst ? q : nst - 1, q);
-    for (int s = 0; s < nst; ++s) {
+    for (int q = 0; q < k2Ring - 1; ++q) issue(s0 + q < s1 ? s0 + q : s1 - 1, q);
+    // one stage: LAST = the second stage of its scale group (accumulate onto
+    // the first's int32 results, then fold)
+    auto stage = [&](int s, auto last_tag) __attribute__((always_inline)) {
+      constexpr bool LAST = decltype(last_tag)::value;
       // this thread's copies of stage s landed (those of s+1, s+2 may still
       // fly) and its LDS reads of stage s-1 done; then the slot of s-1 takes
       // stage s+3
       wait_vmcnt_lgkm0<2 * k2Dma>();
       stage_barrier();
-      issue(s + 3 < nst ? s + 3 : nst - 1, (s + 3) % k2Ring);
-      const uint8_t* st = smem + (s % k2Ring) * k2StageBytes;
+      issue(s + 3 < s1 ? s + 3 : s1 - 1, (s - s0 + 3) % k2Ring);
+      const uint8_t* st = smem + ((s - s0) % k2Ring) * k2StageBytes;
       u32x4 bq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bq[j] = *reinterpret_cast<const u32x4*>(st + boff[j]);
@@ -516,21 +535,30 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4 ah = *reinterpret_cast<const u32x4*>(st + aoff[mt]);
         const u32x4 al = *reinterpret_cast<const u32x4*>(st + k2APlane + aoff[mt]);
-        const f32x4 sr =
-            *reinterpret_cast<const f32x4*>(st + 2 * k2APlane + k2BBytes + wave * 256 + 4 * (mt * 16 + kg * 4));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const i32x4 z = {0, 0, 0, 0};
-          const i32x4 ih = mfma_i8(ah, bq[j], z);
-          const i32x4 il = mfma_i8(al, bq[j], z);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][j][i] += sr[i] * static_cast<float>(ih[i] * 256 + il[i]);
+          const i32x4 z0 = {0, 0, 0, 0};
+          ih[mt][j] = mfma_i8(ah, bq[j], LAST ? ih[mt][j] : z0);
+          il[mt][j] = mfma_i8(al, bq[j], LAST ? il[mt][j] : z0);
         }
-        // one row tile at a time: keeps the int32 results of at most one
-        // tile row live (the scheduler would otherwise start every MFMA of
-        // the stage first and run out of registers)
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LAST) {
+          const f32x4 sr =
+              *reinterpret_cast<const f32x4*>(st + 2 * k2APlane + k2BBytes + wave * 256 + 4 * (mt * 16 + kg * 4));
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[mt][j][i] += sr[i] * static_cast<float>(ih[mt][j][i] * 256 + il[mt][j][i]);
+          // one row tile at a time: keeps the folds of one tile row next to
+          // its MFMAs (the scheduler would otherwise start every MFMA of the
+          // stage first and run out of registers)
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+    };
+    for (int s = s0; s < s1; s += 2) {
+      stage(s, std::false_type{});
+      stage(s + 1, std::true_type{});
     }
   };
   if (ntw > 3) run(std::integral_constant<int, 4>{});
@@ -550,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
       for (int i = 0; i < 4; ++i) {
         const int f = p.sorted_ids[row0 + wm * 64 + mt * 16 + kg * 4 + i];
         if (f < Tk) {
-          float* yr = p.y + static_cast<int64_t>(f) * H + hb + wn * 64 + col;
+          float* yr = p.y + (static_cast<int64_t>(z) * Tk + f) * H + hb + wn * 64 + col;
 #pragma unroll
           for (int j = 0; j < 4; ++j) yr[16 * j] = acc[mt][j][i] * sc[j];
         }
@@ -561,11 +589,12 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
 
 }  // namespace
 
-bool gemm1_w8_big_fits(const Gemm1Args& p) { return p.T * p.H * 2 < (int64_t{1} << 32); }
+bool gemm1_w8_big_fits(const Gemm1Args& p) { return (p.T + 1) * p.H * 2 < (int64_t{1} << 32); }
 
 hipError_t launch_gemm2_w8_big_q16(const Gemm2Args& p, const int8_t* qhi, const int8_t* qlo, const float* qscale,
                                    hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(p.H / k2Cols), static_cast<unsigned>(p.cap / k2Rows));
+  const dim3 grid(static_cast<unsigned>(p.H / k2Cols), static_cast<unsigned>(p.cap / k2Rows),
+                  static_cast<unsigned>(p.splits));
   hipLaunchKernelGGL(gemm2_big_q16_kernel, grid, dim3(kThreads), 0, stream, p, qhi, qlo, qscale);
   return hipGetLastError();
 }

@@ -76,7 +76,7 @@ hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, const int8_t* qhi, const
                             hipStream_t stream);
 // block_m == 256 GEMMs with both operands copied straight into a 3-stage LDS ring
 // (GEMM2 needs H to be a multiple of 256).
-// the 256-row GEMM1 addresses x with 32-bit byte offsets (T * H * 2 < 2^32)
+// the 256-row GEMM1 addresses x with 32-bit byte offsets ((T + 1) * H * 2 < 2^32)
 bool gemm1_w8_big_fits(const Gemm1Args& p);
 // qhi == nullptr: bf16 planes into p.a; else the 16-bit fixed-point form
 // (hi, lo codes [cap, I], scales [cap, I/128]) that launch_gemm2_w8_big_q16 reads.
