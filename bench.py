@@ -71,12 +71,22 @@ def parse():
 HEADLINE_T = {"tiny": 16, "mixtral_decode": 64, "mixtral_prefill": 4096, "fine_grained": 512, "w4a16": 256}
 
 
-def sources_sha() -> str:
-    """Hash of the HIP sources: a traffic summary is valid only for the kernels it was taken on."""
+# source file of each GEMM1 kernel whose traffic the bench reports
+KERNEL_SOURCE = {"gemm1_big_kernel": "gemm_w8_big.hip", "gemm1_dma_kernel": "gemm_w8_dma.hip",
+                 "gemm1_lds_kernel": "gemm_w8_lds.hip", "gemm1_stream_kernel": "gemm_w8_stream.hip",
+                 "gemm1_w8_kernel": "gemm_w8.hip"}
+
+
+def sources_sha(kernel_prefix=None) -> str:
+    """Hash of the HIP sources a kernel is built from (its .hip file and the shared headers; every
+    source without a kernel): a traffic summary is valid only for the kernels it was taken on."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))):
+    hips = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    if kernel_prefix in KERNEL_SOURCE:
+        hips = [os.path.join(CSRC, KERNEL_SOURCE[kernel_prefix])]
+    for f in hips + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))):
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
@@ -115,7 +125,8 @@ def summarize_pmc(args):
     for (name, c), xs in write.items():
         if c == "WRITE_SIZE" and "moe::" in name:
             kernels.setdefault(name, {})["write_kib"] = sum(xs) / len(xs)
-    res = {"sources_sha": sources_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
+    res = {"sources_sha": sources_sha(), "kernel_sources_sha": {k: sources_sha(k) for k in KERNEL_SOURCE},
+           "fetch_scale": f_scale, "write_scale": w_scale,
            "command": args.pmc_command, "workload": args.workload,
            "T": args.tokens or HEADLINE_T[args.workload], "kernels": {}}
     lines = [f"# HBM traffic per launch: {args.workload}, T={res['T']}", "",
@@ -129,7 +140,8 @@ def summarize_pmc(args):
         short = name.replace("moe::(anonymous namespace)::", "").replace("void ", "").split("(moe::")[0][:90]
         res["kernels"][short] = {"fetch_kib": fk, "write_kib": wk, "traffic_bytes": mb * 1e6}
         lines.append(f"| `{short}` | {fk:.0f} | {wk:.0f} | {mb:.1f} |")
-    lines += ["", f"Kernel sources sha256[:16]: `{res['sources_sha']}`"]
+    lines += ["", f"Kernel sources sha256[:16]: `{res['sources_sha']}` (all); per GEMM1 kernel: " +
+              ", ".join(f"`{k}` `{v}`" for k, v in res["kernel_sources_sha"].items())]
     stem = f"traffic_{args.workload}_T{res['T']}"
     os.makedirs(PROFILES, exist_ok=True)
     json.dump(res, open(os.path.join(PROFILES, stem + ".json"), "w"), indent=1)
@@ -194,7 +206,7 @@ def recorded_traffic(workload, T, kernel_prefix):
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("sources_sha") != sources_sha():
+    if d.get("kernel_sources_sha", {}).get(kernel_prefix) != sources_sha(kernel_prefix):
         return None
     for name, v in d["kernels"].items():
         if name.startswith(kernel_prefix):

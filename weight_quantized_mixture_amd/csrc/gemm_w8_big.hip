@@ -189,9 +189,10 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
     auto jlo = [](int m) { return m * 8 / MT1; };
     // scheduling of one slot (8 MFMAs, nconv conversions of 12 VALU each, a
     // few LDS reads): MFMA and VALU alternate so that the conversions and
-    // address arithmetic issue while the matrix core works
+    // address arithmetic issue while the matrix core works (for 8 row tiles,
+    // 2 VALU per MFMA: measured faster than 1 or 3)
     auto interleave = []() {
-      constexpr int per = (12 * ((8 + MT1 - 1) / MT1) + 7) / 8 + 1;
+      constexpr int per = (12 * ((8 + MT1 - 1) / MT1) + 7) / 8;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
@@ -531,6 +532,15 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
       u32x4 bq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bq[j] = *reinterpret_cast<const u32x4*>(st + boff[j]);
+      // fold of row tile m: fp32 += s_row * (256 hi + lo)
+      auto fold = [&](int m) __attribute__((always_inline)) {
+        const f32x4 sr =
+            *reinterpret_cast<const f32x4*>(st + 2 * k2APlane + k2BBytes + wave * 256 + 4 * (m * 16 + kg * 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][j][i] += sr[i] * static_cast<float>(ih[m][j][i] * 256 + il[m][j][i]);
+      };
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4 ah = *reinterpret_cast<const u32x4*>(st + aoff[mt]);
@@ -542,19 +552,14 @@ __global__ __launch_bounds__(kThreads) void gemm2_big_q16_kernel(const Gemm2Args
           il[mt][j] = mfma_i8(al, bq[j], LAST ? il[mt][j] : z0);
         }
         if constexpr (LAST) {
-          const f32x4 sr =
-              *reinterpret_cast<const f32x4*>(st + 2 * k2APlane + k2BBytes + wave * 256 + 4 * (mt * 16 + kg * 4));
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[mt][j][i] += sr[i] * static_cast<float>(ih[mt][j][i] * 256 + il[mt][j][i]);
-          // one row tile at a time: keeps the folds of one tile row next to
-          // its MFMAs (the scheduler would otherwise start every MFMA of the
-          // stage first and run out of registers)
+          // the previous row tile's fold runs under this tile's MFMAs (its
+          // own results are not ready yet); one tile row at a time keeps the
+          // scheduler from hoisting every MFMA of the stage first
+          if (mt > 0) fold(mt - 1);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if constexpr (LAST && MT > 0) fold(MT - 1);
     };
     for (int s = s0; s < s1; s += 2) {
       stage(s, std::false_type{});
