@@ -78,3 +78,22 @@ def test_w4_apply_from_logits():
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy().astype(np.float64), got)
     assert_layer_close(got, ref, "w4 apply from logits")
+
+
+@pytest.mark.parametrize("act,bm,T,H,I,g", [("fp16", 32, 45, 256, 384, 128), ("bf16", 32, 45, 256, 384, 128),
+                                            ("bf16", 16, 7, 384, 256, 128), ("fp16", 16, 30, 384, 384, 128),
+                                            ("fp16", 32, 61, 512, 512, 256), ("bf16", 16, 1, 512, 512, 256)])
+def test_w4_blocks_of_16_and_32(act, bm, T, H, I, g):
+    # GEMM1 of 16/32-row blocks streams packed rows, scales and zero words
+    # through the LDS ring: odd group counts per row (H / g = 3) make the
+    # parity of each row's scale element differ, and g = 256 spans two K steps
+    E, k = 8, 3
+    log(f"[w4 dma] act={act} bm={bm} T={T} H={H} I={I} g={g}")
+    fn = lambda which, e: synthetic.random_master((2 * I, H) if which == "w13" else (H, I),  # noqa: E731
+                                                  300 + e, tag=74 if which == "w13" else 75)
+    W = W4Weights(E, H, I, g, fn)
+    assert W.mismatch == 0
+    xb = synthetic.random_activations(T, H, act, seed=T + 11)
+    logits = synthetic.random_logits(T, E, seed=T + 12)
+    got, ref = _run(W, xb, act, logits, k, bm)
+    assert_layer_close(got, ref, f"w4 dma {act} bm={bm} T={T} H={H} I={I} g={g}")

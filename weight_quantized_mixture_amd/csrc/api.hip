@@ -631,9 +631,11 @@ int forward_w4(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, in
   p1.qw = w13_qweight; p1.sc = w13_scales; p1.qz = w13_qzeros; p1.group = static_cast<int>(group_size);
   p1.sorted_ids = sorted; p1.block_expert = blocks; p1.num_padded = npad;
   p1.block_m = static_cast<int>(block_m); p1.cap = L.cap; p1.a = a;
-  if ((e = w4_stream(block_m) ? moe::launch_gemm1_w4_stream(p1, stream) : moe::launch_gemm1_w4(p1, stream)) !=
-      hipSuccess)
-    return hip_status(e, "gemm1_w4");
+  // blocks of 16 or 32 rows: the DMA-fed ring (it copies the fp16 scales as dwords)
+  const bool w4_dma = (block_m == 16 || block_m == 32) && aligned(w13_scales, 4);
+  e = w4_dma ? moe::launch_gemm1_w4_dma(p1, stream)
+             : (w4_stream(block_m) ? moe::launch_gemm1_w4_stream(p1, stream) : moe::launch_gemm1_w4(p1, stream));
+  if (e != hipSuccess) return hip_status(e, "gemm1_w4");
   moe::Gemm2W4Args p2{};
   p2.a = a; p2.f16 = act_dtype == MOE_FP16; p2.H = H; p2.I = I; p2.Tk = T * k;
   p2.qw = w2_qweight; p2.sc = w2_scales; p2.qz = w2_qzeros; p2.group = static_cast<int>(group_size);

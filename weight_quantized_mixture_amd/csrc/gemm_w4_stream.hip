@@ -25,6 +25,8 @@
 // fp16 range, like the activations), GEMM2 permutes them on the same copy.
 // bf16 activations: codes go through fp32 into bf16 (natural order) and the
 // planes are bf16.
+#include <type_traits>
+
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
@@ -323,6 +325,195 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
   }
 }
 
+// GEMM1 for blocks of 16 or 32 rows fed by direct global -> LDS copies (the
+// ring of the int8 decode GEMM1, with packed uint4 rows).  A workgroup is one
+// align block and 64 output columns; each wave owns 16 gate rows and the
+// matching 16 up rows.  Per 128-K step (one scale group or part of one) every
+// wave copies its 32 packed rows (64 bytes each, 2 KB) and one dword per
+// lane: lanes 0-31 the dword holding their row's fp16 group scale, lanes
+// 32-35 the zero words of the wave's rows (gate n0, n0+8, up I+n0, I+n0+8),
+// the other lanes repeat lane 32's; the workgroup copies the block's
+// activation rows (256 bytes each; rows without a token read token 0's row
+// and their results are replaced by 0).  A 4-deep ring keeps steps s+1..s+3
+// in flight while step s is decoded and multiplied; one barrier per step,
+// after each thread has waited for its own copies of that step.  Lane
+// (col, kg) takes K [32 kg, 32 kg + 32) of its gate and up rows, 8 codes per
+// MFMA, the activation operand read for the same K positions (permuted to
+// the fp16 decode's slot order 0,4,1,5,2,6,3,7 after the LDS read).
+constexpr int kW4Ring = 4;
+constexpr int kW4WWave = 32 * (kStep / 2);             // 2 KB of packed codes per wave and step
+constexpr int kW4WStage = 4 * kW4WWave;
+constexpr int kW4SZWave = kWave * 4;                   // one dword per lane
+constexpr int kW4SZStage = 4 * kW4SZWave;
+constexpr int kW4WDma = kW4WWave / (kWave * 16);       // 2 copies per lane and step
+
+template <int MT, bool F16>
+__global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Args p) {
+  constexpr int kARow = kStep * 2;                     // bytes per activation row and step
+  constexpr int kAStage = 16 * MT * kARow;
+  constexpr int kADma = kAStage / (kThreads * 16);     // = MT
+  constexpr int kStage = kW4WStage + kW4SZStage + kAStage;
+  constexpr int kPer = kW4WDma + 1 + kADma;            // copies per thread and step
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kW4Ring * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
+  if (row0 >= *p.num_padded) return;
+  const int64_t e = p.block_expert[blockIdx.y];
+  const int64_t Tk = p.Tk, H = p.H, I = p.I, N = 2 * I, G = H / p.group;
+  int ntiles = 0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    if (p.sorted_ids[row0 + mt * 16] < Tk) ntiles = mt + 1;
+  const int nst = static_cast<int>(H / kStep);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16;
+  auto wrow = [&](int r) -> int64_t { return r < 16 ? n0 + r : I + n0 + (r - 16); };
+
+  // packed-code copies: row r = 16 i + lane/4 of the wave's 32, LDS chunk
+  // lane%4 holds source chunk (lane%4) ^ swz_b(r)
+  const uint8_t* qwb = reinterpret_cast<const uint8_t*>(p.qw);
+  const uint8_t* wsrc[kW4WDma];
+#pragma unroll
+  for (int i = 0; i < kW4WDma; ++i) {
+    const int r = 16 * i + (lane >> 2);
+    const int c = (lane & 3) ^ swz_b(r);
+    wsrc[i] = qwb + (e * N + wrow(r)) * (H / 2) + c * 16;
+  }
+  // scale / zero dword of this lane: element (row, group) of the fp16 scales
+  // is at srow + group; zero word (rows/8, group) at zrow + group
+  const uint8_t* scb = reinterpret_cast<const uint8_t*>(p.sc);
+  const int64_t srow = (e * N + wrow(lane < 32 ? lane : 0)) * G;
+  const int zl = lane >= 32 && lane < 36 ? lane - 32 : 0;
+  const int64_t zn = zl < 2 ? n0 + 8 * zl : I + n0 + 8 * (zl - 2);
+  const int32_t* zsrc = p.qz + (e * (N / 8) + zn / 8) * G;
+  // activation copies: row r = 4 (wave MT + q) + lane/16, slot lane%16 holds
+  // chunk (lane%16) ^ swz_c(r)
+  const uint16_t* x = static_cast<const uint16_t*>(p.x);
+  const uint16_t* asrc[kADma];
+#pragma unroll
+  for (int q = 0; q < kADma; ++q) {
+    const int r = 4 * (wave * kADma + q) + (lane >> 4);
+    const int c = (lane & 15) ^ swz_c(r);
+    const int f = p.sorted_ids[row0 + r];
+    const int64_t t = f < Tk ? f / static_cast<int>(p.k) : 0;
+    asrc[q] = x + t * H + c * 8;
+  }
+  auto issue = [&](int s, int slot) {
+    uint8_t* base = smem + slot * kStage;
+#pragma unroll
+    for (int i = 0; i < kW4WDma; ++i)
+      dma16(wsrc[i] + static_cast<int64_t>(s) * (kStep / 2), base + wave * kW4WWave + i * 1024);
+    const int64_t grp = static_cast<int64_t>(s) * kStep / p.group;
+    const void* szp = lane < 32 ? static_cast<const void*>(scb + ((srow + grp) & ~int64_t{1}) * 2)
+                                : static_cast<const void*>(zsrc + grp);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)const_cast<void*>(szp),
+                                     (lds_ptr_t)(base + kW4WStage + wave * kW4SZWave), 4, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kADma; ++q)
+      dma16(asrc[q] + static_cast<int64_t>(s) * kStep, base + kW4WStage + kW4SZStage + (wave * kADma + q) * 1024);
+  };
+
+  // LDS offsets this lane reads
+  const int wog = wave * kW4WWave + col * (kStep / 2) + 16 * (kg ^ swz_b(col));
+  const int wou = wave * kW4WWave + (16 + col) * (kStep / 2) + 16 * (kg ^ swz_b(16 + col));
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aoff[i] = kW4WStage + kW4SZStage + col * kARow + 16 * ((4 * kg + i) ^ swz_c(col));
+  // parity of the scale element of group 0 for the gate and up row (the
+  // copied dword holds the even element and the next one)
+  const int pg0 = static_cast<int>(((e * N + n0 + col) * G) & 1);
+  const int pu0 = static_cast<int>(((e * N + I + n0 + col) * G) & 1);
+
+  f32x4 accg[MT], accu[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    accg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accu[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto run = [&](auto tiles) {
+    constexpr int NT = decltype(tiles)::value;
+#pragma unroll
+    for (int q = 0; q < kW4Ring - 1; ++q) issue(q < nst ? q : nst - 1, q);
+    for (int s = 0; s < nst; ++s) {
+      // this thread's copies of step s landed (s+1, s+2 may still fly); then
+      // the slot of step s-1 takes step s+3 (past the end the last step
+      // again, into a slot nobody reads: a fixed copy count per step)
+      wait_vmcnt<(kW4Ring - 2) * kPer>();
+      stage_barrier();
+      issue(s + 3 < nst ? s + 3 : nst - 1, (s + 3) % kW4Ring);
+      const uint8_t* st = smem + (s % kW4Ring) * kStage;
+      const u32x4 wg = *reinterpret_cast<const u32x4*>(st + wog);
+      const u32x4 wu = *reinterpret_cast<const u32x4*>(st + wou);
+      const uint32_t* sz = reinterpret_cast<const uint32_t*>(st + kW4WStage + wave * kW4SZWave);
+      const int grp = static_cast<int>(static_cast<int64_t>(s) * kStep / p.group);
+      const uint32_t sgw = sz[col], suw = sz[16 + col];
+      const float sg = f16_to_f32(static_cast<uint16_t>(((pg0 ^ grp) & 1) ? sgw >> 16 : sgw & 0xffffu));
+      const float su = f16_to_f32(static_cast<uint16_t>(((pu0 ^ grp) & 1) ? suw >> 16 : suw & 0xffffu));
+      const uint32_t zg = (sz[32 + (col >> 3)] >> (4 * (col & 7))) & 0xFu;
+      const uint32_t zu = (sz[34 + (col >> 3)] >> (4 * (col & 7))) & 0xFu;
+      u32x4 bg[4], bu[4];
+      bg[0] = w4_op<F16>(wg.x, zg);
+      bg[1] = w4_op<F16>(wg.y, zg);
+      bg[2] = w4_op<F16>(wg.z, zg);
+      bg[3] = w4_op<F16>(wg.w, zg);
+      bu[0] = w4_op<F16>(wu.x, zu);
+      bu[1] = w4_op<F16>(wu.y, zu);
+      bu[2] = w4_op<F16>(wu.z, zu);
+      bu[3] = w4_op<F16>(wu.w, zu);
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        f32x4 pgs = {0.f, 0.f, 0.f, 0.f}, pus = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4 av = *reinterpret_cast<const u32x4*>(st + aoff[i] + mt * 16 * kARow);
+          if constexpr (F16) av = perm0415(av);
+          pgs = mfma16<F16>(av, bg[i], pgs);
+          pus = mfma16<F16>(av, bu[i], pus);
+        }
+        accg[mt] += pgs * sg;
+        accu[mt] += pus * su;
+      }
+    }
+  };
+  if constexpr (MT == 2) {
+    if (ntiles > 1) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 1>{});
+  }
+  wait_vmcnt<0>();   // no copy into LDS outlives the workgroup
+
+  uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.a);
+  uint16_t* a_lo = a_hi + p.cap * I;
+  const int64_t n = n0 + col;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt < ntiles) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = row0 + mt * 16 + kg * 4 + i;
+        uint16_t hi, lo;
+        split16(p.sorted_ids[r] < Tk ? silu_mul(accg[mt][i], accu[mt][i]) : 0.0f, F16, hi, lo);
+        a_hi[r * I + n] = hi;
+        a_lo[r * I + n] = lo;
+      }
+    }
+  }
+}
+
+template <int MT, bool F16>
+hipError_t w4d_launch1(const Gemm1W4Args& p, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm1_w4_dma_kernel<MT, F16>),
+                     dim3(static_cast<unsigned>(p.I / 64), static_cast<unsigned>(p.cap / p.block_m)),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int MT, bool F16>
 hipError_t w4s_launch1(const Gemm1W4Args& p, hipStream_t stream) {
   const Gemm2W4Args none{};
@@ -354,6 +545,11 @@ hipError_t launch_gemm1_w4_stream(const Gemm1W4Args& p, hipStream_t stream) {
   if (mt == 4) return w4s_launch1<4, false>(p, stream);
   if (mt == 2) return w4s_launch1<2, false>(p, stream);
   return w4s_launch1<1, false>(p, stream);
+}
+
+hipError_t launch_gemm1_w4_dma(const Gemm1W4Args& p, hipStream_t stream) {
+  if (p.block_m == 32) return p.f16 ? w4d_launch1<2, true>(p, stream) : w4d_launch1<2, false>(p, stream);
+  return p.f16 ? w4d_launch1<1, true>(p, stream) : w4d_launch1<1, false>(p, stream);
 }
 
 hipError_t launch_gemm2_w4_stream(const Gemm2W4Args& p, hipStream_t stream) {

@@ -121,6 +121,9 @@ struct Gemm2W4Args {
 hipError_t launch_gemm2_w4(const Gemm2W4Args& p, hipStream_t stream);
 // Weight-streaming uint4 variants for blocks of 16, 32 or 64 rows (intermediate as 16-bit hi/lo planes).
 hipError_t launch_gemm1_w4_stream(const Gemm1W4Args& p, hipStream_t stream);
+// uint4 GEMM1 for blocks of 16 or 32 rows on a 4-step ring of direct global -> LDS copies
+// (needs the fp16 scales 4-byte aligned).
+hipError_t launch_gemm1_w4_dma(const Gemm1W4Args& p, hipStream_t stream);
 hipError_t launch_gemm2_w4_stream(const Gemm2W4Args& p, hipStream_t stream);
 
 // Weighted top-k combine of the split partials.
