@@ -78,15 +78,17 @@ KERNEL_SOURCE = {"gemm1_big_kernel": "gemm_w8_big.hip", "gemm1_dma_kernel": "gem
 
 
 def sources_sha(kernel_prefix=None) -> str:
-    """Hash of the HIP sources a kernel is built from (its .hip file and the shared headers; every
-    source without a kernel): a traffic summary is valid only for the kernels it was taken on."""
+    """Hash of the HIP sources a kernel is built from (its .hip file and the headers with device
+    code; launch.hpp only declares host launchers; every source without a kernel): a traffic
+    summary is valid only for the kernels it was taken on."""
     import glob
     import hashlib
     h = hashlib.sha256()
     hips = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if kernel_prefix in KERNEL_SOURCE:
         hips = [os.path.join(CSRC, KERNEL_SOURCE[kernel_prefix])]
-    for f in hips + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))):
+    headers = [f for f in sorted(glob.glob(os.path.join(CSRC, "*.hpp"))) if os.path.basename(f) != "launch.hpp"]
+    for f in hips + headers:
         h.update(os.path.basename(f).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
