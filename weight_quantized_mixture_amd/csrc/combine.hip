@@ -31,7 +31,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (e < 0 || e >= E) continue;
     const float wj = topk_w[f];
     float4 ys = *reinterpret_cast<const float4*>(y + f * H + h);
-    for (int s = 1; s < splits; ++s) {
+    // partials 8 at a time: their loads are in flight together, the sums
+    // still run in ascending s
+    int s = 1;
+    for (; s + 7 < splits; s += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(y + ((s + u) * Tk + f) * H + h);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ys.x += v[u].x; ys.y += v[u].y; ys.z += v[u].z; ys.w += v[u].w;
+      }
+    }
+    for (; s < splits; ++s) {
       const float4 v = *reinterpret_cast<const float4*>(y + (s * Tk + f) * H + h);
       ys.x += v.x; ys.y += v.y; ys.z += v.z; ys.w += v.w;
     }
