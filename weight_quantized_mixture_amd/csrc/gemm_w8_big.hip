@@ -167,17 +167,21 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
     // h; rw[j][h] = the 8 int8 weight codes of column tile j for K half h;
     // cw[h][j] = those codes as a 16-bit MFMA operand.  Half 0 of a stage
     // multiplies with cw[0] while converting the stage's half-1 codes into
-    // cw[1]; half 1 multiplies with cw[1] while converting the next stage's
-    // half-0 codes into cw[0].  Every register a half has finished with is
-    // refilled from the next stage's LDS slot right away.
+    // cw[1] and reading both halves of the next stage's codes (one 16-byte
+    // read per tile: conflict-free under the row swizzle, where two 8-byte
+    // reads collide in pairs); half 1 multiplies with cw[1] while converting
+    // the next stage's half-0 codes into cw[0].  Every register a half has
+    // finished with is refilled from the next stage's LDS slot right away.
     u32x4 af[MT > 0 ? MT : 1][2];
     u32x2 rw[8][2];
     u32x4 cw[2][8];
     auto read_a = [&](const uint8_t* st, int mt, int h) {
       af[mt][h] = *reinterpret_cast<const u32x4*>(st + mt / 4 * 64 * kARow + aoff[mt & 3][h]);
     };
-    auto read_w = [&](const uint8_t* st, int j, int h) {
-      rw[j][h] = *reinterpret_cast<const u32x2*>(st + boff0 + (j & 3) * 16 * kBRow + (j >> 2) * kOut * kBRow + 8 * h);
+    auto read_w = [&](const uint8_t* st, int j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + boff0 + (j & 3) * 16 * kBRow + (j >> 2) * kOut * kBRow);
+      rw[j][0] = u32x2{v.x, v.y};
+      rw[j][1] = u32x2{v.z, v.w};
     };
     auto conv = [&](int j, int h) {
       const u32x2 p0 = F16 ? i8x4_to_f16x4(rw[j][h].x) : i8x4_to_bf16x4(rw[j][h].x);
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
 #pragma unroll
           for (int j = jlo(mt); j < jlo(mt + 1); ++j) {
             conv(j, 1);
-            if constexpr (MORE) read_w(nx, j, 0);
+            if constexpr (MORE) read_w(nx, j);
           }
           interleave();
         }
@@ -253,7 +257,6 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
 #pragma unroll
             for (int j = jlo(mt); j < jlo(mt + 1); ++j) {
               conv(j, 0);
-              read_w(nx, j, 1);
             }
             interleave();
           }
@@ -277,8 +280,7 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        read_w(smem, j, 0);
-        read_w(smem, j, 1);
+        read_w(smem, j);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) conv(j, 0);
