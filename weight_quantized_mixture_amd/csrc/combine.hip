@@ -12,7 +12,12 @@ namespace moe {
 
 namespace {
 
-template <bool F16>
+// BATCH: the split partials of a row are loaded 8 at a time so that their
+// loads are in flight together (the sums still run in ascending s); only for
+// many splits, which come with few tokens: the batch needs 96 registers where
+// the plain loop needs 26, which would cut the occupancy of the large-T
+// launches.
+template <bool F16, bool BATCH>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int splits,
                                                       int64_t T, int k, int64_t H, int E,
                                                       const float* __restrict__ topk_w,
@@ -31,10 +36,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (e < 0 || e >= E) continue;
     const float wj = topk_w[f];
     float4 ys = *reinterpret_cast<const float4*>(y + f * H + h);
-    // partials 8 at a time: their loads are in flight together, the sums
-    // still run in ascending s
     int s = 1;
-    for (; s + 7 < splits; s += 8) {
+    for (; BATCH && s + 7 < splits; s += 8) {
       float4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(y + ((s + u) * Tk + f) * H + h);
@@ -67,12 +70,18 @@ hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t 
                           hipStream_t stream) {
   const int64_t n = T * (H / 4);
   const int64_t blocks = (n + 255) / 256;
-  if (f16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       y, splits, T, k, H, E, topk_w, topk_ids, out);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       y, splits, T, k, H, E, topk_w, topk_ids, out);
+#define COMBINE(F, B)                                                                                    \
+  hipLaunchKernelGGL((combine_kernel<F, B>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y, splits, \
+                     T, k, H, E, topk_w, topk_ids, out)
+  const bool batch = splits > 8;
+  if (f16) {
+    if (batch) COMBINE(true, true);
+    else COMBINE(true, false);
+  } else {
+    if (batch) COMBINE(false, true);
+    else COMBINE(false, false);
+  }
+#undef COMBINE
   return hipGetLastError();
 }
 
