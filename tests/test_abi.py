@@ -57,6 +57,11 @@ def test_heuristics():
         assert (I // 128) % pkg.moe_w8a16_splits(T, H, I, E, k, 128) == 0     # tiled path: equal splits
         assert pkg.moe_w8a16_workspace_bytes(T, H, I, E, k, 0) > 0
     assert pkg.moe_w8a16_workspace_bytes(0, 4096, 14336, 8, 2, 0) == 0
+    # Mixtral prefill: 256-row blocks; K cut in two at T=1024 (384 workgroups would leave half the
+    # CUs idle in a second round), one part at T=4096
+    assert pkg.moe_w8a16_block_m(1024, 4096, 14336, 8, 2) == 256
+    assert pkg.moe_w8a16_splits(1024, 4096, 14336, 8, 2, 0) == 2
+    assert pkg.moe_w8a16_splits(4096, 4096, 14336, 8, 2, 0) == 1
 
 
 FAKE = 0x100000          # an aligned address that is never dereferenced: every call below fails first
@@ -112,6 +117,12 @@ def test_other_argument_errors():
                              p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # more splits than 128-wide steps
     assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 128, 3,
                              p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # tiled kernels need equal splits
+    # 256-row blocks: the fixed-point GEMM2 (H a multiple of 256) takes uneven parts of whole groups
+    # (T = 0 stops after the argument checks), the tiled kernel (H = 384) does not
+    assert L.moe_w8a16_gemm2(p(FAKE), 0, 512, 384, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 256, 2,
+                             p(FAKE), None) == B.MOE_OK
+    assert L.moe_w8a16_gemm2(p(FAKE), 0, 384, 384, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 256, 2,
+                             p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_combine_topk(p(FAKE), 1, 4, 2, 256, 8, p(FAKE), p(FAKE), 5, p(FAKE), None) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_w8a16_requant(p(FAKE), 4, 500, 8, 2, p(FAKE), p(FAKE), 32, None) == \
         B.MOE_ERR_INVALID_ARGUMENT                         # I not a multiple of 128
