@@ -193,10 +193,11 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
     auto jlo = [](int m) { return m * 8 / MT1; };
     // scheduling of one slot (8 MFMAs, nconv conversions of 12 VALU each, a
     // few LDS reads): MFMA and VALU alternate so that the conversions and
-    // address arithmetic issue while the matrix core works (for 8 row tiles,
-    // 2 VALU per MFMA: measured faster than 1 or 3)
+    // address arithmetic issue while the matrix core works (measured: for 8
+    // row tiles 2 VALU per MFMA beats 1 or 3; partly filled blocks one less
+    // than their conversions need per MFMA)
     auto interleave = []() {
-      constexpr int per = (12 * ((8 + MT1 - 1) / MT1) + 7) / 8;
+      constexpr int per = (12 * ((8 + MT1 - 1) / MT1) + 7) / 8 - (MT1 < 8 ? 1 : 0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
