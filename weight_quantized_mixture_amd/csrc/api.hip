@@ -154,9 +154,11 @@ bool gemm2_int8(int64_t bm) { return bm <= 64; }
 // Expected rows per active expert above 2.5: narrower waves (more
 // workgroups) stream better; with fewer rows, 4 column tiles per wave.
 // Measured on the Mixtral decode shape (E 8, H 4096): 2 tiles faster by 8%
-// at 3 to 6 rows per expert, 4 tiles by 1-8% at 1.5 to 2.2 rows.
-int gemm2_nt(int64_t T, int64_t E, int64_t k, int64_t bm) {
-  if (bm == 64) return 2;
+// at 3 to 6 rows per expert, 4 tiles by 1-8% at 1.5 to 2.2 rows.  Blocks of
+// 64 rows: 4 tiles for H >= 4096 (Mixtral T = 96 and 128: 4-9% faster), 2
+// below (the fine-grained shape, H 2048, T = 128 and 512: 1-4% faster).
+int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
+  if (bm == 64) return H >= 4096 ? 4 : 2;
   const double miss = std::pow(1.0 - static_cast<double>(k) / static_cast<double>(E), static_cast<double>(T));
   const double hit = static_cast<double>(E) * (1.0 - miss);
   return static_cast<double>(T * k) / (hit > 1.0 ? hit : 1.0) > 2.5 ? 2 : 4;
@@ -195,7 +197,7 @@ int64_t gemm2_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int6
       if (steps % sp == 0) best = sp;
     return best;
   }
-  const int64_t groups = (H / (64 * gemm2_nt(T, E, k, bm))) * blocks;
+  const int64_t groups = (H / (64 * gemm2_nt(T, H, E, k, bm))) * blocks;
   int64_t sp = 1;
   while (sp * 2 <= 16 && sp * 2 <= steps && groups * sp * 2 <= 512) sp *= 2;
   return sp;
@@ -232,7 +234,7 @@ hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, h
   }
   if (!gemm2_int8(p.block_m)) return moe::launch_gemm2_w8(p, stream);
   const Q16 q = q16_at(p.a, p.cap, p.I, planes_bytes(p.cap, p.I));
-  return moe::launch_gemm2_q16(p, gemm2_nt(T, E, k, p.block_m), q.hi, q.lo, q.scale, stream);
+  return moe::launch_gemm2_q16(p, gemm2_nt(T, p.H, E, k, p.block_m), q.hi, q.lo, q.scale, stream);
 }
 
 struct Layout {
