@@ -152,3 +152,17 @@ def test_binding_raises_python_errors():
         B._check(B.MOE_ERR_UNSUPPORTED, "x")
     with pytest.raises(B.MoeError):
         B._check(B.MOE_ERR_HIP, "x")
+
+
+def test_binding_rejects_wrong_partial_shapes():
+    # the combine and GEMM2 bindings check the split partials' shape before any call (CPU tensors:
+    # the shape check fires first)
+    import torch
+    T, k, H = 4, 2, 256
+    out = torch.zeros(T, H, dtype=torch.bfloat16)
+    tw = torch.zeros(T, k)
+    ti = torch.zeros(T, k, dtype=torch.int32)
+    with pytest.raises(ValueError, match="y"):
+        pkg.moe_combine_topk(torch.zeros(2, T * k - 1, H), 2, tw, ti, 8, out)
+    with pytest.raises(ValueError, match="topk_w"):
+        pkg.moe_combine_topk(torch.zeros(2, T * k, H), 2, torch.zeros(T, k + 1), ti, 8, out)

@@ -264,6 +264,10 @@ def moe_w8a16_gemm2(a, T, k, w2, w2_scale, sorted_ids, block_expert, num_padded,
 def moe_combine_topk(y, splits, topk_w, topk_ids, E, out, stream=None):
     T, H = out.shape
     k = topk_ids.shape[1]
+    _need(y, torch.float32, (splits, T * k, H), "y")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, out.dtype, (T, H), "out")
     _check(lib().moe_combine_topk(_ptr(y), splits, T, k, H, E, _ptr(topk_w), _ptr(topk_ids), _act(out),
                                   _ptr(out), _stream(stream)), "moe_combine_topk")
 
