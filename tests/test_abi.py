@@ -166,3 +166,71 @@ def test_binding_rejects_wrong_partial_shapes():
         pkg.moe_combine_topk(torch.zeros(2, T * k - 1, H), 2, tw, ti, 8, out)
     with pytest.raises(ValueError, match="y: dtype"):
         pkg.moe_combine_topk(torch.zeros(2, T * k, H, dtype=torch.float64), 2, tw, ti, 8, out)
+
+
+def _no_library(*a, **k):
+    raise AssertionError("the library was called before the arguments were checked")
+
+
+@pytest.mark.parametrize("bad", ["cpu", "strided", "dtype", "rank"])
+def test_binding_checks_x_before_any_call(monkeypatch, bad):
+    """Every entry point that takes activations rejects a host, non-contiguous, wrongly typed or
+    wrongly shaped x before it touches the library (a host pointer would reach the kernels)."""
+    import torch
+    T, H, I, E, k = 4, 256, 512, 8, 2
+    if bad == "cpu":
+        x = torch.zeros(T, H, dtype=torch.bfloat16)
+    elif bad == "strided":
+        x = torch.zeros(H, T, dtype=torch.bfloat16).t()
+    elif bad == "dtype":
+        x = torch.zeros(T, H, dtype=torch.float32)
+    else:
+        x = torch.zeros(T, H, 1, dtype=torch.bfloat16)
+    err = NotImplementedError if bad == "dtype" else ValueError
+    monkeypatch.setattr(B, "lib", _no_library)
+    w13 = torch.zeros(E, 2 * I, H, dtype=torch.int8)
+    w2 = torch.zeros(E, H, I, dtype=torch.int8)
+    s13, s2 = torch.zeros(E, 2 * I), torch.zeros(E, H)
+    tw, ti = torch.zeros(T, k), torch.zeros(T, k, dtype=torch.int32)
+    out = torch.zeros(T, H, dtype=torch.bfloat16)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    logits = torch.zeros(T, E)
+    qw13 = torch.zeros(E, 2 * I, H // 8, dtype=torch.int32)
+    sc13 = torch.zeros(E, 2 * I, H // 128, dtype=torch.float16)
+    qz13 = torch.zeros(E, 2 * I // 8, H // 128, dtype=torch.int32)
+    qw2 = torch.zeros(E, H, I // 8, dtype=torch.int32)
+    sc2 = torch.zeros(E, H, I // 128, dtype=torch.float16)
+    qz2 = torch.zeros(E, H // 8, I // 128, dtype=torch.int32)
+    ids = torch.zeros(16, dtype=torch.int32)
+    calls = [
+        lambda: B.moe_w8a16_forward(x, w13, s13, w2, s2, tw, ti, out, ws),
+        lambda: B.moe_w8a16_apply(x, logits, True, w13, s13, w2, s2, tw, ti, out, ws),
+        lambda: B.moe_w4a16_forward(x, qw13, sc13, qz13, qw2, sc2, qz2, 128, tw, ti, out, ws),
+        lambda: B.moe_w4a16_apply(x, logits, True, qw13, sc13, qz13, qw2, sc2, qz2, 128, tw, ti, out, ws),
+        lambda: B.moe_w8a16_gemm1(x, w13, s13, ids, ids, ids[:1], 16, k, ws),
+    ]
+    for c in calls:
+        with pytest.raises(err, match="x|activation"):
+            c()
+
+
+def test_binding_align_checks():
+    """The stage calls' check of the align outputs: sizes from moe_align_capacity, int32, 1-element
+    num_padded (shape and type checks fire before the device check, so host tensors show them)."""
+    import torch
+    T, k, E, bm = 5, 2, 8, 16
+    cap = pkg.moe_align_capacity(T, k, E, bm)
+    good = (torch.zeros(cap, dtype=torch.int32), torch.zeros(cap // bm, dtype=torch.int32),
+            torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="sorted_ids: shape"):
+        B._need_align(T, k, E, bm, torch.zeros(cap - 1, dtype=torch.int32), *good[1:])
+    with pytest.raises(ValueError, match="sorted_ids: dtype"):
+        B._need_align(T, k, E, bm, torch.zeros(cap, dtype=torch.int64), *good[1:])
+    with pytest.raises(ValueError, match="block_expert: shape"):
+        B._need_align(T, k, E, bm, good[0], torch.zeros(cap, dtype=torch.int32), good[2])
+    with pytest.raises(ValueError, match="num_padded: shape"):
+        B._need_align(T, k, E, bm, good[0], good[1], torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="block_m"):
+        B._need_align(T, k, E, 0, *good)
+    with pytest.raises(ValueError, match="sorted_ids must be a device tensor"):
+        B._need_align(T, k, E, bm, *good)

@@ -56,6 +56,21 @@ def test_ragged_shapes(act, bm, T, pad):
     assert_layer_close(got, ref_w8(W, xb, act, w_ref, ids_ref), f"ragged {act} bm={bm} T={T} pad={pad}")
 
 
+@pytest.mark.parametrize("H,I,T,bm", [(384, 256, 1, 0), (896, 256, 1, 0), (384, 512, 20, 32), (4224, 256, 130, 64),
+                                      (640, 384, 3, 16)])
+def test_hidden_not_multiple_of_256(H, I, T, bm):
+    """H a multiple of 128 but not of 256 on the integer GEMM2 of 16-64-row blocks: every column of
+    y is written (the kernel takes 128 columns per workgroup there, not 256)."""
+    E, k = 8, 2
+    log(f"[layer] H={H} I={I} T={T} block_m={bm}")
+    W = small_w8(E, H, I, seed=H + T, pad=True)
+    xb = synthetic.random_activations(T, H, "bf16", seed=H)
+    logits = synthetic.random_logits(T, E, seed=H + 1)
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, "bf16", logits, k, block_m=bm)
+    _check_routing(ti, tw, ids_ref, w_ref)
+    assert_layer_close(got, ref_w8(W, xb, "bf16", w_ref, ids_ref), f"H={H} T={T} bm={bm}")
+
+
 def test_block256_odd_hidden():
     """256-row blocks with H not a multiple of 256 (the GEMM2 tile): the generic tiled kernel."""
     E, k, H, I, T = 4, 2, 384, 256, 200
@@ -148,31 +163,59 @@ def test_bad_shapes_raise():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("T", [1, 8, 32, 64])
-def test_mixtral_decode(T):
+@pytest.mark.parametrize("T,bm", [(1, 0), (8, 0), (32, 0), (64, 0), (64, 64)])
+def test_mixtral_decode(T, bm):
+    """Every token against the oracle; a second run must give the same bytes (the integer GEMM2 of
+    16/32/64-row blocks with its split-K partials summed in a fixed order)."""
     wl = synthetic.WORKLOADS["mixtral_decode"]
     W = workload_weights(wl)
     assert W.mismatch == 0, "GPU int8 codes or scales differ from the oracle"
     xb = synthetic.activations(wl, T)
     logits = synthetic.router_logits(wl, T)
-    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, wl.act, logits, wl.k)
+    log(f"[layer] mixtral decode T={T} block_m={bm or pkg.moe_w8a16_block_m(T, wl.H, wl.I, wl.E, wl.k)} "
+        f"splits={pkg.moe_w8a16_splits(T, wl.H, wl.I, wl.E, wl.k, bm)}")
+    got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, wl.act, logits, wl.k, block_m=bm)
     _check_routing(ti, tw, ids_ref, w_ref)
-    assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), f"mixtral decode T={T}")
+    again, *_ = run_w8_layer(W, xb, wl.act, logits, wl.k, block_m=bm)
+    assert np.array_equal(got, again), "two runs differ bitwise"
+    assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), f"mixtral decode T={T} bm={bm}")
+
+
+def _edge_block_tokens(ids, E, k, block_m):
+    """Tokens routed through the first or the last align block of every expert."""
+    sorted_ids, block_expert, npad = oracle.align_block(ids, E, block_m)
+    tk = ids.size
+    toks = []
+    for e in range(E):
+        blocks = np.nonzero(block_expert[:npad // block_m] == e)[0]
+        for b in {int(blocks[0]), int(blocks[-1])} if blocks.size else ():
+            f = sorted_ids[b * block_m:(b + 1) * block_m]
+            toks.append(f[f < tk] // k)
+    return np.unique(np.concatenate(toks))
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("T,nsample", [(1024, 96), (4096, 64)])
 def test_mixtral_prefill_sampled(T, nsample):
+    """256-row tiles: every token of the first and the last 256-row block of each expert (all row
+    positions of a full tile and of the ragged last tile), plus an even sample; a second run gives
+    the same bytes (GEMM2 split into 2 K parts at T=1024, one at T=4096)."""
     wl = synthetic.WORKLOADS["mixtral_prefill"]
     W = workload_weights(wl)
     assert W.mismatch == 0
     xb = synthetic.activations(wl, T)
     logits = synthetic.router_logits(wl, T)
+    bm = pkg.moe_w8a16_block_m(T, wl.H, wl.I, wl.E, wl.k)
+    log(f"[layer] mixtral prefill T={T} block_m={bm} splits={pkg.moe_w8a16_splits(T, wl.H, wl.I, wl.E, wl.k, 0)}")
     got, tw, ti, w_ref, ids_ref = run_w8_layer(W, xb, wl.act, logits, wl.k)
     _check_routing(ti, tw, ids_ref, w_ref)
-    rows = np.unique(np.concatenate([[0, T - 1], np.linspace(0, T - 1, nsample).astype(int)]))
+    again, *_ = run_w8_layer(W, xb, wl.act, logits, wl.k)
+    assert np.array_equal(got, again), "two runs differ bitwise"
+    edge = _edge_block_tokens(ids_ref, wl.E, wl.k, bm)
+    rows = np.unique(np.concatenate([[0, T - 1], np.linspace(0, T - 1, nsample).astype(int), edge]))
+    log(f"[layer] checking {rows.size} tokens ({edge.size} from the edge blocks)")
     assert_layer_close(got[rows], ref_w8(W, xb, wl.act, w_ref, ids_ref, rows=rows),
-                       f"mixtral prefill T={T} ({rows.size} sampled tokens)")
+                       f"mixtral prefill T={T} ({rows.size} tokens)")
 
 
 @pytest.mark.timeout(900)

@@ -116,6 +116,28 @@ def _act(t: torch.Tensor) -> int:
     raise NotImplementedError(f"activation dtype {t.dtype} (bf16 or fp16 only)")
 
 
+def _need_act(x, name="x"):
+    """Activations: a contiguous 2-D bf16/fp16 device tensor; returns (T, H, act code)."""
+    act = _act(x)
+    if x.dim() != 2:
+        raise ValueError(f"{name}: expected [T, H], got shape {tuple(x.shape)}")
+    _need(x, x.dtype, tuple(x.shape), name)
+    return x.shape[0], x.shape[1], act
+
+
+def _need_align(T, k, E, block_m, sorted_ids, block_expert, num_padded):
+    """The align outputs the stage calls read, sized by moe_align_capacity."""
+    if block_m < 1:
+        raise ValueError(f"block_m must be >= 1, got {block_m}")
+    cap = moe_align_capacity(T, k, E, block_m)
+    need = [(sorted_ids, (cap,), "sorted_ids"), (block_expert, (cap // block_m,), "block_expert"),
+            (num_padded, (1,), "num_padded")]
+    for t, shape, name in need:
+        _need(t, torch.int32, shape, name, device=False)
+    for t, shape, name in need:
+        _need(t, torch.int32, shape, name)
+
+
 def _row_stride(t, dtype, shape, name) -> int:
     """Weights may be row-padded views: [E, N, K] with strides (N*ld, ld, 1), ld >= K; returns ld."""
     if t.dtype != dtype:
@@ -131,14 +153,14 @@ def _row_stride(t, dtype, shape, name) -> int:
     return ld
 
 
-def _need(t, dtype, shape, name):
+def _need(t, dtype, shape, name, device=True):
     if t.dtype != dtype:
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if not t.is_cuda:
+    if device and not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
 
 
@@ -197,6 +219,8 @@ def moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m=0) -> int:
 def _need_bytes(t: torch.Tensor, nbytes: int, name: str):
     if not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
         raise ValueError(f"{name}: needs a contiguous buffer of at least {nbytes} bytes")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
 
 
 def moe_w8a16_workspace_bytes(T, H, I, E, k, block_m=0) -> int:
@@ -217,7 +241,7 @@ def moe_w8a16_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, wo
                       block_m: int = 0, stream=None):
     """out = MoE(x) for int8 experts; `workspace` is a uint8 device tensor of
     at least moe_w8a16_workspace_bytes(...) bytes; `out` may be `x`."""
-    T, H = x.shape
+    T, H, act = _need_act(x)
     E, _, I = _w8_shapes(w13, w2)
     k = topk_ids.shape[1]
     ld13 = _row_stride(w13, torch.int8, (E, 2 * I, H), "w13")
@@ -227,24 +251,30 @@ def moe_w8a16_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, wo
     _need(topk_w, torch.float32, (T, k), "topk_w")
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
     _need(out, x.dtype, (T, H), "out")
-    _check(lib().moe_w8a16_forward(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13,
+    _need_bytes(workspace, moe_w8a16_workspace_bytes(T, H, I, E, k, block_m), "workspace")
+    _check(lib().moe_w8a16_forward(_ptr(x), act, T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13,
                                    _ptr(w2), _ptr(w2_scale), ld2, _ptr(topk_w), _ptr(topk_ids), block_m,
                                    _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "moe_w8a16_forward")
 
 
 def moe_w8a16_gemm1(x, w13, w13_scale, sorted_ids, block_expert, num_padded, block_m, k, a, stream=None):
-    T, H = x.shape
+    T, H, act = _need_act(x)
     E, N2, _ = w13.shape
     I = N2 // 2
     ld13 = _row_stride(w13, torch.int8, (E, N2, H), "w13")
+    _need(w13_scale, torch.float32, (E, N2), "w13_scale")
+    _need_align(T, k, E, block_m, sorted_ids, block_expert, num_padded)
     _need_bytes(a, moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m), "a")
-    _check(lib().moe_w8a16_gemm1(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13,
+    _check(lib().moe_w8a16_gemm1(_ptr(x), act, T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13,
                                  _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), block_m, _ptr(a),
                                  _stream(stream)), "moe_w8a16_gemm1")
 
 
 def moe_w8a16_requant(a, T, I, E, k, sorted_ids, num_padded, block_m, stream=None):
+    cap = moe_align_capacity(T, k, E, block_m)
+    _need(sorted_ids, torch.int32, (cap,), "sorted_ids")
+    _need(num_padded, torch.int32, (1,), "num_padded")
     _need_bytes(a, moe_w8a16_intermediate_bytes(T, 128, I, E, k, block_m), "a")
     _check(lib().moe_w8a16_requant(_ptr(a), T, I, E, k, _ptr(sorted_ids), _ptr(num_padded), block_m,
                                    _stream(stream)), "moe_w8a16_requant")
@@ -254,6 +284,8 @@ def moe_w8a16_gemm2(a, T, k, w2, w2_scale, sorted_ids, block_expert, num_padded,
                     stream=None):
     E, H, I = w2.shape
     ld2 = _row_stride(w2, torch.int8, (E, H, I), "w2")
+    _need(w2_scale, torch.float32, (E, H), "w2_scale")
+    _need_align(T, k, E, block_m, sorted_ids, block_expert, num_padded)
     _need_bytes(a, moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m), "a")
     _need(y, torch.float32, (splits, T * k, H), "y")
     _check(lib().moe_w8a16_gemm2(_ptr(a), T, H, I, E, k, _ptr(w2), _ptr(w2_scale), ld2, _ptr(sorted_ids),
@@ -267,7 +299,7 @@ def moe_combine_topk(y, splits, topk_w, topk_ids, E, out, stream=None):
     _need(y, torch.float32, (splits, T * k, H), "y")
     _need(topk_w, torch.float32, (T, k), "topk_w")
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
-    _need(out, out.dtype, (T, H), "out")
+    _need_act(out, "out")
     _check(lib().moe_combine_topk(_ptr(y), splits, T, k, H, E, _ptr(topk_w), _ptr(topk_ids), _act(out),
                                   _ptr(out), _stream(stream)), "moe_combine_topk")
 
@@ -284,7 +316,7 @@ def moe_quantize_weights_w4(w, group_size, qweight, scales, qzeros, stream=None)
 
 def moe_w4a16_forward(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales, w2_qzeros,
                       group_size, topk_w, topk_ids, out, workspace, block_m: int = 0, stream=None):
-    T, H = x.shape
+    T, H, act = _need_act(x)
     E, N2, _ = w13_qweight.shape
     I = N2 // 2
     k = topk_ids.shape[1]
@@ -294,8 +326,11 @@ def moe_w4a16_forward(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_sca
     _need(w2_qweight, torch.int32, (E, H, I // 8), "w2_qweight")
     _need(w2_scales, torch.float16, (E, H, I // group_size), "w2_scales")
     _need(w2_qzeros, torch.int32, (E, H // 8, I // group_size), "w2_qzeros")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
     _need(out, x.dtype, (T, H), "out")
-    _check(lib().moe_w4a16_forward(_ptr(x), _act(x), T, H, I, E, k, _ptr(w13_qweight), _ptr(w13_scales),
+    _need_bytes(workspace, moe_w4a16_workspace_bytes(T, H, I, E, k, block_m), "workspace")
+    _check(lib().moe_w4a16_forward(_ptr(x), act, T, H, I, E, k, _ptr(w13_qweight), _ptr(w13_scales),
                                    _ptr(w13_qzeros), _ptr(w2_qweight), _ptr(w2_scales), _ptr(w2_qzeros),
                                    group_size, _ptr(topk_w), _ptr(topk_ids), block_m, _ptr(out),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -305,7 +340,7 @@ def moe_w4a16_forward(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_sca
 def moe_w8a16_apply(x, router_logits, renormalize, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out,
                     workspace, block_m: int = 0, stream=None):
     """Route from logits and run the layer in one call; topk_w / topk_ids receive the routing."""
-    T, H = x.shape
+    T, H, act = _need_act(x)
     E, _, I = _w8_shapes(w13, w2)
     k = topk_ids.shape[1]
     _need(router_logits, torch.float32, (T, E), "router_logits")
@@ -316,7 +351,8 @@ def moe_w8a16_apply(x, router_logits, renormalize, w13, w13_scale, w2, w2_scale,
     _need(topk_w, torch.float32, (T, k), "topk_w")
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
     _need(out, x.dtype, (T, H), "out")
-    _check(lib().moe_w8a16_apply(_ptr(x), _act(x), T, H, I, E, k, _ptr(router_logits), int(bool(renormalize)),
+    _need_bytes(workspace, moe_w8a16_workspace_bytes(T, H, I, E, k, block_m), "workspace")
+    _check(lib().moe_w8a16_apply(_ptr(x), act, T, H, I, E, k, _ptr(router_logits), int(bool(renormalize)),
                                  _ptr(w13), _ptr(w13_scale), ld13, _ptr(w2), _ptr(w2_scale), ld2, _ptr(topk_w),
                                  _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)), "moe_w8a16_apply")
@@ -324,7 +360,7 @@ def moe_w8a16_apply(x, router_logits, renormalize, w13, w13_scale, w2, w2_scale,
 
 def moe_w4a16_apply(x, router_logits, renormalize, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
                     w2_qzeros, group_size, topk_w, topk_ids, out, workspace, block_m: int = 0, stream=None):
-    T, H = x.shape
+    T, H, act = _need_act(x)
     E, N2, _ = w13_qweight.shape
     I = N2 // 2
     k = topk_ids.shape[1]
@@ -338,7 +374,8 @@ def moe_w4a16_apply(x, router_logits, renormalize, w13_qweight, w13_scales, w13_
     _need(topk_w, torch.float32, (T, k), "topk_w")
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
     _need(out, x.dtype, (T, H), "out")
-    _check(lib().moe_w4a16_apply(_ptr(x), _act(x), T, H, I, E, k, _ptr(router_logits), int(bool(renormalize)),
+    _need_bytes(workspace, moe_w4a16_workspace_bytes(T, H, I, E, k, block_m), "workspace")
+    _check(lib().moe_w4a16_apply(_ptr(x), act, T, H, I, E, k, _ptr(router_logits), int(bool(renormalize)),
                                  _ptr(w13_qweight), _ptr(w13_scales), _ptr(w13_qzeros), _ptr(w2_qweight),
                                  _ptr(w2_scales), _ptr(w2_qzeros), group_size, _ptr(topk_w), _ptr(topk_ids),
                                  block_m, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),

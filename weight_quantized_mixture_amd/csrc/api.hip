@@ -157,7 +157,10 @@ bool gemm2_int8(int64_t bm) { return bm <= 64; }
 // at 3 to 6 rows per expert, 4 tiles by 1-8% at 1.5 to 2.2 rows.  Blocks of
 // 64 rows: 4 tiles for H >= 4096 (Mixtral T = 96 and 128: 4-9% faster), 2
 // below (the fine-grained shape, H 2048, T = 128 and 512: 1-4% faster).
+// Four tiles cover 256 columns per workgroup, so they need H a multiple of
+// 256; otherwise two tiles (128 columns, which every H the layer accepts fills).
 int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
+  if (H % 256 != 0) return 2;
   if (bm == 64) return H >= 4096 ? 4 : 2;
   const double miss = std::pow(1.0 - static_cast<double>(k) / static_cast<double>(E), static_cast<double>(T));
   const double hit = static_cast<double>(E) * (1.0 - miss);

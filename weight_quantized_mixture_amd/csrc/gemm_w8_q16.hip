@@ -301,6 +301,7 @@ hipError_t launch_requant_q16(const float* a, int64_t cap, int64_t I, const int3
 hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, const int8_t* qhi, const int8_t* qlo, const float* qscale,
                             hipStream_t stream) {
   const int mt = p.block_m / 16;
+  if ((nt != 2 && nt != 4) || p.H % (64 * nt) != 0 || mt < 1 || mt > 4) return hipErrorInvalidValue;
   const unsigned by = static_cast<unsigned>(p.cap / p.block_m), bz = static_cast<unsigned>(p.splits);
 #define Q16(MT, NT, FQ)                                                                                   \
   hipLaunchKernelGGL((gemm2_q16_kernel<MT, NT, FQ>), dim3(static_cast<unsigned>(p.H / (64 * NT)), by, bz), \
