@@ -20,7 +20,8 @@
  * Conventions for every call:
  *   - Pointers named "device" are device memory of the current HIP device;
  *     the caller allocates and owns every buffer.  The library allocates no
- *     device memory and keeps no state apart from a thread-local error text.
+ *     device memory and keeps no state apart from a thread-local error text
+ *     and the static workspace of moe_w8a16_forward_noalloc (one per device).
  *   - Work is enqueued on `stream` (NULL = the default stream) and never
  *     synchronised; results are ready when the stream reaches them.
  *   - Arguments are checked on the host before anything is enqueued; on an
@@ -141,6 +142,33 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
                       const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
                       const float* topk_w, const int32_t* topk_ids, int64_t block_m,
                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_w8a16_forward without allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc) nor provide a workspace.
+ * Same arguments and result as moe_w8a16_forward (bit for bit: the same
+ * kernels), minus workspace / workspace_bytes: the workspace is a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES bytes (256-byte aligned) that
+ * each GPU the library runs on holds until the process ends.  The first call
+ * on a device looks its address up (hipGetSymbolAddress) with that device
+ * current; no call allocates or frees memory.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on the
+ * same GPU (two streams, two threads) race and must be serialised by the
+ * caller.  Nothing is carried from one call to the next (every region a call
+ * reads it first writes), so no clearing is needed between calls.
+ * Errors: those of moe_w8a16_forward, and MOE_ERR_WORKSPACE_TOO_SMALL when
+ * moe_w8a16_workspace_bytes(T, H, I, E, k, block_m) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB covers the decode-sized batches, e.g.
+ * E 8, top-2, H 4096, I 14336 up to T = 64, 33 MiB); nothing is launched then.
+ * ---------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int moe_w8a16_forward_noalloc(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I,
+                              int64_t E, int64_t k,
+                              const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                              const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                              const float* topk_w, const int32_t* topk_ids, int64_t block_m,
+                              void* out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Routing + forward in one call, from router logits (the moe_wna16 page's

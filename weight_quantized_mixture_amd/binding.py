@@ -40,6 +40,9 @@ SIGNATURES = {
     "moe_w8a16_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
                                    _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
                                    _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_w8a16_forward_noalloc": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                           _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                           _c_p, _c_p, _c_i64, _c_p, _c_p]),
     "moe_w8a16_apply": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_int,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
@@ -256,6 +259,28 @@ def moe_w8a16_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, wo
                                    _ptr(w2), _ptr(w2_scale), ld2, _ptr(topk_w), _ptr(topk_ids), block_m,
                                    _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "moe_w8a16_forward")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20     # size of the static workspace of moe_w8a16_forward_noalloc
+
+
+def moe_w8a16_forward_noalloc(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, block_m: int = 0,
+                              stream=None):
+    """moe_w8a16_forward on the library's static device workspace (no workspace argument, nothing
+    allocated); raises ValueError when the batch needs more than MOE_NOALLOC_SCRATCH_BYTES."""
+    T, H, act = _need_act(x)
+    E, _, I = _w8_shapes(w13, w2)
+    k = topk_ids.shape[1]
+    ld13 = _row_stride(w13, torch.int8, (E, 2 * I, H), "w13")
+    _need(w13_scale, torch.float32, (E, 2 * I), "w13_scale")
+    ld2 = _row_stride(w2, torch.int8, (E, H, I), "w2")
+    _need(w2_scale, torch.float32, (E, H), "w2_scale")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    _check(lib().moe_w8a16_forward_noalloc(_ptr(x), act, T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13,
+                                           _ptr(w2), _ptr(w2_scale), ld2, _ptr(topk_w), _ptr(topk_ids), block_m,
+                                           _ptr(out), _stream(stream)), "moe_w8a16_forward_noalloc")
 
 
 def moe_w8a16_gemm1(x, w13, w13_scale, sorted_ids, block_expert, num_padded, block_m, k, a, stream=None):

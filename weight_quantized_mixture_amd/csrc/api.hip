@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe_wq.h"
 #include "launch.hpp"
@@ -564,6 +565,70 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
   return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
                     router_logits, renormalize, topk_w, topk_ids, nullptr, nullptr, block_m, out, workspace,
                     workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Forward without allocation: the workspace is a static device array
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// Device-resident workspace of moe_w8a16_forward_noalloc.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, never a device address: its device
+// address is looked up once per device with hipGetSymbolAddress and only that
+// pointer is handed to kernels.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_w8a16_forward_noalloc(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E,
+                              int64_t k, const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                              const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                              const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
+                              hipStream_t stream) {
+  int st;
+  if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
+  const int64_t bm = block_m == 0 ? auto_block_m(T, E, k) : block_m;
+  if ((st = check_block_m(bm)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  const size_t need = layout(T, H, I, E, k, bm, splits_for(T, H, I, E, k, bm), true).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "this batch needs %zu bytes of workspace; the static scratch of the no-alloc forward holds %zu "
+                "(use moe_w8a16_forward with a caller workspace)",
+                need, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+  return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                    nullptr, 0, nullptr, nullptr, topk_w, topk_ids, bm, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---------------------------------------------------------------------------
