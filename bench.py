@@ -60,13 +60,18 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace --stats output folder into the kernel-time summary "
                          "under profiles/ and exit")
-    ap.add_argument("--flush-mb", type=int, default=None,
+    ap.add_argument("--flush-mb", type=int, default=512,
                     help="read this many MB of other data between timed steps (outside the events) so "
-                         "the 256 MB Infinity Cache does not serve the weights; default: 512 when the "
-                         "active weights are below 1 GB, else 0.  A read, not a write: written lines "
-                         "would be written back to HBM during the next timed step")
+                         "the 256 MB Infinity Cache does not serve the weights (0 = no flush).  A read, "
+                         "not a write: written lines would be written back to HBM during the next timed step")
+    ap.add_argument("--no-prefill-band", action="store_true",
+                    help="with the default decode workload, skip the Mixtral prefill T=4096 line measured "
+                         "next to it on the same weights")
     return ap.parse_args()
 
+
+# the metric's MFMA band, measured next to the default decode line
+PREFILL_BAND_T = 4096
 
 HEADLINE_T = {"tiny": 16, "mixtral_decode": 64, "mixtral_prefill": 4096, "fine_grained": 512, "w4a16": 256}
 
@@ -216,6 +221,155 @@ def recorded_traffic(workload, T, kernel_prefix):
     return None
 
 
+def _rnd(v, n=5):
+    """Round floats for the JSON line (keeps it short enough for a log tail)."""
+    if isinstance(v, float):
+        return float(f"{v:.{n}g}")
+    if isinstance(v, dict):
+        return {k: _rnd(x, n) for k, x in v.items()}
+    return v
+
+
+def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True):
+    """Time `args.steps` layer calls (logits -> output) of workload `wl` at T tokens on the layer's
+    resident weights, with a read flush of `args.flush_mb` MB before each step (outside the timed
+    events), then time each stage once per repetition for the dominant kernel's roofline."""
+    import numpy as np
+    E, k, H, I = wl.E, wl.k, wl.H, wl.I
+    w4 = wl.weights == "w4"
+    xb = synthetic.activations(wl, T, args.seed)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16 if wl.act == "bf16" else torch.float16).to(dev)
+    logits_np = synthetic.router_logits(wl, T, args.seed)
+    logits = torch.from_numpy(logits_np).to(dev)
+    out = torch.empty_like(x)
+    tw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    ti = torch.empty(T, k, dtype=torch.int32, device=dev)
+    block_m = pkg.moe_w8a16_block_m(T, H, I, E, k)
+    splits = pkg.moe_w8a16_splits(T, H, I, E, k, block_m)
+    ws_bytes = (pkg.moe_w4a16_workspace_bytes if w4 else pkg.moe_w8a16_workspace_bytes)(T, H, I, E, k, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        # logits -> output in one library call (routing, align, GEMM1+SiLU, GEMM2, combine)
+        if w4:
+            pkg.moe_w4a16_apply(x, logits, wl.renormalize, layer.w13_qweight, layer.w13_scales, layer.w13_qzeros,
+                                layer.w2_qweight, layer.w2_scales, layer.w2_qzeros, wl.group_size, tw, ti, out, ws,
+                                0, stream)
+        else:
+            pkg.moe_w8a16_apply(x, logits, wl.renormalize, layer.w13_weight, layer.w13_scale, layer.w2_weight,
+                                layer.w2_scale, tw, ti, out, ws, 0, stream)
+
+    step()
+    torch.cuda.synchronize()
+    ids_np = ti.cpu().numpy()
+    active = np.unique(ids_np[(ids_np >= 0) & (ids_np < E)])
+    n_active = int(active.size)
+
+    # algorithmic work (what the method must move / compute; padding, the a/y
+    # round trips and the second (lo) MFMA of the intermediate are not counted)
+    if w4:
+        g = wl.group_size
+        per_expert_w13 = (2 * I * H) // 2 + (2 * I * (H // g)) * 2 + (2 * I * (H // g)) // 2
+        per_expert_w2 = (H * I) // 2 + (H * (I // g)) * 2 + (H * (I // g)) // 2
+    else:
+        per_expert_w13 = 2 * I * H + 2 * I * 4
+        per_expert_w2 = H * I + H * 4
+    act_bytes = 2
+    bytes_layer = (n_active * (per_expert_w13 + per_expert_w2) + T * H * act_bytes * 2 + T * E * 4 + T * k * 8)
+    bytes_gemm1 = n_active * per_expert_w13 + T * H * act_bytes
+    flops_layer = 6 * T * k * H * I
+    flops_gemm1 = 4 * T * k * H * I
+
+    flush_mb = args.flush_mb
+    flush = torch.ones(flush_mb << 18, dtype=torch.int32, device=dev) if flush_mb else None
+    flush_sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def evict():
+        if flush is not None:
+            torch.amax(flush, dim=0, keepdim=True, out=flush_sink)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        evict()
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = float(np.mean(step_ms))
+
+    # per-kernel durations: the same kernels, one stage call at a time, HIP events on the launch stream
+    stage_ms = {}
+    if not w4 and want_stages:
+        cap = pkg.moe_align_capacity(T, k, E, block_m)
+        s_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+        b_exp = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
+        npad = torch.empty(1, dtype=torch.int32, device=dev)
+        a_buf = torch.empty(pkg.moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m) // 4 + 64, dtype=torch.float32,
+                            device=dev)
+        y_buf = torch.empty(splits, T * k, H, dtype=torch.float32, device=dev)
+        names = ["route", "align", "gemm1", "requant", "gemm2", "combine"]
+        acc = {n: [] for n in names}
+        reps = max(5, min(args.steps, 20))
+        for i in range(reps + 2):
+            evict()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+            ev[0].record(stream)
+            pkg.moe_route_topk(logits, k, wl.renormalize, tw, ti, stream)
+            ev[1].record(stream)
+            pkg.moe_align_block(ti, E, block_m, s_ids, b_exp, npad, stream)
+            ev[2].record(stream)
+            pkg.moe_w8a16_gemm1(x, layer.w13_weight, layer.w13_scale, s_ids, b_exp, npad, block_m, k, a_buf, stream)
+            ev[3].record(stream)
+            pkg.moe_w8a16_requant(a_buf, T, I, E, k, s_ids, npad, block_m, stream)
+            ev[4].record(stream)
+            pkg.moe_w8a16_gemm2(a_buf, T, k, layer.w2_weight, layer.w2_scale, s_ids, b_exp, npad, block_m, splits,
+                                y_buf, stream)
+            ev[5].record(stream)
+            pkg.moe_combine_topk(y_buf, splits, tw, ti, E, out, stream)
+            ev[6].record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                for j, n in enumerate(names):
+                    acc[n].append(ev[j].elapsed_time(ev[j + 1]))
+        stage_ms = {n: float(np.mean(v)) for n, v in acc.items()}
+        del a_buf, y_buf
+
+    mfma_band = T >= 1024
+    layer_hbm_frac = bytes_layer / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS
+    layer_mfma_frac = flops_layer / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS
+    if stage_ms:
+        dur_s = stage_ms["gemm1"] / 1e3
+        if mfma_band:
+            roof = {"bound": "mfma", "achieved": flops_gemm1 / dur_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": bytes_gemm1 / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["kernel"] = gemm1_kernel_name(block_m, H)
+        roof["traffic"] = recorded_traffic(wl.name, T, roof["kernel"])
+        roof["kernel_ms"] = stage_ms["gemm1"]
+    else:
+        dur_s = ms_per_step / 1e3
+        roof = {"bound": "hbm", "achieved": bytes_layer / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": layer_hbm_frac, "traffic": None, "kernel": "whole layer"}
+    # the whole layer (route .. combine) against the same peak as the dominant kernel
+    roof["layer_frac"] = layer_mfma_frac if roof["bound"] == "mfma" else layer_hbm_frac
+    return {"T": T, "value": T / (ms_per_step / 1e3), "ms_per_step": ms_per_step,
+            "ms_per_step_median": float(np.median(step_ms)), "wall_s": wall,
+            "block_m": block_m, "splits": splits, "active_experts": n_active, "flush_mb": flush_mb,
+            "bytes": bytes_layer, "flops": flops_layer, "hbm_frac": layer_hbm_frac, "mfma_frac": layer_mfma_frac,
+            "stage_ms": stage_ms, "roofline": roof, "xb": xb, "logits_np": logits_np, "active": active}
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -254,12 +408,9 @@ def main():
     E, k, H, I = wl.E, wl.k, wl.H, wl.I
     w4 = wl.weights == "w4"
 
-    # ---- set-up: seeded inputs, weights quantized on the GPU ------------------
+    # ---- set-up: seeded weights quantized on the GPU (not part of a step) ----------
     t0 = time.time()
-    if w4:
-        layer = pkg.W4A16MoE(E, H, I, wl.group_size, device=dev)
-    else:
-        layer = pkg.W8A16MoE(E, H, I, device=dev)
+    layer = pkg.W4A16MoE(E, H, I, wl.group_size, device=dev) if w4 else pkg.W8A16MoE(E, H, I, device=dev)
     for e in range(E):
         m13 = torch.from_numpy(synthetic.expert_master(wl, "w13", e, args.seed)).to(dev)
         m2 = torch.from_numpy(synthetic.expert_master(wl, "w2", e, args.seed)).to(dev)
@@ -267,153 +418,34 @@ def main():
         del m13, m2
     torch.cuda.synchronize()
     log(f"[bench] weights ready ({time.time() - t0:.1f}s) workload={wl.name} T={T}")
-    xb = synthetic.activations(wl, T, args.seed)
-    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16 if wl.act == "bf16" else torch.float16).to(dev)
-    logits_np = synthetic.router_logits(wl, T, args.seed)
-    logits = torch.from_numpy(logits_np).to(dev)
-    out = torch.empty_like(x)
-    tw = torch.empty(T, k, dtype=torch.float32, device=dev)
-    ti = torch.empty(T, k, dtype=torch.int32, device=dev)
-    block_m = pkg.moe_w8a16_block_m(T, H, I, E, k)
-    splits = pkg.moe_w8a16_splits(T, H, I, E, k, block_m)
-    ws_bytes = (pkg.moe_w4a16_workspace_bytes if w4 else pkg.moe_w8a16_workspace_bytes)(T, H, I, E, k, 0)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
-    def step():
-        # logits -> output in one library call (routing, align, GEMM1+SiLU, GEMM2, combine)
-        if w4:
-            pkg.moe_w4a16_apply(x, logits, wl.renormalize, layer.w13_qweight, layer.w13_scales, layer.w13_qzeros,
-                                layer.w2_qweight, layer.w2_scales, layer.w2_qzeros, wl.group_size, tw, ti, out, ws,
-                                0, stream)
-        else:
-            pkg.moe_w8a16_apply(x, logits, wl.renormalize, layer.w13_weight, layer.w13_scale, layer.w2_weight,
-                                layer.w2_scale, tw, ti, out, ws, 0, stream)
+    m = measure(pkg, synthetic, torch, dev, layer, wl, T, args)
+    log(f"[bench] {wl.name} T={T}: {m['ms_per_step'] * 1e3:.1f} us/step")
 
-    step()
-    torch.cuda.synchronize()
-    ids_np = ti.cpu().numpy()
-    active = np.unique(ids_np[(ids_np >= 0) & (ids_np < E)])
-    n_active = int(active.size)
+    # ---- the metric's other band: Mixtral prefill T=4096 on the same weights -----------
+    prefill = None
+    if wl.name == "mixtral_decode" and not args.no_prefill_band:
+        pwl = synthetic.WORKLOADS["mixtral_prefill"]
+        pm = measure(pkg, synthetic, torch, dev, layer, pwl, PREFILL_BAND_T, args)
+        log(f"[bench] {pwl.name} T={PREFILL_BAND_T}: {pm['ms_per_step'] * 1e3:.1f} us/step")
+        r = pm["roofline"]
+        prefill = {"workload": pwl.name, "T": PREFILL_BAND_T, "value": pm["value"], "steps": args.steps,
+                   "ms_per_step": pm["ms_per_step"], "mfma_frac": pm["mfma_frac"],
+                   "roofline": {"kernel": r["kernel"], "frac": r["frac"], "kernel_ms": r["kernel_ms"],
+                                "traffic": r["traffic"]}}
 
-    # algorithmic work (what the method must move / compute; padding, the a/y
-    # round trips and the hi+lo second MFMA are not counted)
-    if w4:
-        g = wl.group_size
-        per_expert_w13 = (2 * I * H) // 2 + (2 * I * (H // g)) * 2 + (2 * I * (H // g)) // 2
-        per_expert_w2 = (H * I) // 2 + (H * (I // g)) * 2 + (H * (I // g)) // 2
-    else:
-        per_expert_w13 = 2 * I * H + 2 * I * 4
-        per_expert_w2 = H * I + H * 4
-    act_bytes = 2
-    bytes_layer = (n_active * (per_expert_w13 + per_expert_w2) + T * H * act_bytes * 2 + T * E * 4 + T * k * 8)
-    bytes_gemm1 = n_active * per_expert_w13 + T * H * act_bytes
-    flops_layer = 6 * T * k * H * I
-    flops_gemm1 = 4 * T * k * H * I
-
-    flush_mb = args.flush_mb
-    if flush_mb is None:
-        flush_mb = 512 if n_active * (per_expert_w13 + per_expert_w2) < (1 << 30) else 0
-    flush = torch.ones(flush_mb << 18, dtype=torch.int32, device=dev) if flush_mb else None
-    flush_sink = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    def evict():
-        torch.amax(flush, dim=0, keepdim=True, out=flush_sink)
-
-    # ---- warm-up -----------------------------------------------------------------
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- timed steps ---------------------------------------------------------------
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush is not None:
-            evict()
-        evs[i][0].record(stream)
-        step()
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_per_step = float(np.mean(step_ms))
-    ms_median = float(np.median(step_ms))
-    value = T / (ms_per_step / 1e3)
-
-    # ---- per-kernel durations (same kernels, one stage call at a time) ----------------
-    stage_ms = {}
-    if not w4:
-        cap = pkg.moe_align_capacity(T, k, E, block_m)
-        s_ids = torch.empty(cap, dtype=torch.int32, device=dev)
-        b_exp = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
-        npad = torch.empty(1, dtype=torch.int32, device=dev)
-        a_buf = torch.empty(pkg.moe_w8a16_intermediate_bytes(T, H, I, E, k, block_m) // 4 + 64, dtype=torch.float32,
-                            device=dev)
-        y_buf = torch.empty(splits, T * k, H, dtype=torch.float32, device=dev)
-        names = ["route", "align", "gemm1", "requant", "gemm2", "combine"]
-        acc = {n: [] for n in names}
-        reps = max(5, min(args.steps, 20))
-        for i in range(reps + 2):
-            if flush is not None:
-                evict()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
-            ev[0].record(stream)
-            pkg.moe_route_topk(logits, k, wl.renormalize, tw, ti, stream)
-            ev[1].record(stream)
-            pkg.moe_align_block(ti, E, block_m, s_ids, b_exp, npad, stream)
-            ev[2].record(stream)
-            pkg.moe_w8a16_gemm1(x, layer.w13_weight, layer.w13_scale, s_ids, b_exp, npad, block_m, k, a_buf, stream)
-            ev[3].record(stream)
-            pkg.moe_w8a16_requant(a_buf, T, I, E, k, s_ids, npad, block_m, stream)
-            ev[4].record(stream)
-            pkg.moe_w8a16_gemm2(a_buf, T, k, layer.w2_weight, layer.w2_scale, s_ids, b_exp, npad, block_m, splits,
-                                y_buf, stream)
-            ev[5].record(stream)
-            pkg.moe_combine_topk(y_buf, splits, tw, ti, E, out, stream)
-            ev[6].record(stream)
-            torch.cuda.synchronize()
-            if i >= 2:
-                for j, n in enumerate(names):
-                    acc[n].append(ev[j].elapsed_time(ev[j + 1]))
-        stage_ms = {n: float(np.mean(v)) for n, v in acc.items()}
-
-    if stage_ms:
-        dominant = "gemm1"
-        dur_s = stage_ms["gemm1"] / 1e3
-        if T >= 1024:
-            roof = {"bound": "mfma", "achieved": flops_gemm1 / dur_s / 1e12, "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s"}
-        else:
-            roof = {"bound": "hbm", "achieved": bytes_gemm1 / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["kernel"] = gemm1_kernel_name(block_m, H)
-        roof["traffic"] = recorded_traffic(wl.name, T, roof["kernel"])
-        roof["kernel_ms"] = stage_ms["gemm1"]
-    else:
-        dur_s = ms_per_step / 1e3
-        roof = {"bound": "hbm", "achieved": bytes_layer / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": bytes_layer / dur_s / 1e9 / HBM_PEAK_GBS, "traffic": None, "kernel": "whole layer"}
-
-    layer_hbm_frac = bytes_layer / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS
-    layer_mfma_frac = flops_layer / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS
-
-    # ---- CPU oracle on a bounded sample ---------------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, T, xb, logits_np, args, active)
+        cpu = cpu_baseline(wl, T, m["xb"], m["logits_np"], args, m["active"])
 
     res = {
         "metric": "MoE-layer tokens/s",
-        "value": value,
+        "value": m["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "ms_per_step_median": ms_median,
-        "wall_s_timed_region": wall,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -421,15 +453,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "E": E, "top_k": k, "H": H, "I": I,
                    "weights": "uint4 g128 asym" if w4 else "int8 per-channel sym",
-                   "block_m": block_m, "splits": splits, "active_experts": n_active,
-                   "flush_mb_between_steps": flush_mb},
-        "layer": {"algorithmic_bytes": bytes_layer, "algorithmic_flops": flops_layer,
-                  "hbm_frac": layer_hbm_frac, "mfma_frac": layer_mfma_frac},
-        "stage_ms": stage_ms,
-        "roofline": roof,
+                   "block_m": m["block_m"], "splits": m["splits"], "active_experts": m["active_experts"],
+                   "flush_mb_between_steps": m["flush_mb"]},
+        "stage_ms": m["stage_ms"],
+        "layer": {"hbm_frac": m["hbm_frac"], "mfma_frac": m["mfma_frac"]},
+        "prefill": prefill,
+        "roofline": m["roofline"],
         "cpu_baseline": cpu,
     }
-    print(json.dumps(res), flush=True)
+    # compact: the whole line has to survive in a short log tail
+    print(json.dumps(_rnd(res, 4), separators=(",", ":")), flush=True)
 
 
 def gemm1_kernel_name(block_m, H):
@@ -450,11 +483,7 @@ def cpu_baseline(wl, T, xb, logits_np, args, active):
     import oracle
     from weight_quantized_mixture_amd import synthetic
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads, blas = host_blas()
     Ts = args.cpu_sample_tokens or min(T, 64)
     rows = np.linspace(0, T - 1, Ts).astype(int)
     w_ref, ids_ref = oracle.route_softmax_topk(logits_np[rows], wl.k, wl.renormalize)
@@ -485,9 +514,32 @@ def cpu_baseline(wl, T, xb, logits_np, args, active):
     oracle.moe_forward_dense(x, w13_of, w2_of, w_ref, ids_ref, wl.I)
     dt = time.perf_counter() - t1
     return {"value": Ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"{Ts} of the {T} tokens (evenly spaced), routing + fp64 forward with per-expert "
-                      f"dequantization of the {used.size} experts they use; weight quantization not timed"}
+            "seconds": round(dt, 3), "cpu": host_cpu_model(), "blas": blas,
+            "sample": f"{Ts}/{T} tokens: route + fp64 forward, dequant of {used.size} experts"}
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_blas():
+    """(threads, 'vendor version') of the BLAS numpy uses, from threadpoolctl."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            p = libs[0]
+            return int(p.get("num_threads", 1)), f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0)), "unknown"
 
 
 if __name__ == "__main__":
