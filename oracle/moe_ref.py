@@ -126,6 +126,69 @@ def route_softmax_topk(logits: np.ndarray, k: int, renormalize: bool = True):
     return w, ids
 
 
+def route_select(logits: np.ndarray, k: int, renormalize: bool = True, scoring: str = "softmax",
+                 num_expert_group: int = 0, topk_group: int = 0, bias=None,
+                 routed_scaling_factor: float = 1.0):
+    """Routing with the options ``select_experts`` takes on the pages: scoring function,
+    grouped top-k, a score-correction bias and a routed scaling factor.
+
+    experts_int8 page, ``ExpertsInt8MoEMethod.apply`` (``use_grouped_topk``, ``topk_group``,
+    ``num_expert_group``, ``scoring_func``, ``e_score_correction_bias``); moe_wna16 page,
+    ``MoeWNA16Method.apply_monolithic`` (``routed_scaling_factor``).  The bodies are not on the
+    pages; the reading used here, in order:
+
+    1. score s_e: softmax over the E logits, or sigmoid of each logit (fp64).
+    2. choice key c_e: with no bias, the fp32 logit (both scores increase with the logit, so the
+       order is the same and is decided exactly); with a bias, fp32(s_e) + fp32(bias_e) added in
+       fp32 (the score is rounded to fp32 first: the same precision on every side that decides).
+    3. with G = num_expert_group > 1 groups of E/G consecutive experts: a group's key is the
+       largest c_e in it; the topk_group groups with the largest keys (equal keys: lower group
+       id) stay, the experts of the others are out.
+    4. the k experts with the largest c_e among those left, descending, equal keys by lower id.
+    5. weights: the unbiased scores s of the chosen experts, divided by their sum when
+       renormalize, then multiplied by routed_scaling_factor.
+
+    Returns (weights float64 [T, k], ids int32 [T, k]).
+    """
+    l32 = np.asarray(logits, dtype=np.float32)
+    T, E = l32.shape
+    if not 1 <= k <= E:
+        raise ValueError("k must be in [1, E]")
+    l = l32.astype(np.float64)
+    if scoring == "softmax":
+        ex = np.exp(l - np.max(l, axis=1, keepdims=True))
+        s = ex / np.sum(ex, axis=1, keepdims=True)
+    elif scoring == "sigmoid":
+        s = 1.0 / (1.0 + np.exp(-l))
+    else:
+        raise ValueError(f"scoring {scoring!r}")
+    if bias is None:
+        key = l32
+    else:
+        key = (s.astype(np.float32) + np.asarray(bias, np.float32)[None, :]).astype(np.float32)
+    eligible = np.ones((T, E), bool)
+    G = int(num_expert_group)
+    if G > 1:
+        if E % G or not 1 <= topk_group <= G:
+            raise ValueError("E must split into num_expert_group groups and 1 <= topk_group <= groups")
+        if k > topk_group * (E // G):
+            raise ValueError("k is larger than the experts of the kept groups")
+        gkey = key.reshape(T, G, E // G).max(axis=2)
+        keep = np.argsort(-gkey, axis=1, kind="stable")[:, :topk_group]
+        gmask = np.zeros((T, G), bool)
+        np.put_along_axis(gmask, keep, True, axis=1)
+        eligible = np.repeat(gmask, E // G, axis=1)
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        cand = np.nonzero(eligible[t])[0]                         # ascending ids
+        order = np.argsort(-key[t, cand], kind="stable")          # descending key, lower id first
+        ids[t] = cand[order[:k]]
+    w = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    if renormalize:
+        w = w / np.sum(w, axis=1, keepdims=True)
+    return w * float(routed_scaling_factor), ids
+
+
 # ---------------------------------------------------------------------------
 # a3: token -> expert align (histogram, prefix scan, padded-block permutation)
 # ---------------------------------------------------------------------------
