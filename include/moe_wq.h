@@ -88,6 +88,49 @@ int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t k, int ren
                    float* topk_w, int32_t* topk_ids, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Routing options of select_experts (experts_int8 page,
+ * ExpertsInt8MoEMethod.apply: use_grouped_topk, topk_group,
+ * num_expert_group, scoring_func, e_score_correction_bias; moe_wna16 page,
+ * MoeWNA16Method.apply_monolithic: routed_scaling_factor).  The pages show
+ * the options, not the procedure; this library computes, per token:
+ *   1. scores s_e: softmax over the E logits, or sigmoid of each logit
+ *      (computed in fp64);
+ *   2. choice keys: the fp32 logit when e_score_correction_bias is NULL (the
+ *      same order as the scores), else fp32(s_e) + bias_e added in fp32;
+ *   3. num_expert_group = G > 1: E splits into G groups of E/G consecutive
+ *      experts; a group's key is its largest choice key; the topk_group
+ *      groups with the largest keys (equal keys: lower group) keep their
+ *      experts, the others' experts cannot be chosen;
+ *   4. the k largest choice keys among the experts left, in descending
+ *      order, equal keys by lower id;
+ *   5. topk_w = the chosen unbiased s, divided by their sum when
+ *      renormalize != 0, times routed_scaling_factor (fp64, rounded to fp32).
+ * With the defaults (softmax, no groups, no bias, factor 1) this is
+ * moe_route_topk.  A NULL moe_routing pointer means those defaults with
+ * renormalize = 1.
+ * ---------------------------------------------------------------------- */
+enum moe_scoring { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
+typedef struct moe_routing {
+  int scoring;                          /* MOE_SCORING_SOFTMAX or MOE_SCORING_SIGMOID           */
+  int renormalize;                      /* divide the chosen scores by their sum                 */
+  int64_t num_expert_group;             /* G: 0 or 1 = no groups; else G <= 64, E % G == 0      */
+  int64_t topk_group;                   /* groups kept, 1 <= topk_group <= G (ignored if G < 2)  */
+  const float* e_score_correction_bias; /* device fp32 [E] or NULL                               */
+  float routed_scaling_factor;          /* multiplies the weights (finite)                       */
+} moe_routing;
+
+/* moe_route_select: the routing above.
+ *   logits   device fp32  [T, E]
+ *   topk_w   device fp32  [T, k]  (written)
+ *   topk_ids device int32 [T, k]  (written)
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null pointer with T > 0, E < 1, k < 1,
+ * k > E, T < 0, unknown scoring, G not dividing E, topk_group outside
+ * [1, G], k above topk_group * E / G, non-finite factor);
+ * MOE_ERR_UNSUPPORTED if E > 1024 or G > 64.  T = 0 launches nothing. */
+int moe_route_select(const float* logits, int64_t T, int64_t E, int64_t k, const moe_routing* routing,
+                     float* topk_w, int32_t* topk_ids, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * a3. Token -> expert align: histogram, prefix scan, padded-block permutation.
  * The pages call the fused kernel that consumes this grouping without
  * printing it (experts_int8 page, ExpertsInt8MoEMethod.apply).  Definition:

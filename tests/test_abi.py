@@ -234,3 +234,19 @@ def test_binding_align_checks():
         B._need_align(T, k, E, 0, *good)
     with pytest.raises(ValueError, match="sorted_ids must be a device tensor"):
         B._need_align(T, k, E, bm, *good)
+
+
+def test_route_select_argument_errors():
+    L = pkg.lib()
+    p = ctypes.c_void_p(FAKE)
+    for fields, want in [((0, 1, 3, 1, None, 1.0), B.MOE_ERR_INVALID_ARGUMENT),      # 3 does not divide 8
+                         ((0, 1, 4, 0, None, 1.0), B.MOE_ERR_INVALID_ARGUMENT),      # topk_group 0
+                         ((0, 1, 4, 1, None, 1.0), B.MOE_ERR_INVALID_ARGUMENT),      # k=3 > 1 group of 2
+                         ((2, 1, 0, 0, None, 1.0), B.MOE_ERR_INVALID_ARGUMENT),      # unknown scoring
+                         ((1, 1, 0, 0, None, float("nan")), B.MOE_ERR_INVALID_ARGUMENT),
+                         ((1, 1, 128, 1, None, 1.0), B.MOE_ERR_UNSUPPORTED)]:        # more than 64 groups
+        r = B.MoeRouting(*fields)
+        E = 256 if fields[2] == 128 else 8
+        assert L.moe_route_select(p, 4, E, 3, ctypes.byref(r), p, p, None) == want, fields
+    assert L.moe_route_select(None, 0, 8, 2, None, None, None, None) == B.MOE_OK          # T = 0
+    assert L.moe_route_select(None, 4, 8, 2, None, None, None, None) == B.MOE_ERR_INVALID_ARGUMENT

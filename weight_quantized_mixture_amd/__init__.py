@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     moe_combine_topk,
     moe_quantize_weights_int8,
     moe_quantize_weights_w4,
+    moe_route_select,
     moe_route_topk,
     moe_w4a16_apply,
     moe_w4a16_forward,

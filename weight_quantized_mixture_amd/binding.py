@@ -33,6 +33,7 @@ SIGNATURES = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_quantize_weights_int8": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "moe_route_topk": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_p]),
+    "moe_route_select": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "moe_align_capacity": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "moe_align_block": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "moe_w8a16_block_m": (_c_i64, [_c_i64] * 5),
@@ -64,6 +65,15 @@ SIGNATURES = {
                                    _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                    _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
 }
+
+class MoeRouting(ctypes.Structure):
+    """struct moe_routing of moe_wq.h (routing options of select_experts)."""
+    _fields_ = [("scoring", ctypes.c_int), ("renormalize", ctypes.c_int), ("num_expert_group", ctypes.c_int64),
+                ("topk_group", ctypes.c_int64), ("e_score_correction_bias", ctypes.c_void_p),
+                ("routed_scaling_factor", ctypes.c_float)]
+
+
+MOE_SCORING = {"softmax": 0, "sigmoid": 1}
 
 _lib = None
 
@@ -189,6 +199,32 @@ def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool, topk_w: torc
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
     _check(lib().moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(topk_w),
                                 _ptr(topk_ids), _stream(stream)), "moe_route_topk")
+
+
+def routing_struct(E: int, renormalize: bool = True, scoring: str = "softmax", num_expert_group: int = 0,
+                   topk_group: int = 0, e_score_correction_bias=None, routed_scaling_factor: float = 1.0):
+    """A MoeRouting for the C calls; the bias (fp32 [E] device tensor) must stay alive while it is used."""
+    if scoring not in MOE_SCORING:
+        raise ValueError(f"scoring must be one of {sorted(MOE_SCORING)}, got {scoring!r}")
+    if e_score_correction_bias is not None:
+        _need(e_score_correction_bias, torch.float32, (E,), "e_score_correction_bias")
+    return MoeRouting(MOE_SCORING[scoring], int(bool(renormalize)), int(num_expert_group), int(topk_group),
+                      None if e_score_correction_bias is None else e_score_correction_bias.data_ptr(),
+                      float(routed_scaling_factor))
+
+
+def moe_route_select(logits: torch.Tensor, k: int, topk_w: torch.Tensor, topk_ids: torch.Tensor,
+                     renormalize: bool = True, scoring: str = "softmax", num_expert_group: int = 0,
+                     topk_group: int = 0, e_score_correction_bias=None, routed_scaling_factor: float = 1.0,
+                     stream=None):
+    T, E = logits.shape
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    r = routing_struct(E, renormalize, scoring, num_expert_group, topk_group, e_score_correction_bias,
+                       routed_scaling_factor)
+    _check(lib().moe_route_select(_ptr(logits), T, E, k, ctypes.byref(r), _ptr(topk_w), _ptr(topk_ids),
+                                  _stream(stream)), "moe_route_select")
 
 
 def moe_align_capacity(T: int, k: int, E: int, block_m: int) -> int:

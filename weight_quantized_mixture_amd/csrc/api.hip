@@ -290,6 +290,46 @@ int check_act(int act) {
 }
 
 
+// Checks of the routing options (moe_route_select); a NULL pointer is the default routing.
+int check_routing(int64_t T, int64_t E, int64_t k, const moe_routing* r) {
+  if (T < 0 || E < 1 || k < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "need T >= 0, E >= 1, k >= 1");
+  if (k > E) return fail(MOE_ERR_INVALID_ARGUMENT, "k (%lld) > E (%lld)", (long long)k, (long long)E);
+  if (E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "E > %lld", (long long)kMaxExperts);
+  if (!r) return MOE_OK;
+  if (r->scoring != MOE_SCORING_SOFTMAX && r->scoring != MOE_SCORING_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown scoring %d", r->scoring);
+  if (!std::isfinite(r->routed_scaling_factor))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "routed_scaling_factor must be finite");
+  const int64_t G = r->num_expert_group;
+  if (G < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_expert_group must be >= 0");
+  if (G > 1) {
+    if (G > 64) return fail(MOE_ERR_UNSUPPORTED, "num_expert_group above 64");
+    if (E % G) return fail(MOE_ERR_INVALID_ARGUMENT, "num_expert_group %lld does not divide E %lld", (long long)G,
+                           (long long)E);
+    if (r->topk_group < 1 || r->topk_group > G)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "topk_group must be in [1, num_expert_group]");
+    if (k > r->topk_group * (E / G))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "k exceeds the experts of the kept groups");
+  }
+  return MOE_OK;
+}
+
+bool default_routing(const moe_routing* r) {
+  return !r || (r->scoring == MOE_SCORING_SOFTMAX && r->num_expert_group <= 1 && !r->e_score_correction_bias &&
+                r->routed_scaling_factor == 1.0f);
+}
+
+hipError_t launch_routing(const float* logits, int64_t T, int64_t E, int64_t k, const moe_routing* r, float* tw,
+                          int32_t* ti, hipStream_t stream) {
+  if (default_routing(r))
+    return moe::launch_route(logits, T, static_cast<int>(E), static_cast<int>(k), r ? r->renormalize : 1, tw, ti,
+                             stream);
+  const int G = r->num_expert_group > 1 ? static_cast<int>(r->num_expert_group) : 0;
+  return moe::launch_route_select(logits, T, static_cast<int>(E), static_cast<int>(k), r->renormalize,
+                                  r->scoring == MOE_SCORING_SIGMOID, G, G ? static_cast<int>(r->topk_group) : 0,
+                                  r->e_score_correction_bias, r->routed_scaling_factor, tw, ti, stream);
+}
+
 // Routing (when logits are given) and align.  Up to 8 tokens (one per wave)
 // one workgroup does both and saves a launch; larger batches route with one
 // wave per token across the chip, then align.
@@ -342,6 +382,15 @@ int moe_route_topk(const float* logits, int64_t T, int64_t E, int64_t k, int ren
   return hip_status(moe::launch_route(logits, T, static_cast<int>(E), static_cast<int>(k),
                                       renormalize, topk_w, topk_ids, stream),
                     "route_topk");
+}
+
+int moe_route_select(const float* logits, int64_t T, int64_t E, int64_t k, const moe_routing* routing,
+                     float* topk_w, int32_t* topk_ids, hipStream_t stream) {
+  int st;
+  if ((st = check_routing(T, E, k, routing)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!logits || !topk_w || !topk_ids) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(launch_routing(logits, T, E, k, routing, topk_w, topk_ids, stream), "route_select");
 }
 
 int64_t moe_align_capacity(int64_t T, int64_t k, int64_t E, int64_t block_m) {

@@ -19,6 +19,12 @@ hipError_t launch_quantize_w4(const float* w, int64_t E, int64_t N, int64_t K, i
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int renormalize,
                         float* topk_w, int32_t* topk_ids, hipStream_t stream);
 
+// Routing with scoring function, grouped top-k, correction bias and scaling factor, one wave per token
+// (E <= 1024; G <= 64 groups dividing E when G > 1).
+hipError_t launch_route_select(const float* logits, int64_t T, int E, int k, int renormalize, int sigmoid, int G,
+                               int topk_group, const float* bias, float scale, float* topk_w, int32_t* topk_ids,
+                               hipStream_t stream);
+
 // Routing followed by the padded-block align in one workgroup (small batches).
 hipError_t launch_route_align(const float* logits, int64_t T, int E, int k, int renormalize, float* topk_w,
                               int32_t* topk_ids, int block_m, int64_t cap, int32_t* sorted_ids,
