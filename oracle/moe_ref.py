@@ -263,7 +263,7 @@ def silu(g: np.ndarray) -> np.ndarray:
 
 
 def moe_forward_dense(x: np.ndarray, w13_of, w2_of, topk_w: np.ndarray, topk_ids: np.ndarray,
-                      I: int) -> np.ndarray:
+                      I: int, weight_on_input: bool = False) -> np.ndarray:
     """Routed MoE layer with dense fp64 expert weights.
 
     experts_int8 page, ``ExpertsInt8MoEMethod.apply`` and ``create_weights``: for
@@ -271,8 +271,10 @@ def moe_forward_dense(x: np.ndarray, w13_of, w2_of, topk_w: np.ndarray, topk_ids
     h = W13[e] x_t (rows 0..I-1 are the gate projection, rows I..2I-1 the up
     projection, ``quantizing_weight_loader``), a = silu(h_gate) * h_up,
     y = W2[e] a, and out_t = sum_j topk_w[t, j] * y (the routing weight multiplies
-    the expert output: ``apply_router_weight_on_input=False``).  Ids outside
-    [0, E) contribute nothing.
+    the expert output: ``apply_router_weight_on_input=False``).  With
+    ``weight_on_input`` (``apply_router_weight_on_input=True``) the weight
+    multiplies the expert's input instead: out_t = sum_j FFN_e(topk_w[t, j] * x_t).
+    Ids outside [0, E) contribute nothing.
 
     x: float64 [T, H]; w13_of(e) -> float64 [2I, H]; w2_of(e) -> float64 [H, I].
     Returns float64 [T, H].
@@ -291,18 +293,48 @@ def moe_forward_dense(x: np.ndarray, w13_of, w2_of, topk_w: np.ndarray, topk_ids
         W2 = w2_of(e)
         if W13 is None or W2 is None:      # expert not present (id out of range)
             continue
-        hmat = x[t_idx] @ W13.T            # [n, 2I]
+        wt = w[t_idx, j_idx][:, None]
+        xin = wt * x[t_idx] if weight_on_input else x[t_idx]
+        hmat = xin @ W13.T                 # [n, 2I]
         a = silu(hmat[:, :I]) * hmat[:, I:]
         y = a @ W2.T                       # [n, H]
-        np.add.at(out, t_idx, w[t_idx, j_idx][:, None] * y)
+        np.add.at(out, t_idx, y if weight_on_input else wt * y)
     return out
 
 
+def with_shared_experts(topk_w: np.ndarray, topk_ids: np.ndarray, E: int, num_shared: int):
+    """Routing extended by shared experts.
+
+    moe_wna16 page, ``MoeWNA16Method.apply`` (``shared_experts``, ``shared_experts_input``): the
+    shared experts' output is added to the routed experts' output for every token.  Reading: the
+    S shared experts are gated MLPs of the routed experts' shape, stored after them (expert slots
+    E .. E+S-1), that every token takes with weight 1 (a shared MLP of intermediate size S*I is
+    S such experts, its intermediate split in S consecutive parts).  Returns the [T, k+S] weights
+    and ids to pass to the forward.
+    """
+    T, k = np.asarray(topk_ids).shape
+    ids = np.concatenate([np.asarray(topk_ids, np.int64),
+                          np.broadcast_to(np.arange(E, E + num_shared, dtype=np.int64), (T, num_shared))], axis=1)
+    w = np.concatenate([np.asarray(topk_w, np.float64), np.ones((T, num_shared))], axis=1)
+    return w, ids.astype(np.int32)
+
+
 def moe_forward_w8(x: np.ndarray, q13: np.ndarray, s13: np.ndarray, q2: np.ndarray, s2: np.ndarray,
-                   topk_w: np.ndarray, topk_ids: np.ndarray) -> np.ndarray:
-    """The W8A16 layer: dequantize each used expert exactly in fp64 (W = q*s), then ``moe_forward_dense``."""
+                   topk_w: np.ndarray, topk_ids: np.ndarray, weight_on_input: bool = False,
+                   num_shared: int = 0) -> np.ndarray:
+    """The W8A16 layer: dequantize each used expert exactly in fp64 (W = q*s), then ``moe_forward_dense``.
+
+    The weight tensors hold the routed experts and, after them, ``num_shared`` shared experts
+    (``with_shared_experts``); topk_ids index the routed ones.  With shared experts and
+    ``weight_on_input`` the shared experts take the input unscaled (weight 1)."""
     E = q13.shape[0]
     I = q13.shape[1] // 2
+    if num_shared:
+        topk_w, topk_ids = with_shared_experts(topk_w, topk_ids, E - num_shared, num_shared)
+        # ids past the routed range that the router could not give are dropped as usual
+        routed = np.asarray(topk_ids)[:, :-num_shared]
+        topk_ids = np.concatenate([np.where((routed >= 0) & (routed < E - num_shared), routed, -1),
+                                   np.asarray(topk_ids)[:, -num_shared:]], axis=1).astype(np.int32)
 
     def w13_of(e):
         return dequant_int8_rows(q13[e], s13[e]) if 0 <= e < E else None
@@ -310,7 +342,7 @@ def moe_forward_w8(x: np.ndarray, q13: np.ndarray, s13: np.ndarray, q2: np.ndarr
     def w2_of(e):
         return dequant_int8_rows(q2[e], s2[e]) if 0 <= e < E else None
 
-    return moe_forward_dense(x, w13_of, w2_of, topk_w, topk_ids, I)
+    return moe_forward_dense(x, w13_of, w2_of, topk_w, topk_ids, I, weight_on_input)
 
 
 def moe_expert_intermediate(x: np.ndarray, W13: np.ndarray, I: int) -> np.ndarray:

@@ -115,3 +115,68 @@ def test_tolerance_helper():
     assert ok
     ok, d = oracle.layer_within_tolerance(ref + np.array([0.0, 0.0, 0.0011, 0.0]), ref)
     assert not ok and d["n_bad"] == 1
+
+
+def _golden():
+    g = json.load(open(os.path.join(GOLD, "layer_handworked.json")))
+    return g, np.array(g["x"]), np.array(g["q13"], np.int8), np.array(g["s13"], np.float32), \
+        np.array(g["q2"], np.int8), np.array(g["s2"], np.float32)
+
+
+def test_weight_on_input_handworked():
+    """experts_int8 page, apply(apply_router_weight_on_input): the weight scales the expert input."""
+    g, x, q13, s13, q2, s2 = _golden()
+    out = oracle.moe_forward_w8(x, q13, s13, q2, s2, np.array(g["topk_w"]), np.array(g["topk_ids"]),
+                                weight_on_input=True)
+    np.testing.assert_allclose(out, g["weight_on_input"]["out"], rtol=1e-15, atol=1e-16)
+
+
+def test_shared_experts_handworked():
+    """moe_wna16 page, MoeWNA16Method.apply(shared_experts): shared experts added for every token."""
+    g, x, q13, s13, q2, s2 = _golden()
+    sh = g["shared"]
+    out = oracle.moe_forward_w8(x, q13, s13, q2, s2, np.array(sh["topk_w"]), np.array(sh["topk_ids"]),
+                                num_shared=sh["num_shared"])
+    np.testing.assert_allclose(out, sh["out"], rtol=1e-15, atol=1e-16)
+
+
+def test_weight_on_input_is_the_scaled_input_through_a_gated_mlp():
+    x, q13, s13, q2, s2, w, ids = _tiny_layer(seed=8)
+    ones = np.ones_like(w)
+    np.testing.assert_allclose(oracle.moe_forward_w8(x, q13, s13, q2, s2, ones, ids, weight_on_input=True),
+                               oracle.moe_forward_w8(x, q13, s13, q2, s2, ones, ids), rtol=1e-14, atol=1e-16)
+    # token by token: sum_j MLP_e(w x) with torch's silu on the dequantized expert
+    out = oracle.moe_forward_w8(x, q13, s13, q2, s2, w, ids, weight_on_input=True)
+    I = q13.shape[1] // 2
+    for t in range(x.shape[0]):
+        acc = torch.zeros(x.shape[1], dtype=torch.float64)
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            W1 = torch.from_numpy(q13[e, :I].astype(np.float64) * s13[e, :I, None])
+            W3 = torch.from_numpy(q13[e, I:].astype(np.float64) * s13[e, I:, None])
+            W2 = torch.from_numpy(q2[e].astype(np.float64) * s2[e, :, None])
+            xi = torch.from_numpy(w[t, j] * x[t])
+            acc += (torch.nn.functional.silu(W1 @ xi) * (W3 @ xi)) @ W2.T
+        np.testing.assert_allclose(out[t], acc.numpy(), rtol=1e-12, atol=1e-15)
+    # the weight is not linear through the layer: scaling the output instead differs
+    assert np.abs(out - oracle.moe_forward_w8(x, q13, s13, q2, s2, w, ids)).max() > 1e-4 * np.abs(out).max()
+
+
+def test_shared_experts_add_a_gated_mlp_for_every_token():
+    x, q13, s13, q2, s2, w, ids = _tiny_layer(E=5, seed=9)
+    E_routed = 4
+    ids = np.where(ids < E_routed, ids, 0).astype(np.int32)
+    routed = oracle.moe_forward_w8(x, q13[:E_routed], s13[:E_routed], q2[:E_routed], s2[:E_routed], w, ids)
+    out = oracle.moe_forward_w8(x, q13, s13, q2, s2, w, ids, num_shared=1)
+    I = q13.shape[1] // 2
+    W1 = torch.from_numpy(q13[4, :I].astype(np.float64) * s13[4, :I, None])
+    W3 = torch.from_numpy(q13[4, I:].astype(np.float64) * s13[4, I:, None])
+    W2 = torch.from_numpy(q2[4].astype(np.float64) * s2[4, :, None])
+    X = torch.from_numpy(x)
+    shared = ((torch.nn.functional.silu(X @ W1.T) * (X @ W3.T)) @ W2.T).numpy()
+    np.testing.assert_allclose(out, routed + shared, rtol=1e-12, atol=1e-15)
+    # with weight on input the shared expert still takes the unscaled input
+    out_i = oracle.moe_forward_w8(x, q13, s13, q2, s2, w, ids, weight_on_input=True, num_shared=1)
+    routed_i = oracle.moe_forward_w8(x, q13[:E_routed], s13[:E_routed], q2[:E_routed], s2[:E_routed], w, ids,
+                                     weight_on_input=True)
+    np.testing.assert_allclose(out_i, routed_i + shared, rtol=1e-12, atol=1e-15)
