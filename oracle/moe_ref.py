@@ -319,6 +319,16 @@ def with_shared_experts(topk_w: np.ndarray, topk_ids: np.ndarray, E: int, num_sh
     return w, ids.astype(np.int32)
 
 
+def _extend_routing(topk_w, topk_ids, E_total: int, num_shared: int):
+    """Routing over weight tensors of E_total experts whose last num_shared are shared experts:
+    routed ids outside the routed range are dropped (id -1), the shared experts appended."""
+    if not num_shared:
+        return topk_w, topk_ids
+    routed = np.asarray(topk_ids)
+    routed = np.where((routed >= 0) & (routed < E_total - num_shared), routed, -1)
+    return with_shared_experts(topk_w, routed, E_total - num_shared, num_shared)
+
+
 def moe_forward_w8(x: np.ndarray, q13: np.ndarray, s13: np.ndarray, q2: np.ndarray, s2: np.ndarray,
                    topk_w: np.ndarray, topk_ids: np.ndarray, weight_on_input: bool = False,
                    num_shared: int = 0) -> np.ndarray:
@@ -329,12 +339,7 @@ def moe_forward_w8(x: np.ndarray, q13: np.ndarray, s13: np.ndarray, q2: np.ndarr
     ``weight_on_input`` the shared experts take the input unscaled (weight 1)."""
     E = q13.shape[0]
     I = q13.shape[1] // 2
-    if num_shared:
-        topk_w, topk_ids = with_shared_experts(topk_w, topk_ids, E - num_shared, num_shared)
-        # ids past the routed range that the router could not give are dropped as usual
-        routed = np.asarray(topk_ids)[:, :-num_shared]
-        topk_ids = np.concatenate([np.where((routed >= 0) & (routed < E - num_shared), routed, -1),
-                                   np.asarray(topk_ids)[:, -num_shared:]], axis=1).astype(np.int32)
+    topk_w, topk_ids = _extend_routing(topk_w, topk_ids, E, num_shared)
 
     def w13_of(e):
         return dequant_int8_rows(q13[e], s13[e]) if 0 <= e < E else None
@@ -450,10 +455,13 @@ def dequant_w4(qweight: np.ndarray, scales: np.ndarray, qzeros: np.ndarray, grou
 
 
 def moe_forward_w4(x: np.ndarray, qw13, s13, z13, qw2, s2, z2, group_size: int,
-                   topk_w: np.ndarray, topk_ids: np.ndarray) -> np.ndarray:
-    """The W4A16 layer: per used expert, dense fp64 dequantization, then ``moe_forward_dense``."""
+                   topk_w: np.ndarray, topk_ids: np.ndarray, weight_on_input: bool = False,
+                   num_shared: int = 0) -> np.ndarray:
+    """The W4A16 layer: per used expert, dense fp64 dequantization, then ``moe_forward_dense``
+    (options as ``moe_forward_w8``)."""
     E = qw13.shape[0]
     I = qw13.shape[1] // 2
+    topk_w, topk_ids = _extend_routing(topk_w, topk_ids, E, num_shared)
 
     def w13_of(e):
         return dequant_w4(qw13[e], s13[e], z13[e], group_size) if 0 <= e < E else None
@@ -461,7 +469,7 @@ def moe_forward_w4(x: np.ndarray, qw13, s13, z13, qw2, s2, z2, group_size: int,
     def w2_of(e):
         return dequant_w4(qw2[e], s2[e], z2[e], group_size) if 0 <= e < E else None
 
-    return moe_forward_dense(x, w13_of, w2_of, topk_w, topk_ids, I)
+    return moe_forward_dense(x, w13_of, w2_of, topk_w, topk_ids, I, weight_on_input)
 
 
 # ---------------------------------------------------------------------------

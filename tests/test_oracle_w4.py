@@ -83,3 +83,14 @@ def test_w4_forward_equals_dense_forward():
     D2 = (q2.astype(np.float64) - np.repeat(z2, g, -1)) * np.repeat(s2.astype(np.float64), g, -1)
     ref = oracle.moe_forward_dense(x, lambda e: D13[e], lambda e: D2[e], w, ids, I)
     np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-16)
+    # options: shared expert (the last one) and the routing weight on the input
+    ids_r = np.where(ids < E - 1, ids, 0).astype(np.int32)
+    for woi in (False, True):
+        out = oracle.moe_forward_w4(x, P13, s13, Z13, P2, s2, Z2, g, w, ids_r, weight_on_input=woi, num_shared=1)
+        we, ie = oracle.with_shared_experts(w, ids_r, E - 1, 1)
+        ref = oracle.moe_forward_dense(x, lambda e: D13[e], lambda e: D2[e], we, ie, I, weight_on_input=woi)
+        np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-16)
+        if woi:
+            we[:, -1] = 1.0
+            ref2 = oracle.moe_forward_dense(x, lambda e: D13[e], lambda e: D2[e], we, ie, I, weight_on_input=True)
+            np.testing.assert_allclose(out, ref2, rtol=1e-14, atol=1e-16)
