@@ -187,6 +187,43 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Options of fused_experts / apply beyond the defaults.
+ *   apply_router_weight_on_input (experts_int8 page, ExpertsInt8MoEMethod.apply
+ *     -> fused_experts): != 0 scales each assignment's input by its routing
+ *     weight instead of the output: out_t = sum_j FFN_e(w[t,j] * x_t), with
+ *     w * x rounded to the activation type.
+ *   num_shared_experts (moe_wna16 page, MoeWNA16Method.apply: shared_experts,
+ *     whose output is added to the routed output): S gated MLPs of the routed
+ *     experts' shape stored after the E routed ones in every weight tensor
+ *     (tensors of E + S experts), taken by every token with weight 1 (a
+ *     shared MLP of intermediate S * I is S such experts).  topk_ids still
+ *     index the E routed experts; routed ids outside [0, E) are dropped.
+ * A NULL pointer means both off.  The _ex calls below take these options;
+ * their workspace is moe_*_workspace_bytes_ex(..., opts).
+ * ---------------------------------------------------------------------- */
+typedef struct moe_fused_opts {
+  int apply_router_weight_on_input;
+  int64_t num_shared_experts;
+} moe_fused_opts;
+
+size_t moe_w8a16_workspace_bytes_ex(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
+                                    const moe_fused_opts* opts);
+/* moe_w8a16_forward with the options (weights [E + S, ...], topk [T, k] of routed experts). */
+int moe_w8a16_forward_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                         const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                         const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                         const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* opts,
+                         int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+/* moe_w8a16_apply with routing options (moe_route_select) and the options above. */
+int moe_w8a16_apply_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                       const float* router_logits, const moe_routing* routing,
+                       const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                       const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                       const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids, int64_t block_m,
+                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * moe_w8a16_forward without allocation, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc) nor provide a workspace.
@@ -338,6 +375,23 @@ int moe_w4a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
                     const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros,
                     int64_t group_size, float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t moe_w4a16_workspace_bytes_ex(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
+                                    const moe_fused_opts* opts);
+/* moe_w4a16_forward / moe_w4a16_apply with the options (see moe_fused_opts, moe_routing). */
+int moe_w4a16_forward_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                         const int32_t* w13_qweight, const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                         const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros,
+                         int64_t group_size, const float* topk_w, const int32_t* topk_ids,
+                         const moe_fused_opts* opts, int64_t block_m, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+int moe_w4a16_apply_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                       const float* router_logits, const moe_routing* routing,
+                       const int32_t* w13_qweight, const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                       const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros,
+                       int64_t group_size, const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids,
+                       int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

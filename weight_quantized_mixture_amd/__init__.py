@@ -17,6 +17,12 @@ from .binding import (  # noqa: F401
     moe_route_select,
     moe_route_topk,
     moe_w4a16_apply,
+    moe_w4a16_apply_ex,
+    moe_w4a16_forward_ex,
+    moe_w4a16_workspace_bytes_ex,
+    moe_w8a16_apply_ex,
+    moe_w8a16_forward_ex,
+    moe_w8a16_workspace_bytes_ex,
     moe_w4a16_forward,
     moe_w4a16_workspace_bytes,
     moe_w8a16_apply,

@@ -51,6 +51,20 @@ SIGNATURES = {
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_w8a16_splits": (_c_i64, [_c_i64] * 6),
+    "moe_w8a16_workspace_bytes_ex": (_c_size, [_c_i64] * 6 + [_c_p]),
+    "moe_w4a16_workspace_bytes_ex": (_c_size, [_c_i64] * 6 + [_c_p]),
+    "moe_w8a16_forward_ex": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                      _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                      _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_w8a16_apply_ex": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
+                                    _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                    _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_w4a16_forward_ex": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                      _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                      _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_w4a16_apply_ex": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
+                                    _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                    _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_w8a16_intermediate_bytes": (_c_size, [_c_i64] * 6),
     "moe_w8a16_requant": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p]),
     "moe_w8a16_gemm1": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
@@ -74,6 +88,11 @@ class MoeRouting(ctypes.Structure):
 
 
 MOE_SCORING = {"softmax": 0, "sigmoid": 1}
+
+
+class MoeFusedOpts(ctypes.Structure):
+    """struct moe_fused_opts of moe_wq.h (apply_router_weight_on_input, shared experts)."""
+    _fields_ = [("apply_router_weight_on_input", ctypes.c_int), ("num_shared_experts", ctypes.c_int64)]
 
 _lib = None
 
@@ -441,3 +460,136 @@ def moe_w4a16_apply(x, router_logits, renormalize, w13_qweight, w13_scales, w13_
                                  _ptr(w2_scales), _ptr(w2_qzeros), group_size, _ptr(topk_w), _ptr(topk_ids),
                                  block_m, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)), "moe_w4a16_apply")
+
+
+# ---------------------------------------------------------------------------
+# Layer calls with routing options (moe_routing) and fused options (moe_fused_opts)
+# ---------------------------------------------------------------------------
+
+
+def fused_opts(num_shared_experts: int = 0, apply_router_weight_on_input: bool = False) -> MoeFusedOpts:
+    return MoeFusedOpts(int(bool(apply_router_weight_on_input)), int(num_shared_experts))
+
+
+def moe_w8a16_workspace_bytes_ex(T, H, I, E, k, block_m=0, num_shared_experts=0,
+                                 apply_router_weight_on_input=False) -> int:
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    return int(lib().moe_w8a16_workspace_bytes_ex(T, H, I, E, k, block_m, ctypes.byref(o)))
+
+
+def moe_w4a16_workspace_bytes_ex(T, H, I, E, k, block_m=0, num_shared_experts=0,
+                                 apply_router_weight_on_input=False) -> int:
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    return int(lib().moe_w4a16_workspace_bytes_ex(T, H, I, E, k, block_m, ctypes.byref(o)))
+
+
+def _w8_checked(x, w13, w13_scale, w2, w2_scale, S):
+    T, H, act = _need_act(x)
+    Et, N2, _ = w13.shape
+    I = N2 // 2
+    if S < 0 or S >= Et:
+        raise ValueError(f"num_shared_experts {S} must be in [0, {Et})")
+    ld13 = _row_stride(w13, torch.int8, (Et, 2 * I, H), "w13")
+    _need(w13_scale, torch.float32, (Et, 2 * I), "w13_scale")
+    ld2 = _row_stride(w2, torch.int8, (Et, H, I), "w2")
+    _need(w2_scale, torch.float32, (Et, H), "w2_scale")
+    return T, H, I, Et - S, act, ld13, ld2
+
+
+def moe_w8a16_forward_ex(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, workspace, num_shared_experts=0,
+                         apply_router_weight_on_input=False, block_m: int = 0, stream=None):
+    """moe_w8a16_forward with shared experts (the last `num_shared_experts` of the weight tensors) and
+    the routing weight optionally applied to the input; topk_ids index the routed experts."""
+    T, H, I, E, act, ld13, ld2 = _w8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
+    k = topk_ids.shape[1]
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    _need_bytes(workspace, moe_w8a16_workspace_bytes_ex(T, H, I, E, k, block_m, num_shared_experts,
+                                                        apply_router_weight_on_input), "workspace")
+    _check(lib().moe_w8a16_forward_ex(_ptr(x), act, T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13, _ptr(w2),
+                                      _ptr(w2_scale), ld2, _ptr(topk_w), _ptr(topk_ids), ctypes.byref(o), block_m,
+                                      _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "moe_w8a16_forward_ex")
+
+
+def moe_w8a16_apply_ex(x, router_logits, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, workspace,
+                       renormalize=True, scoring="softmax", num_expert_group=0, topk_group=0,
+                       e_score_correction_bias=None, routed_scaling_factor=1.0, num_shared_experts=0,
+                       apply_router_weight_on_input=False, block_m: int = 0, stream=None):
+    """Route from logits with the select_experts options, then the layer with the fused options."""
+    T, H, I, E, act, ld13, ld2 = _w8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
+    k = topk_ids.shape[1]
+    _need(router_logits, torch.float32, (T, E), "router_logits")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    r = routing_struct(E, renormalize, scoring, num_expert_group, topk_group, e_score_correction_bias,
+                       routed_scaling_factor)
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    _need_bytes(workspace, moe_w8a16_workspace_bytes_ex(T, H, I, E, k, block_m, num_shared_experts,
+                                                        apply_router_weight_on_input), "workspace")
+    _check(lib().moe_w8a16_apply_ex(_ptr(x), act, T, H, I, E, k, _ptr(router_logits), ctypes.byref(r), _ptr(w13),
+                                    _ptr(w13_scale), ld13, _ptr(w2), _ptr(w2_scale), ld2, ctypes.byref(o),
+                                    _ptr(topk_w), _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_w8a16_apply_ex")
+
+
+def _w4_checked(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales, w2_qzeros, group_size, S):
+    T, H, act = _need_act(x)
+    Et, N2, _ = w13_qweight.shape
+    I = N2 // 2
+    if S < 0 or S >= Et:
+        raise ValueError(f"num_shared_experts {S} must be in [0, {Et})")
+    _need(w13_qweight, torch.int32, (Et, 2 * I, H // 8), "w13_qweight")
+    _need(w13_scales, torch.float16, (Et, 2 * I, H // group_size), "w13_scales")
+    _need(w13_qzeros, torch.int32, (Et, 2 * I // 8, H // group_size), "w13_qzeros")
+    _need(w2_qweight, torch.int32, (Et, H, I // 8), "w2_qweight")
+    _need(w2_scales, torch.float16, (Et, H, I // group_size), "w2_scales")
+    _need(w2_qzeros, torch.int32, (Et, H // 8, I // group_size), "w2_qzeros")
+    return T, H, I, Et - S, act
+
+
+def moe_w4a16_forward_ex(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales, w2_qzeros, group_size,
+                         topk_w, topk_ids, out, workspace, num_shared_experts=0, apply_router_weight_on_input=False,
+                         block_m: int = 0, stream=None):
+    T, H, I, E, act = _w4_checked(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales, w2_qzeros,
+                                  group_size, num_shared_experts)
+    k = topk_ids.shape[1]
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    _need_bytes(workspace, moe_w4a16_workspace_bytes_ex(T, H, I, E, k, block_m, num_shared_experts,
+                                                        apply_router_weight_on_input), "workspace")
+    _check(lib().moe_w4a16_forward_ex(_ptr(x), act, T, H, I, E, k, _ptr(w13_qweight), _ptr(w13_scales),
+                                      _ptr(w13_qzeros), _ptr(w2_qweight), _ptr(w2_scales), _ptr(w2_qzeros),
+                                      group_size, _ptr(topk_w), _ptr(topk_ids), ctypes.byref(o), block_m, _ptr(out),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "moe_w4a16_forward_ex")
+
+
+def moe_w4a16_apply_ex(x, router_logits, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales, w2_qzeros,
+                       group_size, topk_w, topk_ids, out, workspace, renormalize=True, scoring="softmax",
+                       num_expert_group=0, topk_group=0, e_score_correction_bias=None, routed_scaling_factor=1.0,
+                       num_shared_experts=0, apply_router_weight_on_input=False, block_m: int = 0, stream=None):
+    T, H, I, E, act = _w4_checked(x, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales, w2_qzeros,
+                                  group_size, num_shared_experts)
+    k = topk_ids.shape[1]
+    _need(router_logits, torch.float32, (T, E), "router_logits")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    r = routing_struct(E, renormalize, scoring, num_expert_group, topk_group, e_score_correction_bias,
+                       routed_scaling_factor)
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    _need_bytes(workspace, moe_w4a16_workspace_bytes_ex(T, H, I, E, k, block_m, num_shared_experts,
+                                                        apply_router_weight_on_input), "workspace")
+    _check(lib().moe_w4a16_apply_ex(_ptr(x), act, T, H, I, E, k, _ptr(router_logits), ctypes.byref(r),
+                                    _ptr(w13_qweight), _ptr(w13_scales), _ptr(w13_qzeros), _ptr(w2_qweight),
+                                    _ptr(w2_scales), _ptr(w2_qzeros), group_size, ctypes.byref(o), _ptr(topk_w),
+                                    _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_w4a16_apply_ex")

@@ -241,23 +241,37 @@ hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, h
   return moe::launch_gemm2_q16(p, gemm2_nt(T, p.H, E, k, p.block_m), q.hi, q.lo, q.scale, stream);
 }
 
+enum class Fmt { W8, W4 };
+
 struct Layout {
   int64_t cap, nblocks, splits;
-  size_t off_sorted, off_block, off_npad, off_a, off_y, total;
+  size_t off_sorted, off_block, off_npad, off_a, off_y, off_ids_ext, off_w_ext, off_x_ext, total;
 };
 
-Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, int64_t splits, bool w8) {
+// Workspace regions, 256-byte aligned: align outputs, the intermediate, the
+// split partials y; with `expand` (shared experts or weight on input) the
+// extended routing [T, k]; with `woi` the scaled input rows [T*k, H].
+// E and k here count the shared experts too.
+Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm, int64_t splits, Fmt fmt,
+              bool expand = false, bool woi = false) {
   Layout L{};
   L.cap = capacity(T, k, E, bm);
   L.nblocks = bm > 0 ? L.cap / bm : 0;
   L.splits = splits;
+  const size_t Tk = static_cast<size_t>(T * k);
   size_t o = 0;
   L.off_sorted = o; o += align_up(static_cast<size_t>(L.cap) * 4);
   L.off_block = o;  o += align_up(static_cast<size_t>(L.nblocks) * 4);
   L.off_npad = o;   o += align_up(4);
-  L.off_a = o;      o += intermediate_bytes(L.cap, I, bm, w8);
-  L.off_y = o;      o += align_up(static_cast<size_t>(splits) * static_cast<size_t>(T * k) *
-                                  static_cast<size_t>(H) * 4);
+  L.off_a = o;      o += intermediate_bytes(L.cap, I, bm, fmt == Fmt::W8);
+  L.off_y = o;      o += align_up(static_cast<size_t>(splits) * Tk * static_cast<size_t>(H) * 4);
+  if (expand) {
+    L.off_ids_ext = o; o += align_up(Tk * 4);
+    L.off_w_ext = o;   o += align_up(Tk * 4);
+  }
+  if (woi) {
+    L.off_x_ext = o;   o += align_up(Tk * static_cast<size_t>(H) * 2);
+  }
   L.total = o;
   return L;
 }
@@ -330,22 +344,127 @@ hipError_t launch_routing(const float* logits, int64_t T, int64_t E, int64_t k, 
                                   r->e_score_correction_bias, r->routed_scaling_factor, tw, ti, stream);
 }
 
-// Routing (when logits are given) and align.  Up to 8 tokens (one per wave)
-// one workgroup does both and saves a launch; larger batches route with one
-// wave per token across the chip, then align.
 constexpr int64_t kFusedRouteTokens = 8;
 
-hipError_t route_and_align(const float* logits, int renormalize, float* topk_w_out, int32_t* topk_ids_out,
-                           const int32_t* topk_ids, int64_t T, int64_t E, int64_t k, int64_t bm, int64_t cap,
-                           int32_t* sorted, int32_t* blocks, int32_t* npad, hipStream_t stream) {
-  const int Ei = static_cast<int>(E), ki = static_cast<int>(k), bmi = static_cast<int>(bm);
-  if (!logits) return moe::launch_align(topk_ids, T * k, Ei, bmi, cap, sorted, blocks, npad, stream);
-  if (T <= kFusedRouteTokens)
-    return moe::launch_route_align(logits, T, Ei, ki, renormalize, topk_w_out, topk_ids_out, bmi, cap, sorted,
-                                   blocks, npad, stream);
-  hipError_t e = moe::launch_route(logits, T, Ei, ki, renormalize, topk_w_out, topk_ids_out, stream);
-  if (e != hipSuccess) return e;
-  return moe::launch_align(topk_ids_out, T * k, Ei, bmi, cap, sorted, blocks, npad, stream);
+struct Opts {
+  int64_t S;     // shared experts after the routed ones
+  bool woi;      // routing weight applied to the input
+};
+
+Opts opts_of(const moe_fused_opts* fo) {
+  return fo ? Opts{fo->num_shared_experts, fo->apply_router_weight_on_input != 0} : Opts{0, false};
+}
+
+int64_t splits_fmt(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
+  return fmt == Fmt::W8 ? splits_for(T, H, I, E, k, bm) : w4_splits(T, H, I, E, k, bm);
+}
+
+// Workspace of a layer call; 0 for bad sizes.
+size_t workspace_for(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm,
+                     const moe_fused_opts* fo) {
+  const Opts o = opts_of(fo);
+  if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1 || o.S < 0) return 0;
+  const int64_t Ex = E + o.S, kx = k + o.S;
+  if (bm == 0) bm = auto_block_m(T, Ex, kx);
+  if (bm < 16 || bm > 256 || bm % 16) return 0;
+  return layout(T, H, I, Ex, kx, bm, splits_fmt(fmt, T, H, I, Ex, kx, bm), fmt, o.S > 0 || o.woi, o.woi).total;
+}
+
+// What the GEMMs of a format need, set up by layer_front.
+struct Front {
+  const void* x;               // GEMM1's activation rows
+  int64_t Tg, kg;              // rows of x; assignment f reads row f / kg
+  int64_t T, Tk, Ex, kx, bm, splits, cap;
+  int32_t* sorted;
+  int32_t* blocks;
+  int32_t* npad;
+  float* a;
+  float* y;
+  const float* cw;             // combine weights and ids [T, kx]
+  const int32_t* cids;
+};
+
+// Checks, workspace layout, routing (from logits, with the routing options),
+// the shared-expert / weight-on-input extension and the align.  Returns MOE_OK
+// and fills F; T = 0 returns MOE_OK with F->T = 0 and nothing enqueued.
+int layer_front(Fmt fmt, const void* x, int act, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                const moe_fused_opts* fo, const float* logits, const moe_routing* r, float* tw_out,
+                int32_t* ti_out, const float* tw, const int32_t* ti, int64_t block_m, void* workspace,
+                size_t workspace_bytes, hipStream_t stream, Front* F) {
+  int st;
+  const Opts o = opts_of(fo);
+  if (o.S < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "num_shared_experts must be >= 0");
+  if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
+  const int64_t Ex = E + o.S, kx = k + o.S;
+  if (Ex > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "routed plus shared experts above %lld", (long long)kMaxExperts);
+  if ((st = check_act(act)) != MOE_OK) return st;
+  if (logits && (st = check_routing(T, E, k, r)) != MOE_OK) return st;
+  const int64_t bm = block_m == 0 ? auto_block_m(T, Ex, kx) : block_m;
+  if ((st = check_block_m(bm)) != MOE_OK) return st;
+  F->T = 0;
+  if (T == 0) return ok();
+  if (T * kx > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^31-1");
+  if (!x || !workspace) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (logits ? (!tw_out || !ti_out) : (!tw || !ti)) return fail(MOE_ERR_INVALID_ARGUMENT, "null routing pointer");
+  if (!aligned(x, 16) || !aligned(workspace, kAlign))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 16-byte and the workspace 256-byte aligned");
+  const bool expand = o.S > 0 || o.woi;
+  const int64_t splits = splits_fmt(fmt, T, H, I, Ex, kx, bm);
+  const Layout L = layout(T, H, I, Ex, kx, bm, splits, fmt, expand, o.woi);
+  if (workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
+  char* ws = static_cast<char*>(workspace);
+  F->sorted = reinterpret_cast<int32_t*>(ws + L.off_sorted);
+  F->blocks = reinterpret_cast<int32_t*>(ws + L.off_block);
+  F->npad = reinterpret_cast<int32_t*>(ws + L.off_npad);
+  F->a = reinterpret_cast<float*>(ws + L.off_a);
+  F->y = reinterpret_cast<float*>(ws + L.off_y);
+  F->T = T; F->Tk = T * kx; F->Ex = Ex; F->kx = kx; F->bm = bm; F->splits = splits; F->cap = L.cap;
+  const int bmi = static_cast<int>(bm);
+  hipError_t e = hipSuccess;
+  bool aligned_done = false;
+  if (logits) {
+    if (!expand && default_routing(r) && T <= kFusedRouteTokens) {
+      // up to 8 tokens one workgroup routes (one wave per token) and aligns: one launch less
+      e = moe::launch_route_align(logits, T, static_cast<int>(E), static_cast<int>(k), r ? r->renormalize : 1,
+                                  tw_out, ti_out, bmi, L.cap, F->sorted, F->blocks, F->npad, stream);
+      aligned_done = true;
+    } else {
+      e = launch_routing(logits, T, E, k, r, tw_out, ti_out, stream);
+    }
+    if (e != hipSuccess) return hip_status(e, "route");
+    tw = tw_out;
+    ti = ti_out;
+  }
+  F->x = x; F->Tg = T; F->kg = kx; F->cw = tw; F->cids = ti;
+  if (expand) {
+    float* w_ext = reinterpret_cast<float*>(ws + L.off_w_ext);
+    int32_t* ids_ext = reinterpret_cast<int32_t*>(ws + L.off_ids_ext);
+    e = moe::launch_expand_routing(tw, ti, T, static_cast<int>(k), static_cast<int>(o.S), static_cast<int>(E),
+                                   o.woi ? 1 : 0, w_ext, ids_ext, stream);
+    if (e != hipSuccess) return hip_status(e, "expand routing");
+    F->cw = w_ext;
+    F->cids = ids_ext;
+    if (o.woi) {
+      void* x_ext = ws + L.off_x_ext;
+      e = moe::launch_prescale_input(x, act == MOE_FP16, tw, T, static_cast<int>(k), static_cast<int>(o.S), H,
+                                     x_ext, stream);
+      if (e != hipSuccess) return hip_status(e, "scale input");
+      F->x = x_ext; F->Tg = T * kx; F->kg = 1;
+    }
+  }
+  if (!aligned_done) {
+    e = moe::launch_align(F->cids, F->Tk, static_cast<int>(Ex), bmi, L.cap, F->sorted, F->blocks, F->npad, stream);
+    if (e != hipSuccess) return hip_status(e, "align");
+  }
+  return MOE_OK;
+}
+
+// The weighted combine of the split partials into `out`.
+int layer_back(const Front& F, int64_t H, int act, void* out, hipStream_t stream) {
+  return hip_status(moe::launch_combine(F.y, static_cast<int>(F.splits), F.T, static_cast<int>(F.kx), H,
+                                        static_cast<int>(F.Ex), F.cw, F.cids, act == MOE_FP16, out, stream),
+                    "combine");
 }
 
 }  // namespace
@@ -434,9 +553,12 @@ int64_t moe_w8a16_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, 
 
 size_t moe_w8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                                  int64_t block_m) {
-  if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
-  if (block_m == 0) block_m = auto_block_m(T, E, k);
-  return layout(T, H, I, E, k, block_m, splits_for(T, H, I, E, k, block_m), true).total;
+  return workspace_for(Fmt::W8, T, H, I, E, k, block_m, nullptr);
+}
+
+size_t moe_w8a16_workspace_bytes_ex(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
+                                    const moe_fused_opts* opts) {
+  return workspace_for(Fmt::W8, T, H, I, E, k, block_m, opts);
 }
 
 size_t moe_w8a16_intermediate_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m) {
@@ -536,58 +658,33 @@ namespace {
 // Route (when logits are given) + align + GEMM1 + GEMM2 + combine.
 int forward_w8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                const int8_t* w13, const float* w13_scale, int64_t w13_row_stride, const int8_t* w2,
-               const float* w2_scale, int64_t w2_row_stride, const float* logits, int renormalize,
+               const float* w2_scale, int64_t w2_row_stride, const float* logits, const moe_routing* routing,
                float* topk_w_out, int32_t* topk_ids_out, const float* topk_w, const int32_t* topk_ids,
-               int64_t block_m, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st;
-  if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
-  if ((st = check_act(act_dtype)) != MOE_OK) return st;
-  if (block_m == 0) block_m = auto_block_m(T, E, k);
-  if ((st = check_block_m(block_m)) != MOE_OK) return st;
+               const moe_fused_opts* fo, int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
   const int64_t ld13 = w13_row_stride ? w13_row_stride : H;
   const int64_t ld2 = w2_row_stride ? w2_row_stride : I;
   if (ld13 < H || ld13 % 16 || ld2 < I || ld2 % 16)
     return fail(MOE_ERR_INVALID_ARGUMENT, "row strides must cover the row and be multiples of 16");
-  if (T == 0) return ok();
-  if (T * k > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^31-1");
-  if (!x || !w13 || !w13_scale || !w2 || !w2_scale || !out || !workspace)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
-  if (logits ? (!topk_w_out || !topk_ids_out) : (!topk_w || !topk_ids))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "null routing pointer");
-  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 8) ||
-      !aligned(workspace, kAlign))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "x, w13, w2 16-byte, out 8-byte, workspace 256-byte alignment required");
-  const int64_t splits = splits_for(T, H, I, E, k, block_m);
-  const Layout L = layout(T, H, I, E, k, block_m, splits, true);
-  if (workspace_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
-  char* ws = static_cast<char*>(workspace);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.off_sorted);
-  int32_t* blocks = reinterpret_cast<int32_t*>(ws + L.off_block);
-  int32_t* npad = reinterpret_cast<int32_t*>(ws + L.off_npad);
-  float* a = reinterpret_cast<float*>(ws + L.off_a);
-  float* y = reinterpret_cast<float*>(ws + L.off_y);
-  hipError_t e = route_and_align(logits, renormalize, topk_w_out, topk_ids_out, topk_ids, T, E, k, block_m,
-                                 L.cap, sorted, blocks, npad, stream);
-  if (e != hipSuccess) return hip_status(e, "route/align");
-  if (logits) {
-    topk_w = topk_w_out;
-    topk_ids = topk_ids_out;
-  }
+  if (T > 0 && (!w13 || !w13_scale || !w2 || !w2_scale || !out)) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (T > 0 && (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 8)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w13, w2 16-byte and out 8-byte alignment required");
+  Front F{};
+  int st = layer_front(Fmt::W8, x, act_dtype, T, H, I, E, k, fo, logits, routing, topk_w_out, topk_ids_out, topk_w,
+                       topk_ids, block_m, workspace, workspace_bytes, stream, &F);
+  if (st != MOE_OK || F.T == 0) return st;
   moe::Gemm1Args p1{};
-  p1.x = x; p1.f16 = act_dtype == MOE_FP16; p1.T = T; p1.H = H; p1.I = I; p1.k = k; p1.Tk = T * k;
-  p1.w13 = w13; p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = sorted; p1.block_expert = blocks;
-  p1.num_padded = npad; p1.block_m = static_cast<int>(block_m); p1.cap = L.cap; p1.a = a;
-  if ((e = run_gemm1_and_requant(p1, T, E, stream)) != hipSuccess) return hip_status(e, "gemm1_w8");
+  p1.x = F.x; p1.f16 = act_dtype == MOE_FP16; p1.T = F.Tg; p1.H = H; p1.I = I; p1.k = F.kg; p1.Tk = F.Tk;
+  p1.w13 = w13; p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = F.sorted; p1.block_expert = F.blocks;
+  p1.num_padded = F.npad; p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap; p1.a = F.a;
+  hipError_t e;
+  if ((e = run_gemm1_and_requant(p1, F.Tg, F.Ex, stream)) != hipSuccess) return hip_status(e, "gemm1_w8");
   moe::Gemm2Args p2{};
-  p2.a = a; p2.H = H; p2.I = I; p2.Tk = T * k; p2.w2 = w2; p2.s2 = w2_scale; p2.ldw = ld2;
-  p2.sorted_ids = sorted; p2.block_expert = blocks; p2.num_padded = npad;
-  p2.block_m = static_cast<int>(block_m); p2.cap = L.cap; p2.splits = static_cast<int>(splits); p2.y = y;
-  if ((e = run_gemm2(p2, T, E, k, stream)) != hipSuccess) return hip_status(e, "gemm2_w8");
-  return hip_status(moe::launch_combine(y, static_cast<int>(splits), T, static_cast<int>(k), H,
-                                        static_cast<int>(E), topk_w, topk_ids, act_dtype == MOE_FP16,
-                                        out, stream),
-                    "combine");
+  p2.a = F.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = w2; p2.s2 = w2_scale; p2.ldw = ld2;
+  p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
+  p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y;
+  if ((e = run_gemm2(p2, F.Tg, F.Ex, F.kg, stream)) != hipSuccess) return hip_status(e, "gemm2_w8");
+  return layer_back(F, H, act_dtype, out, stream);
 }
 
 }  // namespace
@@ -600,8 +697,18 @@ int moe_w8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
                       const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
-                    nullptr, 0, nullptr, nullptr, topk_w, topk_ids, block_m, out, workspace, workspace_bytes,
-                    stream);
+                    nullptr, nullptr, nullptr, nullptr, topk_w, topk_ids, nullptr, block_m, out, workspace,
+                    workspace_bytes, stream);
+}
+
+int moe_w8a16_forward_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                         const int8_t* w13, const float* w13_scale, int64_t w13_row_stride, const int8_t* w2,
+                         const float* w2_scale, int64_t w2_row_stride, const float* topk_w, const int32_t* topk_ids,
+                         const moe_fused_opts* opts, int64_t block_m, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                    nullptr, nullptr, nullptr, nullptr, topk_w, topk_ids, opts, block_m, out, workspace,
+                    workspace_bytes, stream);
 }
 
 int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
@@ -611,8 +718,20 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
                     float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
+  const moe_routing r{MOE_SCORING_SOFTMAX, renormalize, 0, 0, nullptr, 1.0f};
   return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
-                    router_logits, renormalize, topk_w, topk_ids, nullptr, nullptr, block_m, out, workspace,
+                    router_logits, &r, topk_w, topk_ids, nullptr, nullptr, nullptr, block_m, out, workspace,
+                    workspace_bytes, stream);
+}
+
+int moe_w8a16_apply_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                       const float* router_logits, const moe_routing* routing, const int8_t* w13,
+                       const float* w13_scale, int64_t w13_row_stride, const int8_t* w2, const float* w2_scale,
+                       int64_t w2_row_stride, const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids,
+                       int64_t block_m, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
+  return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                    router_logits, routing, topk_w, topk_ids, nullptr, nullptr, opts, block_m, out, workspace,
                     workspace_bytes, stream);
 }
 
@@ -668,7 +787,7 @@ int moe_w8a16_forward_noalloc(const void* x, int act_dtype, int64_t T, int64_t H
   const int64_t bm = block_m == 0 ? auto_block_m(T, E, k) : block_m;
   if ((st = check_block_m(bm)) != MOE_OK) return st;
   if (T == 0) return ok();
-  const size_t need = layout(T, H, I, E, k, bm, splits_for(T, H, I, E, k, bm), true).total;
+  const size_t need = workspace_for(Fmt::W8, T, H, I, E, k, bm, nullptr);
   if (need > MOE_NOALLOC_SCRATCH_BYTES)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
                 "this batch needs %zu bytes of workspace; the static scratch of the no-alloc forward holds %zu "
@@ -677,7 +796,8 @@ int moe_w8a16_forward_noalloc(const void* x, int act_dtype, int64_t T, int64_t H
   void* ws = nullptr;
   if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
   return forward_w8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
-                    nullptr, 0, nullptr, nullptr, topk_w, topk_ids, bm, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
+                    nullptr, nullptr, nullptr, nullptr, topk_w, topk_ids, nullptr, bm, out, ws,
+                    MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -697,9 +817,12 @@ int moe_quantize_weights_w4(const float* w, int64_t E, int64_t N, int64_t K, int
 
 size_t moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                                  int64_t block_m) {
-  if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
-  if (block_m == 0) block_m = auto_block_m(T, E, k);
-  return layout(T, H, I, E, k, block_m, w4_splits(T, H, I, E, k, block_m), false).total;
+  return workspace_for(Fmt::W4, T, H, I, E, k, block_m, nullptr);
+}
+
+size_t moe_w4a16_workspace_bytes_ex(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
+                                    const moe_fused_opts* opts) {
+  return workspace_for(Fmt::W4, T, H, I, E, k, block_m, opts);
 }
 
 }  // extern "C"
@@ -709,66 +832,39 @@ namespace {
 int forward_w4(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                const int32_t* w13_qweight, const uint16_t* w13_scales, const int32_t* w13_qzeros,
                const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros, int64_t group_size,
-               const float* logits, int renormalize, float* topk_w_out, int32_t* topk_ids_out,
-               const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out, void* workspace,
-               size_t workspace_bytes, hipStream_t stream) {
-  int st;
-  if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
-  if ((st = check_act(act_dtype)) != MOE_OK) return st;
+               const float* logits, const moe_routing* routing, float* topk_w_out, int32_t* topk_ids_out,
+               const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* fo, int64_t block_m, void* out,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (group_size < 128 || group_size % 128 || H % group_size || I % group_size)
     return fail(MOE_ERR_UNSUPPORTED, "group_size must be a multiple of 128 dividing H and I (got %lld)",
                 (long long)group_size);
-  if (block_m == 0) block_m = auto_block_m(T, E, k);
-  if ((st = check_block_m(block_m)) != MOE_OK) return st;
-  if (T == 0) return ok();
-  if (T * k > 0x7fffffffLL) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^31-1");
-  if (!x || !w13_qweight || !w13_scales || !w13_qzeros || !w2_qweight || !w2_scales || !w2_qzeros || !out ||
-      !workspace)
+  if (T > 0 && (!w13_qweight || !w13_scales || !w13_qzeros || !w2_qweight || !w2_scales || !w2_qzeros || !out))
     return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
-  if (logits ? (!topk_w_out || !topk_ids_out) : (!topk_w || !topk_ids))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "null routing pointer");
-  if (!aligned(x, 16) || !aligned(w13_qweight, 16) || !aligned(w2_qweight, 16) || !aligned(out, 8) ||
-      !aligned(workspace, kAlign))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "alignment: x and qweights 16 bytes, out 8, workspace 256");
-  const int64_t splits = w4_splits(T, H, I, E, k, block_m);
-  const Layout L = layout(T, H, I, E, k, block_m, splits, false);
-  if (workspace_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", L.total, workspace_bytes);
-  char* ws = static_cast<char*>(workspace);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.off_sorted);
-  int32_t* blocks = reinterpret_cast<int32_t*>(ws + L.off_block);
-  int32_t* npad = reinterpret_cast<int32_t*>(ws + L.off_npad);
-  float* a = reinterpret_cast<float*>(ws + L.off_a);
-  float* y = reinterpret_cast<float*>(ws + L.off_y);
-  hipError_t e = route_and_align(logits, renormalize, topk_w_out, topk_ids_out, topk_ids, T, E, k, block_m,
-                                 L.cap, sorted, blocks, npad, stream);
-  if (e != hipSuccess) return hip_status(e, "route/align");
-  if (logits) {
-    topk_w = topk_w_out;
-    topk_ids = topk_ids_out;
-  }
+  if (T > 0 && (!aligned(w13_qweight, 16) || !aligned(w2_qweight, 16) || !aligned(out, 8)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "alignment: qweights 16 bytes, out 8");
+  Front F{};
+  int st = layer_front(Fmt::W4, x, act_dtype, T, H, I, E, k, fo, logits, routing, topk_w_out, topk_ids_out, topk_w,
+                       topk_ids, block_m, workspace, workspace_bytes, stream, &F);
+  if (st != MOE_OK || F.T == 0) return st;
   moe::Gemm1W4Args p1{};
-  p1.x = x; p1.f16 = act_dtype == MOE_FP16; p1.T = T; p1.H = H; p1.I = I; p1.k = k; p1.Tk = T * k;
+  p1.x = F.x; p1.f16 = act_dtype == MOE_FP16; p1.T = F.Tg; p1.H = H; p1.I = I; p1.k = F.kg; p1.Tk = F.Tk;
   p1.qw = w13_qweight; p1.sc = w13_scales; p1.qz = w13_qzeros; p1.group = static_cast<int>(group_size);
-  p1.sorted_ids = sorted; p1.block_expert = blocks; p1.num_padded = npad;
-  p1.block_m = static_cast<int>(block_m); p1.cap = L.cap; p1.a = a;
+  p1.sorted_ids = F.sorted; p1.block_expert = F.blocks; p1.num_padded = F.npad;
+  p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap; p1.a = F.a;
   // blocks of 16 or 32 rows: the DMA-fed ring (it copies the fp16 scales as dwords)
-  const bool w4_dma = (block_m == 16 || block_m == 32) && aligned(w13_scales, 4);
-  e = w4_dma ? moe::launch_gemm1_w4_dma(p1, stream)
-             : (w4_stream(block_m) ? moe::launch_gemm1_w4_stream(p1, stream) : moe::launch_gemm1_w4(p1, stream));
+  const bool w4_dma = (F.bm == 16 || F.bm == 32) && aligned(w13_scales, 4);
+  hipError_t e = w4_dma ? moe::launch_gemm1_w4_dma(p1, stream)
+                        : (w4_stream(F.bm) ? moe::launch_gemm1_w4_stream(p1, stream) : moe::launch_gemm1_w4(p1, stream));
   if (e != hipSuccess) return hip_status(e, "gemm1_w4");
   moe::Gemm2W4Args p2{};
-  p2.a = a; p2.f16 = act_dtype == MOE_FP16; p2.H = H; p2.I = I; p2.Tk = T * k;
+  p2.a = F.a; p2.f16 = act_dtype == MOE_FP16; p2.H = H; p2.I = I; p2.Tk = F.Tk;
   p2.qw = w2_qweight; p2.sc = w2_scales; p2.qz = w2_qzeros; p2.group = static_cast<int>(group_size);
-  p2.sorted_ids = sorted; p2.block_expert = blocks; p2.num_padded = npad;
-  p2.block_m = static_cast<int>(block_m); p2.cap = L.cap; p2.splits = static_cast<int>(splits); p2.y = y;
-  if ((e = w4_stream(block_m) ? moe::launch_gemm2_w4_stream(p2, stream) : moe::launch_gemm2_w4(p2, stream)) !=
+  p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
+  p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y;
+  if ((e = w4_stream(F.bm) ? moe::launch_gemm2_w4_stream(p2, stream) : moe::launch_gemm2_w4(p2, stream)) !=
       hipSuccess)
     return hip_status(e, "gemm2_w4");
-  return hip_status(moe::launch_combine(y, static_cast<int>(splits), T, static_cast<int>(k), H,
-                                        static_cast<int>(E), topk_w, topk_ids, act_dtype == MOE_FP16,
-                                        out, stream),
-                    "combine");
+  return layer_back(F, H, act_dtype, out, stream);
 }
 
 }  // namespace
@@ -782,8 +878,19 @@ int moe_w4a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_
                       const float* topk_w, const int32_t* topk_ids, int64_t block_m, void* out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return forward_w4(x, act_dtype, T, H, I, E, k, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
-                    w2_qzeros, group_size, nullptr, 0, nullptr, nullptr, topk_w, topk_ids, block_m, out, workspace,
-                    workspace_bytes, stream);
+                    w2_qzeros, group_size, nullptr, nullptr, nullptr, nullptr, topk_w, topk_ids, nullptr, block_m, out,
+                    workspace, workspace_bytes, stream);
+}
+
+int moe_w4a16_forward_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                         const int32_t* w13_qweight, const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                         const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros,
+                         int64_t group_size, const float* topk_w, const int32_t* topk_ids,
+                         const moe_fused_opts* opts, int64_t block_m, void* out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return forward_w4(x, act_dtype, T, H, I, E, k, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
+                    w2_qzeros, group_size, nullptr, nullptr, nullptr, nullptr, topk_w, topk_ids, opts, block_m, out,
+                    workspace, workspace_bytes, stream);
 }
 
 int moe_w4a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
@@ -793,8 +900,21 @@ int moe_w4a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
                     int64_t group_size, float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
+  const moe_routing r{MOE_SCORING_SOFTMAX, renormalize, 0, 0, nullptr, 1.0f};
   return forward_w4(x, act_dtype, T, H, I, E, k, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
-                    w2_qzeros, group_size, router_logits, renormalize, topk_w, topk_ids, nullptr, nullptr, block_m,
+                    w2_qzeros, group_size, router_logits, &r, topk_w, topk_ids, nullptr, nullptr, nullptr, block_m,
+                    out, workspace, workspace_bytes, stream);
+}
+
+int moe_w4a16_apply_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                       const float* router_logits, const moe_routing* routing, const int32_t* w13_qweight,
+                       const uint16_t* w13_scales, const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                       const uint16_t* w2_scales, const int32_t* w2_qzeros, int64_t group_size,
+                       const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
+  return forward_w4(x, act_dtype, T, H, I, E, k, w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
+                    w2_qzeros, group_size, router_logits, routing, topk_w, topk_ids, nullptr, nullptr, opts, block_m,
                     out, workspace, workspace_bytes, stream);
 }
 

@@ -132,6 +132,14 @@ hipError_t launch_gemm1_w4_stream(const Gemm1W4Args& p, hipStream_t stream);
 hipError_t launch_gemm1_w4_dma(const Gemm1W4Args& p, hipStream_t stream);
 hipError_t launch_gemm2_w4_stream(const Gemm2W4Args& p, hipStream_t stream);
 
+// Shared experts / routing weight on the input: routing extended to k + S columns (shared experts
+// E .. E+S-1 with weight 1; weights 1 everywhere when the weight goes on the input), and the input rows
+// rne(w * x[t]) of every extended assignment.
+hipError_t launch_expand_routing(const float* topk_w, const int32_t* topk_ids, int64_t T, int k, int S, int E,
+                                 int weight_on_input, float* w_ext, int32_t* ids_ext, hipStream_t stream);
+hipError_t launch_prescale_input(const void* x, int f16, const float* topk_w, int64_t T, int k, int S, int64_t H,
+                                 void* x_ext, hipStream_t stream);
+
 // Weighted top-k combine of the split partials.
 hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,
                           const float* topk_w, const int32_t* topk_ids, int f16, void* out,
