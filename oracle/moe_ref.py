@@ -473,6 +473,110 @@ def moe_forward_w4(x: np.ndarray, qw13, s13, z13, qw2, s2, z2, group_size: int,
 
 
 # ---------------------------------------------------------------------------
+# GPTQ / AWQ checkpoint import into the canonical 4-bit layout
+# ---------------------------------------------------------------------------
+# moe_wna16 page, ``MoeWNA16Method.get_weight_loader``: ``convert_awq_tensor``,
+# ``convert_gptq_int4_qzeros`` and ``moe_wna16_weight_loader`` turn the packed
+# int32 tensors of AWQ and GPTQ checkpoints into the page's canonical uint8
+# layout (codes [N, K/2] along K, zeros [N/2, K/g] along N, even index in the
+# low nibble; scales [N, K/g]); ``MoeWNA16Method.create_weights`` halves the
+# group size until it divides both H and I and the loader repeats scales and
+# zeros to match.  The steps below follow the loader; the last one, from the
+# page's uint8 layout to this library's int32 words, is this library's own
+# packing (codes: the same bytes; zeros: 8 rows of one group per word).
+
+AWQ_REVERSE_ORDER = (0, 4, 1, 5, 2, 6, 3, 7)   # the page's reverse_awq_pack_order
+
+
+def _nibbles_low_first(t: np.ndarray) -> np.ndarray:
+    """int32 [a, b] -> uint8 nibbles [a, 8b]: bytes in memory order, low nibble before high."""
+    b8 = np.ascontiguousarray(np.asarray(t, np.int32)).view(np.uint8)          # [a, 4b] little-endian bytes
+    nib = np.stack([b8 & 0xF, b8 >> 4], axis=-1)                                # [a, 4b, 2]
+    return nib.reshape(t.shape[0], -1)
+
+
+def awq_to_page_uint8(t: np.ndarray, kind: str) -> np.ndarray:
+    """``convert_awq_tensor``: AWQ qweight int32 [K, N/8] -> uint8 [N, K/2]; AWQ qzeros int32
+    [K/g, N/8] -> uint8 [N/2, K/g].  Unpack the nibbles, undo AWQ's order inside every group of
+    eight, transpose, and pack pairs again (along K for codes, along N for zeros)."""
+    a = t.shape[0]
+    nib = _nibbles_low_first(t).reshape(-1, 8)[:, list(AWQ_REVERSE_ORDER)].reshape(a, -1)   # [a, n]
+    tt = nib.T                                                                              # [n, a]
+    if kind == "qweight":
+        return (tt[:, 0::2] + 16 * tt[:, 1::2]).astype(np.uint8)
+    if kind == "qzeros":
+        return (tt[0::2, :] + 16 * tt[1::2, :]).astype(np.uint8)
+    raise ValueError(kind)
+
+
+def gptq_qweight_to_page_uint8(t: np.ndarray) -> np.ndarray:
+    """GPTQ qweight int32 [K/8, N] (codes packed along K) -> uint8 [N, K/2]: transpose, view bytes."""
+    return np.ascontiguousarray(np.asarray(t, np.int32).T).view(np.uint8)
+
+
+def gptq_qzeros_to_page_uint8(t: np.ndarray) -> np.ndarray:
+    """``convert_gptq_int4_qzeros``: GPTQ qzeros int32 [K/g, N/8] store zero - 1; add 1 to each nibble
+    and pack the pair again with uint8 arithmetic (a stored 15 carries into the high nibble, as the
+    page's byte sum does), then transpose -> uint8 [N/2, K/g]."""
+    b8 = np.ascontiguousarray(np.asarray(t, np.int32)).view(np.uint8)          # [K/g, N/2]
+    lo = (b8 & 0xF).astype(np.uint8) + np.uint8(1)
+    hi = (b8 >> 4).astype(np.uint8) + np.uint8(1)
+    packed = (lo + hi * np.uint8(16)).astype(np.uint8)                           # wraps like uint8 tensors
+    return np.ascontiguousarray(packed.T)
+
+
+def wna16_group_size(H: int, I: int, group_size: int):
+    """``MoeWNA16Method.create_weights``: halve the group size until it divides I and H (never below 32);
+    returns (group size, factor the loaded scales and zeros are repeated by)."""
+    g, f = int(group_size), 1
+    while I % g or H % g:
+        g //= 2
+        f *= 2
+        if g < 32:
+            raise ValueError("group size fell below 32")
+    return g, f
+
+
+def repeat_groups(t: np.ndarray, factor: int) -> np.ndarray:
+    """``repeat_interleave(factor, 1)`` of the loader: every group column repeated factor times."""
+    return np.repeat(np.asarray(t), factor, axis=1)
+
+
+def page_codes_to_words(u8: np.ndarray) -> np.ndarray:
+    """uint8 codes [N, K/2] -> int32 [N, K/8]: the same bytes read as little-endian words."""
+    return np.ascontiguousarray(u8).view(np.int32)
+
+
+def page_zeros_to_words(u8: np.ndarray) -> np.ndarray:
+    """uint8 zeros [N/2, G] (rows 2i, 2i+1 in byte i) -> int32 [N/8, G] with row n at bits 4(n mod 8)."""
+    u = np.asarray(u8, np.uint32)
+    N2, G = u.shape
+    q = u.reshape(N2 // 4, 4, G)
+    return (q[:, 0] | (q[:, 1] << 8) | (q[:, 2] << 16) | (q[:, 3] << 24)).view(np.int32)
+
+
+def import_awq(qweight: np.ndarray, qzeros: np.ndarray, scales: np.ndarray, H: int, I: int, group_size: int):
+    """One expert matrix of an AWQ checkpoint -> (qweight int32 [N, K/8], scales fp16 [N, K/g'],
+    qzeros int32 [N/8, K/g']) in this library's layout, with the group size g' of ``wna16_group_size``.
+    AWQ shapes: qweight [K, N/8], qzeros [K/g, N/8], scales [K/g, N]."""
+    _, f = wna16_group_size(H, I, group_size)
+    qw = page_codes_to_words(awq_to_page_uint8(qweight, "qweight"))
+    qz = page_zeros_to_words(repeat_groups(awq_to_page_uint8(qzeros, "qzeros"), f))
+    sc = repeat_groups(np.asarray(scales, np.float16).T, f)
+    return qw, np.ascontiguousarray(sc), qz
+
+
+def import_gptq(qweight: np.ndarray, qzeros: np.ndarray, scales: np.ndarray, H: int, I: int, group_size: int):
+    """One expert matrix of a GPTQ checkpoint (4-bit) -> the layout of ``import_awq``.
+    GPTQ shapes: qweight [K/8, N], qzeros [K/g, N/8] (zero - 1), scales [K/g, N]."""
+    _, f = wna16_group_size(H, I, group_size)
+    qw = page_codes_to_words(gptq_qweight_to_page_uint8(qweight))
+    qz = page_zeros_to_words(repeat_groups(gptq_qzeros_to_page_uint8(qzeros), f))
+    sc = repeat_groups(np.asarray(scales, np.float16).T, f)
+    return qw, np.ascontiguousarray(sc), qz
+
+
+# ---------------------------------------------------------------------------
 # Tolerance of the layer output (floating-point result)
 # ---------------------------------------------------------------------------
 
