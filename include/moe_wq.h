@@ -393,6 +393,43 @@ int moe_w4a16_apply_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64
                        int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * GPTQ / AWQ 4-bit checkpoint import (moe_wna16 page,
+ * MoeWNA16Method.get_weight_loader: convert_awq_tensor, convert_gptq_int4_qzeros,
+ * moe_wna16_weight_loader; MoeWNA16Method.create_weights: group size halving).
+ *
+ * moe_wna16_group_size: the group size create_weights settles on: halved
+ * (and *repeat doubled) until it divides both H and I.  Returns MOE_OK and
+ * writes *group / *repeat, or MOE_ERR_INVALID_ARGUMENT if it would fall
+ * below 32 (or on non-positive sizes / null pointers).
+ *
+ * moe_w4_import: one [N, K] matrix of a checkpoint (one expert's gate, up or
+ * down projection; gate and up go to rows [0, I) and [I, 2I) of w13):
+ *   format MOE_W4_AWQ:  qweight device int32 [K, N/8], packed along N in
+ *                       AWQ's nibble order (column c of each group of eight
+ *                       in nibble (0,4,1,5,2,6,3,7)[c]); qzeros device int32
+ *                       [ceil(K/group_size), N/8] the same way;
+ *   format MOE_W4_GPTQ: qweight device int32 [K/8, N], packed along K
+ *                       (code k at bits 4(k mod 8)); qzeros device int32
+ *                       [ceil(K/group_size), N/8] holding zero - 1 (the
+ *                       loader adds 1 per nibble in uint8 arithmetic, so a
+ *                       stored 15 carries into its pair's high nibble);
+ *   scales device fp16 [ceil(K/group_size), N] (both formats);
+ *   repeat: from moe_wna16_group_size (1 = none).
+ * Writes this library's layout with groups of group_size / repeat columns:
+ *   out_qweight device int32 [N, K/8], out_scales device fp16 [N, K*repeat/group_size],
+ *   out_qzeros device int32 [N/8, K*repeat/group_size];
+ * output group j takes input group j / repeat.  Integer work: bit exact.
+ * Errors: MOE_ERR_INVALID_ARGUMENT (null pointers, unknown format, N or K
+ * not multiples of 8, repeat < 1, group_size not a multiple of repeat, the
+ * output group not dividing K).
+ * ---------------------------------------------------------------------- */
+enum moe_w4_format { MOE_W4_AWQ = 0, MOE_W4_GPTQ = 1 };
+int moe_wna16_group_size(int64_t H, int64_t I, int64_t group_size, int64_t* group, int64_t* repeat);
+int moe_w4_import(int format, const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                  int64_t N, int64_t K, int64_t group_size, int64_t repeat,
+                  int32_t* out_qweight, uint16_t* out_scales, int32_t* out_qzeros, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

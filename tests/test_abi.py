@@ -250,3 +250,21 @@ def test_route_select_argument_errors():
         assert L.moe_route_select(p, 4, E, 3, ctypes.byref(r), p, p, None) == want, fields
     assert L.moe_route_select(None, 0, 8, 2, None, None, None, None) == B.MOE_OK          # T = 0
     assert L.moe_route_select(None, 4, 8, 2, None, None, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_wna16_group_size_matches_oracle():
+    """The group-size rule is host code: the C call and the oracle agree, errors included."""
+    for H, I, g in [(4096, 14336, 128), (2048, 1408, 256), (2048, 1344, 128), (2048, 768, 512), (2048, 1400, 128)]:
+        try:
+            want = oracle.wna16_group_size(H, I, g)
+        except ValueError:
+            with pytest.raises(ValueError):
+                pkg.moe_wna16_group_size(H, I, g)
+            continue
+        assert pkg.moe_wna16_group_size(H, I, g) == want
+    L = pkg.lib()
+    p = ctypes.c_void_p(FAKE)
+    assert L.moe_w4_import(3, p, p, p, 16, 256, 128, 1, p, p, p, None) == B.MOE_ERR_INVALID_ARGUMENT   # format
+    assert L.moe_w4_import(0, p, p, p, 12, 256, 128, 1, p, p, p, None) == B.MOE_ERR_INVALID_ARGUMENT   # N % 8
+    assert L.moe_w4_import(0, p, p, p, 16, 256, 128, 3, p, p, p, None) == B.MOE_ERR_INVALID_ARGUMENT   # repeat
+    assert L.moe_w4_import(0, p, p, p, 16, 200, 128, 2, p, p, p, None) == B.MOE_ERR_INVALID_ARGUMENT   # 64 ∤ 200

@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     moe_quantize_weights_w4,
     moe_route_select,
     moe_route_topk,
+    moe_w4_import,
+    moe_wna16_group_size,
     moe_w4a16_apply,
     moe_w4a16_apply_ex,
     moe_w4a16_forward_ex,

@@ -51,6 +51,8 @@ SIGNATURES = {
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_w8a16_splits": (_c_i64, [_c_i64] * 6),
+    "moe_wna16_group_size": (_c_int, [_c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "moe_w4_import": (_c_int, [_c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "moe_w8a16_workspace_bytes_ex": (_c_size, [_c_i64] * 6 + [_c_p]),
     "moe_w4a16_workspace_bytes_ex": (_c_size, [_c_i64] * 6 + [_c_p]),
     "moe_w8a16_forward_ex": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
@@ -593,3 +595,35 @@ def moe_w4a16_apply_ex(x, router_logits, w13_qweight, w13_scales, w13_qzeros, w2
                                     _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "moe_w4a16_apply_ex")
+
+
+# ---------------------------------------------------------------------------
+# GPTQ / AWQ 4-bit checkpoint import
+# ---------------------------------------------------------------------------
+
+MOE_W4_FORMAT = {"awq": 0, "gptq": 1}
+
+
+def moe_wna16_group_size(H: int, I: int, group_size: int):
+    """(group size, repeat) that MoeWNA16Method.create_weights settles on for a checkpoint group size."""
+    g, r = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().moe_wna16_group_size(H, I, group_size, ctypes.byref(g), ctypes.byref(r)), "moe_wna16_group_size")
+    return g.value, r.value
+
+
+def moe_w4_import(fmt: str, qweight, qzeros, scales, N: int, K: int, group_size: int, repeat: int, out_qweight,
+                  out_scales, out_qzeros, stream=None):
+    """One [N, K] matrix of a 4-bit AWQ or GPTQ checkpoint into this library's layout (see moe_wq.h)."""
+    if fmt not in MOE_W4_FORMAT:
+        raise ValueError(f"format must be one of {sorted(MOE_W4_FORMAT)}, got {fmt!r}")
+    gin = -(-K // group_size)
+    gout = K * repeat // group_size
+    _need(qweight, torch.int32, (K, N // 8) if fmt == "awq" else (K // 8, N), "qweight")
+    _need(qzeros, torch.int32, (gin, N // 8), "qzeros")
+    _need(scales, torch.float16, (gin, N), "scales")
+    _need(out_qweight, torch.int32, (N, K // 8), "out_qweight")
+    _need(out_scales, torch.float16, (N, gout), "out_scales")
+    _need(out_qzeros, torch.int32, (N // 8, gout), "out_qzeros")
+    _check(lib().moe_w4_import(MOE_W4_FORMAT[fmt], _ptr(qweight), _ptr(qzeros), _ptr(scales), N, K, group_size,
+                               repeat, _ptr(out_qweight), _ptr(out_scales), _ptr(out_qzeros), _stream(stream)),
+           "moe_w4_import")

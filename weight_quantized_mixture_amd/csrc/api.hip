@@ -919,3 +919,42 @@ int moe_w4a16_apply_ex(const void* x, int act_dtype, int64_t T, int64_t H, int64
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// GPTQ / AWQ import
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+int moe_wna16_group_size(int64_t H, int64_t I, int64_t group_size, int64_t* group, int64_t* repeat) {
+  if (H < 1 || I < 1 || group_size < 1 || !group || !repeat)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "need H, I, group_size >= 1 and output pointers");
+  int64_t g = group_size, r = 1;
+  while (I % g || H % g) {
+    g /= 2;
+    r *= 2;
+    if (g < 32) return fail(MOE_ERR_INVALID_ARGUMENT, "the group size would fall below 32");
+  }
+  *group = g;
+  *repeat = r;
+  return ok();
+}
+
+int moe_w4_import(int format, const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales, int64_t N,
+                  int64_t K, int64_t group_size, int64_t repeat, int32_t* out_qweight, uint16_t* out_scales,
+                  int32_t* out_qzeros, hipStream_t stream) {
+  if (format != MOE_W4_AWQ && format != MOE_W4_GPTQ) return fail(MOE_ERR_INVALID_ARGUMENT, "unknown format %d", format);
+  if (N < 8 || K < 8 || N % 8 || K % 8) return fail(MOE_ERR_INVALID_ARGUMENT, "N and K must be positive multiples of 8");
+  if (repeat < 1 || group_size < 1 || group_size % repeat)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "repeat must be >= 1 and divide group_size");
+  const int64_t gout = group_size / repeat;
+  if (K % gout) return fail(MOE_ERR_INVALID_ARGUMENT, "the output group %lld does not divide K %lld", (long long)gout,
+                            (long long)K);
+  if (!qweight || !qzeros || !scales || !out_qweight || !out_scales || !out_qzeros)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_import_w4(format == MOE_W4_GPTQ, qweight, qzeros, scales, N, K, gout, repeat,
+                                          out_qweight, out_scales, out_qzeros, stream),
+                    "import_w4");
+}
+
+}  // extern "C"

@@ -140,6 +140,12 @@ hipError_t launch_expand_routing(const float* topk_w, const int32_t* topk_ids, i
 hipError_t launch_prescale_input(const void* x, int f16, const float* topk_w, int64_t T, int k, int S, int64_t H,
                                  void* x_ext, hipStream_t stream);
 
+// 4-bit GPTQ (gptq = 1) or AWQ (gptq = 0) checkpoint tensors of one [N, K] matrix -> this library's
+// layout; output groups of group_out columns, group j' from input group j' / repeat.
+hipError_t launch_import_w4(int gptq, const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                            int64_t N, int64_t K, int64_t group_out, int64_t repeat, int32_t* out_qweight,
+                            uint16_t* out_scales, int32_t* out_qzeros, hipStream_t stream);
+
 // Weighted top-k combine of the split partials.
 hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,
                           const float* topk_w, const int32_t* topk_ids, int f16, void* out,
