@@ -473,6 +473,104 @@ def moe_forward_w4(x: np.ndarray, qw13, s13, z13, qw2, s2, z2, group_size: int,
 
 
 # ---------------------------------------------------------------------------
+# Weight-only fp8 (OCP e4m3fn) experts with per-tensor scales
+# ---------------------------------------------------------------------------
+# fp8 page (vllm ... quantization.fp8): ``Fp8MoEMethod.create_weights`` (w13 [E, 2I, H] and
+# w2 [E, H, I] in float8_e4m3fn, scales w13 [E, 2] (one per shard) and w2 [E]),
+# ``process_weights_after_loading`` (a 16-bit checkpoint is quantized per expert with one scale
+# for the merged w13 and one for w2; an fp8 checkpoint's two w13 scales are merged into their
+# maximum, each shard dequantized with its own scale and quantized again with the maximum), and
+# ``__init__`` (the weight-only path without fp8 activations).  ``scaled_fp8_quant`` and
+# ``per_tensor_dequantize`` are only called; reading: scale = max|w| / 448 in fp32, code =
+# e4m3fn(clamp(w / scale, -448, 448)) rounded to nearest even, dequant = fp32(value * scale).
+
+E4M3_MAX = 448.0
+
+
+def e4m3_round(v) -> np.ndarray:
+    """fp32 values -> e4m3fn codes (uint8): clamp to [-448, 448], round to nearest even on the
+    format's grid (step 2^(e-3) in binade [2^e, 2^(e+1)) for e >= -6, step 2^-9 below 2^-6); the
+    sign bit is the value's (so -0 and small negatives that round to 0 give 0x80)."""
+    v = np.asarray(v, np.float32).astype(np.float64)
+    sign = np.signbit(v)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    step = np.where(a >= 2.0 ** -6, 2.0 ** (e - 3), 2.0 ** -9)
+    r = np.rint(a / step) * step                        # exact: step is a power of two
+    # encode the rounded magnitude
+    with np.errstate(divide="ignore"):
+        er = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    normal = r >= 2.0 ** -6
+    mant = np.where(normal, np.rint((r / 2.0 ** np.where(normal, er, 0) - 1.0) * 8), np.rint(r / 2.0 ** -9))
+    bits = np.where(normal, ((er + 7).astype(np.int64) << 3) | mant.astype(np.int64), mant.astype(np.int64))
+    return (bits | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """e4m3fn codes -> float64, exactly (codes 0x7F / 0xFF are NaN)."""
+    b = np.asarray(codes, np.uint8).astype(np.int64)
+    sgn = np.where(b & 0x80, -1.0, 1.0)
+    ex = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    val = np.where(ex == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (ex - 7))
+    val = np.where((b & 0x7F) == 0x7F, np.nan, val)
+    return sgn * val
+
+
+def quantize_fp8_tensor(w, scale=None):
+    """``scaled_fp8_quant``: one scale for the whole tensor (dynamic: max|w| / 448 in fp32; or the
+    given fp32 scale), codes e4m3fn(w / scale) (fp32 divide).  A zero tensor gets scale 0 and
+    codes 0.  Returns (codes uint8, scale float32)."""
+    w = np.asarray(w, np.float32)
+    if scale is None:
+        scale = np.float32(np.max(np.abs(w)) / np.float32(E4M3_MAX)) if w.size else np.float32(0)
+    scale = np.float32(scale)
+    if scale == 0:
+        return np.zeros(w.shape, np.uint8), scale
+    return e4m3_round((w / scale).astype(np.float32)), scale
+
+
+def dequant_fp8(codes, scale) -> np.ndarray:
+    """``per_tensor_dequantize``: fp32(value * scale)."""
+    return (e4m3_decode(codes).astype(np.float32) * np.float32(scale)).astype(np.float32)
+
+
+def fp8_merge_w13_scales(q13, s13):
+    """fp8 checkpoint with one scale per w13 shard (s13 [E, 2]): per expert the larger scale is kept;
+    each shard is dequantized with its own scale (fp32) and quantized again with the larger one.
+    Returns (codes uint8 [E, 2I, H], scales float32 [E])."""
+    q13 = np.asarray(q13, np.uint8)
+    s13 = np.asarray(s13, np.float32)
+    E, N2, _ = q13.shape
+    I = N2 // 2
+    out = np.empty_like(q13)
+    smax = s13.max(axis=1).astype(np.float32)
+    for e in range(E):
+        for shard in range(2):
+            rows = slice(shard * I, (shard + 1) * I)
+            out[e, rows] = quantize_fp8_tensor(dequant_fp8(q13[e, rows], s13[e, shard]), smax[e])[0]
+    return out, smax
+
+
+def moe_forward_fp8(x, q13, s13, q2, s2, topk_w, topk_ids, weight_on_input=False, num_shared=0):
+    """The weight-only fp8 layer: W = decode(q) * s exactly in fp64 (one scale per expert and
+    matrix), then ``moe_forward_dense`` (options as ``moe_forward_w8``)."""
+    E = q13.shape[0]
+    I = q13.shape[1] // 2
+    topk_w, topk_ids = _extend_routing(topk_w, topk_ids, E, num_shared)
+
+    def w13_of(e):
+        return e4m3_decode(q13[e]) * float(s13[e]) if 0 <= e < E else None
+
+    def w2_of(e):
+        return e4m3_decode(q2[e]) * float(s2[e]) if 0 <= e < E else None
+
+    return moe_forward_dense(x, w13_of, w2_of, topk_w, topk_ids, I, weight_on_input)
+
+
+# ---------------------------------------------------------------------------
 # GPTQ / AWQ checkpoint import into the canonical 4-bit layout
 # ---------------------------------------------------------------------------
 # moe_wna16 page, ``MoeWNA16Method.get_weight_loader``: ``convert_awq_tensor``,
