@@ -430,6 +430,49 @@ int moe_w4_import(int format, const int32_t* qweight, const int32_t* qzeros, con
                   int64_t N, int64_t K, int64_t group_size, int64_t repeat,
                   int32_t* out_qweight, uint16_t* out_scales, int32_t* out_qzeros, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Weight-only fp8 experts (fp8 page: Fp8MoEMethod.__init__ keeps a
+ * weight-only path for GPUs without fp8 arithmetic; create_weights: w13
+ * [E, 2I, H] and w2 [E, H, I] in float8_e4m3fn (OCP: 1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, largest finite 448, codes 0x7F/0xFF NaN),
+ * w13 scales [E, 2] merged into w13_weight_scale [E], w2_weight_scale [E];
+ * process_weights_after_loading).  Activations stay bf16 / fp16:
+ *   h = w13_scale[e] * sum_c x[t,c] e4m3(w13[e,n,c]),  a = silu(h_gate) h_up,
+ *   y = w2_scale[e] * sum_i a[i] e4m3(w2[e,h,i]),     out_t = sum_j w_j y.
+ *
+ * moe_quantize_weights_fp8: one scale per [N, K] tensor (scaled_fp8_quant of a
+ * 16-bit checkpoint): scale[e] = max |w[e]| / 448 (fp32 IEEE divide), code =
+ * e4m3fn(clamp(w / scale, -448, 448)), fp32 divide, round to nearest even,
+ * the sign bit kept (so -0 codes 0x80); a zero tensor gets scale 0 and codes 0.
+ *   w device fp32 [E, N, K]; q device uint8 [E, N, K]; scale device fp32 [E].
+ *   (For w13 pass N = 2I: one scale for the merged gate and up rows.)
+ * moe_fp8_merge_w13_scales: an fp8 checkpoint's two w13 shard scales
+ * (device fp32 [E, 2]) become one (device fp32 [E], their maximum): each
+ * shard is dequantized with its own scale (fp32 code value * scale) and
+ * quantized again with the maximum as above; w13 (device uint8 [E, 2I, H]) is
+ * rewritten in place.
+ * moe_wfp8a16_forward / moe_wfp8a16_apply: the layer, as moe_w8a16_forward_ex /
+ * moe_w8a16_apply_ex (routing and fused options may be NULL) with the weights
+ * above (rows unpadded; w13 and w2 16-byte aligned).  Workspace:
+ * moe_wfp8a16_workspace_bytes.  Requirements as moe_w8a16_forward.
+ * ---------------------------------------------------------------------- */
+int moe_quantize_weights_fp8(const float* w, int64_t E, int64_t N, int64_t K, uint8_t* q, float* scale,
+                             hipStream_t stream);
+int moe_fp8_merge_w13_scales(uint8_t* w13, const float* w13_shard_scales, int64_t E, int64_t I, int64_t H,
+                             float* w13_scale, hipStream_t stream);
+size_t moe_wfp8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
+                                   const moe_fused_opts* opts);
+int moe_wfp8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                        const uint8_t* w13, const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                        const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* opts,
+                        int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+int moe_wfp8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                      const float* router_logits, const moe_routing* routing,
+                      const uint8_t* w13, const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                      const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids, int64_t block_m,
+                      void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,11 @@ from .binding import (  # noqa: F401
     moe_quantize_weights_w4,
     moe_route_select,
     moe_route_topk,
+    moe_fp8_merge_w13_scales,
+    moe_quantize_weights_fp8,
+    moe_wfp8a16_apply,
+    moe_wfp8a16_forward,
+    moe_wfp8a16_workspace_bytes,
     moe_w4_import,
     moe_wna16_group_size,
     moe_w4a16_apply,
@@ -37,4 +42,4 @@ from .binding import (  # noqa: F401
     moe_w8a16_requant,
     moe_w8a16_workspace_bytes,
 )
-from .layer import W4A16MoE, W8A16MoE  # noqa: F401
+from .layer import W4A16MoE, W8A16MoE, WFP8A16MoE  # noqa: F401

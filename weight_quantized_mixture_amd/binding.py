@@ -51,6 +51,13 @@ SIGNATURES = {
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_w8a16_splits": (_c_i64, [_c_i64] * 6),
+    "moe_quantize_weights_fp8": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "moe_fp8_merge_w13_scales": (_c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
+    "moe_wfp8a16_workspace_bytes": (_c_size, [_c_i64] * 6 + [_c_p]),
+    "moe_wfp8a16_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                     _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_wfp8a16_apply": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
+                                   _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_wna16_group_size": (_c_int, [_c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "moe_w4_import": (_c_int, [_c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "moe_w8a16_workspace_bytes_ex": (_c_size, [_c_i64] * 6 + [_c_p]),
@@ -627,3 +634,84 @@ def moe_w4_import(fmt: str, qweight, qzeros, scales, N: int, K: int, group_size:
     _check(lib().moe_w4_import(MOE_W4_FORMAT[fmt], _ptr(qweight), _ptr(qzeros), _ptr(scales), N, K, group_size,
                                repeat, _ptr(out_qweight), _ptr(out_scales), _ptr(out_qzeros), _stream(stream)),
            "moe_w4_import")
+
+
+# ---------------------------------------------------------------------------
+# Weight-only fp8 (e4m3fn) experts
+# ---------------------------------------------------------------------------
+
+
+def moe_quantize_weights_fp8(w, q, scale, stream=None):
+    """Per-tensor e4m3fn quantization of w [E, N, K] fp32 into q uint8 [E, N, K] and scale fp32 [E]."""
+    E, N, K = w.shape
+    _need(w, torch.float32, (E, N, K), "w")
+    _need(q, torch.uint8, (E, N, K), "q")
+    _need(scale, torch.float32, (E,), "scale")
+    _check(lib().moe_quantize_weights_fp8(_ptr(w), E, N, K, _ptr(q), _ptr(scale), _stream(stream)),
+           "moe_quantize_weights_fp8")
+
+
+def moe_fp8_merge_w13_scales(w13, w13_shard_scales, w13_scale, stream=None):
+    """w13 uint8 [E, 2I, H] with shard scales [E, 2] -> requantized in place under w13_scale [E] = the maxima."""
+    E, N2, H = w13.shape
+    _need(w13, torch.uint8, (E, N2, H), "w13")
+    _need(w13_shard_scales, torch.float32, (E, 2), "w13_shard_scales")
+    _need(w13_scale, torch.float32, (E,), "w13_scale")
+    _check(lib().moe_fp8_merge_w13_scales(_ptr(w13), _ptr(w13_shard_scales), E, N2 // 2, H, _ptr(w13_scale),
+                                          _stream(stream)), "moe_fp8_merge_w13_scales")
+
+
+def moe_wfp8a16_workspace_bytes(T, H, I, E, k, block_m=0, num_shared_experts=0,
+                                apply_router_weight_on_input=False) -> int:
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    return int(lib().moe_wfp8a16_workspace_bytes(T, H, I, E, k, block_m, ctypes.byref(o)))
+
+
+def _fp8_checked(x, w13, w13_scale, w2, w2_scale, S):
+    T, H, act = _need_act(x)
+    Et, N2, _ = w13.shape
+    I = N2 // 2
+    if S < 0 or S >= Et:
+        raise ValueError(f"num_shared_experts {S} must be in [0, {Et})")
+    _need(w13, torch.uint8, (Et, 2 * I, H), "w13")
+    _need(w13_scale, torch.float32, (Et,), "w13_scale")
+    _need(w2, torch.uint8, (Et, H, I), "w2")
+    _need(w2_scale, torch.float32, (Et,), "w2_scale")
+    return T, H, I, Et - S, act
+
+
+def moe_wfp8a16_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, workspace, num_shared_experts=0,
+                        apply_router_weight_on_input=False, block_m: int = 0, stream=None):
+    T, H, I, E, act = _fp8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
+    k = topk_ids.shape[1]
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    _need_bytes(workspace, moe_wfp8a16_workspace_bytes(T, H, I, E, k, block_m, num_shared_experts,
+                                                       apply_router_weight_on_input), "workspace")
+    _check(lib().moe_wfp8a16_forward(_ptr(x), act, T, H, I, E, k, _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                                     _ptr(w2_scale), _ptr(topk_w), _ptr(topk_ids), ctypes.byref(o), block_m, _ptr(out),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_wfp8a16_forward")
+
+
+def moe_wfp8a16_apply(x, router_logits, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, workspace,
+                      renormalize=True, scoring="softmax", num_expert_group=0, topk_group=0,
+                      e_score_correction_bias=None, routed_scaling_factor=1.0, num_shared_experts=0,
+                      apply_router_weight_on_input=False, block_m: int = 0, stream=None):
+    T, H, I, E, act = _fp8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
+    k = topk_ids.shape[1]
+    _need(router_logits, torch.float32, (T, E), "router_logits")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    r = routing_struct(E, renormalize, scoring, num_expert_group, topk_group, e_score_correction_bias,
+                       routed_scaling_factor)
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    _need_bytes(workspace, moe_wfp8a16_workspace_bytes(T, H, I, E, k, block_m, num_shared_experts,
+                                                       apply_router_weight_on_input), "workspace")
+    _check(lib().moe_wfp8a16_apply(_ptr(x), act, T, H, I, E, k, _ptr(router_logits), ctypes.byref(r), _ptr(w13),
+                                   _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), ctypes.byref(o), _ptr(topk_w),
+                                   _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)), "moe_wfp8a16_apply")

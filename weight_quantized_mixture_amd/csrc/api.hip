@@ -241,7 +241,7 @@ hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, h
   return moe::launch_gemm2_q16(p, gemm2_nt(T, p.H, E, k, p.block_m), q.hi, q.lo, q.scale, stream);
 }
 
-enum class Fmt { W8, W4 };
+enum class Fmt { W8, W4, FP8 };
 
 struct Layout {
   int64_t cap, nblocks, splits;
@@ -356,7 +356,9 @@ Opts opts_of(const moe_fused_opts* fo) {
 }
 
 int64_t splits_fmt(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
-  return fmt == Fmt::W8 ? splits_for(T, H, I, E, k, bm) : w4_splits(T, H, I, E, k, bm);
+  if (fmt == Fmt::W8) return splits_for(T, H, I, E, k, bm);
+  if (fmt == Fmt::W4) return w4_splits(T, H, I, E, k, bm);
+  return gemm2_splits(T, H, I, E, k, bm, true);     // fp8: the tiled GEMM2, equal parts
 }
 
 // Workspace of a layer call; 0 for bad sizes.
@@ -955,6 +957,84 @@ int moe_w4_import(int format, const int32_t* qweight, const int32_t* qzeros, con
   return hip_status(moe::launch_import_w4(format == MOE_W4_GPTQ, qweight, qzeros, scales, N, K, gout, repeat,
                                           out_qweight, out_scales, out_qzeros, stream),
                     "import_w4");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Weight-only fp8 (e4m3fn) experts
+// ---------------------------------------------------------------------------
+
+namespace {
+
+int forward_fp8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                const uint8_t* w13, const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                const float* logits, const moe_routing* routing, float* topk_w_out, int32_t* topk_ids_out,
+                const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* fo, int64_t block_m, void* out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T > 0 && (!w13 || !w13_scale || !w2 || !w2_scale || !out)) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (T > 0 && (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 8)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w13, w2 16-byte and out 8-byte alignment required");
+  Front F{};
+  int st = layer_front(Fmt::FP8, x, act_dtype, T, H, I, E, k, fo, logits, routing, topk_w_out, topk_ids_out, topk_w,
+                       topk_ids, block_m, workspace, workspace_bytes, stream, &F);
+  if (st != MOE_OK || F.T == 0) return st;
+  moe::Gemm1Args p1{};
+  p1.x = F.x; p1.f16 = act_dtype == MOE_FP16; p1.T = F.Tg; p1.H = H; p1.I = I; p1.k = F.kg; p1.Tk = F.Tk;
+  p1.w13 = reinterpret_cast<const int8_t*>(w13); p1.s13 = w13_scale; p1.ldw = H; p1.sorted_ids = F.sorted;
+  p1.block_expert = F.blocks; p1.num_padded = F.npad; p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap;
+  p1.a = F.a; p1.fp8 = 1;
+  hipError_t e = (F.bm == 16 || F.bm == 32) ? moe::launch_gemm1_w8_dma(p1, stream) : moe::launch_gemm1_w8(p1, stream);
+  if (e != hipSuccess) return hip_status(e, "gemm1_fp8");
+  moe::Gemm2Args p2{};
+  p2.a = F.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = reinterpret_cast<const int8_t*>(w2); p2.s2 = w2_scale;
+  p2.ldw = I; p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
+  p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y; p2.fp8 = 1;
+  if ((e = moe::launch_gemm2_w8(p2, stream)) != hipSuccess) return hip_status(e, "gemm2_fp8");
+  return layer_back(F, H, act_dtype, out, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_quantize_weights_fp8(const float* w, int64_t E, int64_t N, int64_t K, uint8_t* q, float* scale,
+                             hipStream_t stream) {
+  if (E < 1 || N < 1 || K < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "E, N and K must be >= 1");
+  if (E > 65535) return fail(MOE_ERR_UNSUPPORTED, "more than 65535 tensors");
+  if (!w || !q || !scale) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_quantize_fp8(w, E, N * K, q, scale, stream), "quantize_fp8");
+}
+
+int moe_fp8_merge_w13_scales(uint8_t* w13, const float* w13_shard_scales, int64_t E, int64_t I, int64_t H,
+                             float* w13_scale, hipStream_t stream) {
+  if (E < 1 || I < 1 || H < 1) return fail(MOE_ERR_INVALID_ARGUMENT, "E, I and H must be >= 1");
+  if (E > 65535) return fail(MOE_ERR_UNSUPPORTED, "more than 65535 experts");
+  if (!w13 || !w13_shard_scales || !w13_scale) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  return hip_status(moe::launch_fp8_merge_w13(w13, w13_shard_scales, E, I, H, w13_scale, stream), "fp8_merge");
+}
+
+size_t moe_wfp8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
+                                   const moe_fused_opts* opts) {
+  return workspace_for(Fmt::FP8, T, H, I, E, k, block_m, opts);
+}
+
+int moe_wfp8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                        const uint8_t* w13, const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                        const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* opts, int64_t block_m,
+                        void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_fp8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w2, w2_scale, nullptr, nullptr, nullptr, nullptr,
+                     topk_w, topk_ids, opts, block_m, out, workspace, workspace_bytes, stream);
+}
+
+int moe_wfp8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                      const float* router_logits, const moe_routing* routing, const uint8_t* w13,
+                      const float* w13_scale, const uint8_t* w2, const float* w2_scale, const moe_fused_opts* opts,
+                      float* topk_w, int32_t* topk_ids, int64_t block_m, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
+  return forward_fp8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w2, w2_scale, router_logits, routing, topk_w,
+                     topk_ids, nullptr, nullptr, opts, block_m, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

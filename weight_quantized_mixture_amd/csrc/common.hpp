@@ -149,6 +149,31 @@ __device__ __forceinline__ void i8x16_to_operands(u32x4 w, u32x4& lo, u32x4& hi)
   hi = u32x4{p2.x, p2.y, p3.x, p3.y};
 }
 
+// 16 OCP e4m3fn codes (one dwordx4) -> two 8-wide 16-bit MFMA operands in
+// natural K order, exact (e4m3 values have 4 significant bits and exponents
+// in [-9, 8], inside both bf16 and fp16).  gfx950's conversion instructions
+// take a code pair from the low (false) or high (true) half of a dword.
+template <bool kF16, bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_16x2(uint32_t w) {
+  if constexpr (kF16) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi));
+  else return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
+template <bool kF16>
+__device__ __forceinline__ void fp8x16_to_operands(u32x4 w, u32x4& lo, u32x4& hi) {
+  lo = u32x4{fp8x2_to_16x2<kF16, false>(w.x), fp8x2_to_16x2<kF16, true>(w.x), fp8x2_to_16x2<kF16, false>(w.y),
+             fp8x2_to_16x2<kF16, true>(w.y)};
+  hi = u32x4{fp8x2_to_16x2<kF16, false>(w.z), fp8x2_to_16x2<kF16, true>(w.z), fp8x2_to_16x2<kF16, false>(w.w),
+             fp8x2_to_16x2<kF16, true>(w.w)};
+}
+
+// 16 weight codes (int8 or e4m3fn) -> two 8-wide MFMA operands.
+template <bool kF16, bool kFP8>
+__device__ __forceinline__ void w8_operands(u32x4 w, u32x4& lo, u32x4& hi) {
+  if constexpr (kFP8) fp8x16_to_operands<kF16>(w, lo, hi);
+  else i8x16_to_operands<kF16>(w, lo, hi);
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }

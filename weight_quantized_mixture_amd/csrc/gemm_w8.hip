@@ -13,7 +13,9 @@
 //     chunks of 16*MT rows; every lane of a wave owns one weight row (MFMA
 //     column l%16) and a 32-byte slice of K (l/16), so one wave reads 16 rows x
 //     128 contiguous bytes of int8 per K step: whole cache lines, coalesced;
-//   * int8 codes become bf16/fp16 in registers (exact), the activation rows
+//   * int8 codes (or e4m3fn codes of the weight-only fp8 experts, fp8 page,
+//     Fp8MoEMethod: one scale per expert) become bf16/fp16 in registers
+//     (exact), the activation rows
 //     are gathered through sorted_ids straight into MFMA A operands;
 //   * the K order inside a step is permuted identically for A and B, which
 //     leaves the dot products unchanged;
@@ -34,7 +36,7 @@ namespace {
 constexpr int kGemmThreads = 256;
 constexpr int kKStep = 128;
 
-template <int MT, bool F16>
+template <int MT, bool F16, bool FP8>
 __global__ __launch_bounds__(kGemmThreads) void gemm1_w8_kernel(const Gemm1Args p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -49,8 +51,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_w8_kernel(const Gemm1Args 
   const int8_t* wg = p.w13 + (static_cast<int64_t>(e) * 2 * I + n0 + col) * p.ldw + kg * 32;
   const int8_t* wu = wg + I * p.ldw;
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
-  const float sg = p.s13[static_cast<int64_t>(e) * 2 * I + n0 + col];
-  const float su = p.s13[static_cast<int64_t>(e) * 2 * I + I + n0 + col];
+  const float sg = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + n0 + col];
+  const float su = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + I + n0 + col];
 
   for (int rc = 0; rc < p.block_m; rc += 16 * MT) {
     const uint16_t* xr[MT];
@@ -74,10 +76,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_w8_kernel(const Gemm1Args 
       const u32x4 u0 = *reinterpret_cast<const u32x4*>(wu + k0);
       const u32x4 u1 = *reinterpret_cast<const u32x4*>(wu + k0 + 16);
       u32x4 bg[4], bu[4];
-      i8x16_to_operands<F16>(g0, bg[0], bg[1]);
-      i8x16_to_operands<F16>(g1, bg[2], bg[3]);
-      i8x16_to_operands<F16>(u0, bu[0], bu[1]);
-      i8x16_to_operands<F16>(u1, bu[2], bu[3]);
+      w8_operands<F16, FP8>(g0, bg[0], bg[1]);
+      w8_operands<F16, FP8>(g1, bg[2], bg[3]);
+      w8_operands<F16, FP8>(u0, bu[0], bu[1]);
+      w8_operands<F16, FP8>(u1, bu[2], bu[3]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         u32x4 av[4];
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_w8_kernel(const Gemm1Args 
   }
 }
 
-template <int MT>
+template <int MT, bool FP8>
 __global__ __launch_bounds__(kGemmThreads) void gemm2_w8_kernel(const Gemm2Args p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -125,8 +127,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_w8_kernel(const Gemm2Args 
 
   const int8_t* w0 = p.w2 + (static_cast<int64_t>(e) * H + h0 + col) * p.ldw + kbeg + kg * 32;
   const int8_t* w1 = w0 + 16 * p.ldw;
-  const float s0 = p.s2[static_cast<int64_t>(e) * H + h0 + col];
-  const float s1 = p.s2[static_cast<int64_t>(e) * H + h0 + 16 + col];
+  const float s0 = FP8 ? p.s2[e] : p.s2[static_cast<int64_t>(e) * H + h0 + col];
+  const float s1 = FP8 ? p.s2[e] : p.s2[static_cast<int64_t>(e) * H + h0 + 16 + col];
 
   const uint16_t* a_hi = reinterpret_cast<const uint16_t*>(p.a);
   const uint16_t* a_lo = a_hi + p.cap * I;
@@ -146,10 +148,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_w8_kernel(const Gemm2Args 
       const u32x4 q10 = *reinterpret_cast<const u32x4*>(w1 + k0);
       const u32x4 q11 = *reinterpret_cast<const u32x4*>(w1 + k0 + 16);
       u32x4 b0[4], b1[4];
-      i8x16_to_operands<false>(q00, b0[0], b0[1]);
-      i8x16_to_operands<false>(q01, b0[2], b0[3]);
-      i8x16_to_operands<false>(q10, b1[0], b1[1]);
-      i8x16_to_operands<false>(q11, b1[2], b1[3]);
+      w8_operands<false, FP8>(q00, b0[0], b0[1]);
+      w8_operands<false, FP8>(q01, b0[2], b0[3]);
+      w8_operands<false, FP8>(q10, b1[0], b1[1]);
+      w8_operands<false, FP8>(q11, b1[2], b1[3]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -179,33 +181,43 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_w8_kernel(const Gemm2Args 
   }
 }
 
-template <int MT>
+template <int MT, bool FP8>
 hipError_t gemm1_dispatch_dtype(const Gemm1Args& p, dim3 grid, hipStream_t stream) {
   if (p.f16)
-    hipLaunchKernelGGL((gemm1_w8_kernel<MT, true>), grid, dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm1_w8_kernel<MT, true, FP8>), grid, dim3(kGemmThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm1_w8_kernel<MT, false>), grid, dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm1_w8_kernel<MT, false, FP8>), grid, dim3(kGemmThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int MT>
+hipError_t gemm1_dispatch_fmt(const Gemm1Args& p, dim3 grid, hipStream_t stream) {
+  return p.fp8 ? gemm1_dispatch_dtype<MT, true>(p, grid, stream) : gemm1_dispatch_dtype<MT, false>(p, grid, stream);
+}
+
+template <int MT>
+void gemm2_dispatch_fmt(const Gemm2Args& p, dim3 grid, hipStream_t stream) {
+  if (p.fp8)
+    hipLaunchKernelGGL((gemm2_w8_kernel<MT, true>), grid, dim3(kGemmThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm2_w8_kernel<MT, false>), grid, dim3(kGemmThreads), 0, stream, p);
 }
 
 }  // namespace
 
 hipError_t launch_gemm1_w8(const Gemm1Args& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.I / 64), static_cast<unsigned>(p.cap / p.block_m));
-  if (p.block_m % 64 == 0) return gemm1_dispatch_dtype<4>(p, grid, stream);
-  if (p.block_m % 32 == 0) return gemm1_dispatch_dtype<2>(p, grid, stream);
-  return gemm1_dispatch_dtype<1>(p, grid, stream);
+  if (p.block_m % 64 == 0) return gemm1_dispatch_fmt<4>(p, grid, stream);
+  if (p.block_m % 32 == 0) return gemm1_dispatch_fmt<2>(p, grid, stream);
+  return gemm1_dispatch_fmt<1>(p, grid, stream);
 }
 
 hipError_t launch_gemm2_w8(const Gemm2Args& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.H / 128), static_cast<unsigned>(p.cap / p.block_m),
                   static_cast<unsigned>(p.splits));
-  if (p.block_m % 64 == 0)
-    hipLaunchKernelGGL((gemm2_w8_kernel<4>), grid, dim3(kGemmThreads), 0, stream, p);
-  else if (p.block_m % 32 == 0)
-    hipLaunchKernelGGL((gemm2_w8_kernel<2>), grid, dim3(kGemmThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm2_w8_kernel<1>), grid, dim3(kGemmThreads), 0, stream, p);
+  if (p.block_m % 64 == 0) gemm2_dispatch_fmt<4>(p, grid, stream);
+  else if (p.block_m % 32 == 0) gemm2_dispatch_fmt<2>(p, grid, stream);
+  else gemm2_dispatch_fmt<1>(p, grid, stream);
   return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@
 // global_load_lds_dwordx4: per step every wave copies its own 32 weight rows
 // (4 KB) and the workgroup copies the block's activation rows (the gathered
 // bf16 rows, 256 bytes each).  Step s+2 is requested while step s is
-// converted (int8 -> bf16/fp16, exact) and multiplied, so the HBM requests
+// converted (int8 or e4m3fn -> bf16/fp16, exact) and multiplied, so the HBM requests
 // of a wave never wait for its own arithmetic, and nothing passes through
 // registers on the way to LDS.  One barrier per step, after each thread has
 // waited for its own copies of that step.
@@ -43,7 +43,8 @@ struct DecodeRing {
   static constexpr int kADma = kAStage / (kThreads * 16);   // = MT
 };
 
-template <int MT, bool F16>
+// FP8: w13 holds e4m3fn codes with one scale per expert (fp8 page, weight-only path).
+template <int MT, bool F16, bool FP8>
 __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p) {
   using R = DecodeRing<MT>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing * R::kStage];
@@ -131,10 +132,10 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p) 
       if (s + 2 < nst) issue(s + 2, slot == 0 ? 2 : slot - 1);
       const uint8_t* st = smem + slot * R::kStage;
       u32x4 bg[4], bu[4];
-      i8x16_to_operands<F16>(*reinterpret_cast<const u32x4*>(st + woff[0]), bg[0], bg[1]);
-      i8x16_to_operands<F16>(*reinterpret_cast<const u32x4*>(st + woff[1]), bg[2], bg[3]);
-      i8x16_to_operands<F16>(*reinterpret_cast<const u32x4*>(st + woff[2]), bu[0], bu[1]);
-      i8x16_to_operands<F16>(*reinterpret_cast<const u32x4*>(st + woff[3]), bu[2], bu[3]);
+      w8_operands<F16, FP8>(*reinterpret_cast<const u32x4*>(st + woff[0]), bg[0], bg[1]);
+      w8_operands<F16, FP8>(*reinterpret_cast<const u32x4*>(st + woff[1]), bg[2], bg[3]);
+      w8_operands<F16, FP8>(*reinterpret_cast<const u32x4*>(st + woff[2]), bu[0], bu[1]);
+      w8_operands<F16, FP8>(*reinterpret_cast<const u32x4*>(st + woff[3]), bu[2], bu[3]);
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p) 
   uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.a);
   uint16_t* a_lo = a_hi + p.cap * I;
   const int64_t n = n0 + col;
-  const float sg = p.s13[static_cast<int64_t>(e) * 2 * I + n];
-  const float su = p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
+  const float sg = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + n];
+  const float su = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt < ntiles) {
@@ -178,10 +179,17 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p) 
 template <int MT>
 hipError_t dma_launch(const Gemm1Args& p, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.I / 64), static_cast<unsigned>(p.cap / p.block_m));
-  if (p.f16)
-    hipLaunchKernelGGL((gemm1_dma_kernel<MT, true>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm1_dma_kernel<MT, false>), grid, dim3(kThreads), 0, stream, p);
+  if (p.fp8) {
+    if (p.f16)
+      hipLaunchKernelGGL((gemm1_dma_kernel<MT, true, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm1_dma_kernel<MT, false, true>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (p.f16)
+      hipLaunchKernelGGL((gemm1_dma_kernel<MT, true, false>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm1_dma_kernel<MT, false, false>), grid, dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ struct Gemm1Args {
   int block_m;
   int64_t cap;
   float* a;               // int8 path: two bf16 planes [2, cap, I] (hi, lo); uint4 path: fp32 [cap, I]
+  int fp8;                // w13 holds e4m3fn codes and s13 one scale per expert [E]
 };
 hipError_t launch_gemm1_w8(const Gemm1Args& p, hipStream_t stream);
 // Weight-streaming variant for block_m <= 64; kw = K-ways inside a workgroup (1, 2, 4).
@@ -66,6 +67,7 @@ struct Gemm2Args {
   int64_t cap;
   int splits;
   float* y;               // [splits, Tk, H]
+  int fp8;                // w2 holds e4m3fn codes and s2 one scale per expert [E]
 };
 hipError_t launch_gemm2_w8(const Gemm2Args& p, hipStream_t stream);
 // LDS-staged GEMM1 for blocks of 32 or 64 rows (kw <= 2 at 32, 1 at 64; ng = 16-column groups per wave).
@@ -145,6 +147,13 @@ hipError_t launch_prescale_input(const void* x, int f16, const float* topk_w, in
 hipError_t launch_import_w4(int gptq, const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                             int64_t N, int64_t K, int64_t group_out, int64_t repeat, int32_t* out_qweight,
                             uint16_t* out_scales, int32_t* out_qzeros, hipStream_t stream);
+
+// Per-tensor e4m3fn quantization of `tensors` fp32 tensors of per_tensor values (scale[t] = max|w| / 448).
+hipError_t launch_quantize_fp8(const float* w, int64_t tensors, int64_t per_tensor, uint8_t* q, float* scale,
+                               hipStream_t stream);
+// w13 codes [E, 2I, H] with shard scales [E, 2] -> codes under the larger scale, scales [E].
+hipError_t launch_fp8_merge_w13(uint8_t* q13, const float* s_in, int64_t E, int64_t I, int64_t H, float* s_out,
+                                hipStream_t stream);
 
 // Weighted top-k combine of the split partials.
 hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,

@@ -137,3 +137,50 @@ class W4A16MoE:
                           self.w2_qweight, self.w2_scales, self.w2_qzeros, self.group_size, self.topk_w,
                           self.topk_ids, out, ws, block_m)
         return out
+
+
+class WFP8A16MoE:
+    """Weight-only fp8 experts, named as on the fp8 page (Fp8MoEMethod.create_weights):
+    w13_weight / w2_weight (e4m3fn codes, uint8 here), w13_weight_scale / w2_weight_scale
+    (one fp32 scale per expert after process_weights_after_loading)."""
+
+    def __init__(self, num_experts: int, hidden_size: int, intermediate_size: int, device="cuda",
+                 params_dtype=torch.bfloat16):
+        E, H, I = num_experts, hidden_size, intermediate_size
+        self.E, self.H, self.I = E, H, I
+        self.params_dtype = params_dtype
+        self.w13_weight = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
+        self.w2_weight = torch.empty(E, H, I, dtype=torch.uint8, device=device)
+        self.w13_weight_scale = torch.zeros(E, dtype=torch.float32, device=device)
+        self.w2_weight_scale = torch.zeros(E, dtype=torch.float32, device=device)
+        self._ws = _Workspace()
+
+    def load_expert(self, e: int, w13_master: torch.Tensor, w2_master: torch.Tensor):
+        """Quantize one expert's 16/32-bit masters (scaled_fp8_quant: one scale for w13, one for w2)."""
+        B.moe_quantize_weights_fp8(w13_master.reshape(1, 2 * self.I, self.H).float().contiguous(),
+                                   self.w13_weight[e:e + 1], self.w13_weight_scale[e:e + 1])
+        B.moe_quantize_weights_fp8(w2_master.reshape(1, self.H, self.I).float().contiguous(),
+                                   self.w2_weight[e:e + 1], self.w2_weight_scale[e:e + 1])
+
+    route = W8A16MoE.route
+
+    def forward_topk(self, x, topk_w, topk_ids, out=None, block_m: int = 0):
+        T, k = x.shape[0], topk_ids.shape[1]
+        if out is None:
+            out = torch.empty_like(x)
+        ws = self._ws.get(B.moe_wfp8a16_workspace_bytes(T, self.H, self.I, self.E, k, block_m), x.device)
+        B.moe_wfp8a16_forward(x, self.w13_weight, self.w13_weight_scale, self.w2_weight, self.w2_weight_scale,
+                              topk_w, topk_ids, out, ws, block_m=block_m)
+        return out
+
+    def apply(self, x, router_logits, top_k: int, renormalize: bool = True, inplace: bool = False,
+              block_m: int = 0):
+        T = x.shape[0]
+        out = x if inplace else torch.empty_like(x)
+        self.topk_w = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+        self.topk_ids = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+        ws = self._ws.get(B.moe_wfp8a16_workspace_bytes(T, self.H, self.I, self.E, top_k, block_m), x.device)
+        B.moe_wfp8a16_apply(x, router_logits, self.w13_weight, self.w13_weight_scale, self.w2_weight,
+                            self.w2_weight_scale, self.topk_w, self.topk_ids, out, ws, renormalize=renormalize,
+                            block_m=block_m)
+        return out
