@@ -473,6 +473,56 @@ def moe_forward_w4(x: np.ndarray, qw13, s13, z13, qw2, s2, z2, group_size: int,
 
 
 # ---------------------------------------------------------------------------
+# W8A8: int8 weights with int8 activations quantized per token
+# ---------------------------------------------------------------------------
+# fused_moe oracle/int8 page, ``select_int8_moe_backend``: the int8 MoE kernels' default keys
+# are static per-channel symmetric int8 weights (``kInt8StaticChannelSym``, the experts_int8
+# weights above) and dynamic per-token symmetric int8 activations (``kInt8DynamicTokenSym``).
+# The activation quantizer is not printed; reading: the per-row rule of the weights
+# (``quantize_in_place_and_get_scales``) applied to every token row of the GEMM's input, in
+# fp32: GEMM1's input x and GEMM2's input a = silu(h_gate) * h_up, one row per assignment.
+
+
+def quantize_act_int8_rows(a) -> tuple:
+    """Dynamic per-token symmetric int8 codes of the rows of a (any float dtype, taken to fp32):
+    scale = max|row| / 127, code = clamp(rint(row / scale), -127, 127) in fp32; a zero row gets
+    scale 0 and codes 0 (``quantize_int8_rows``)."""
+    return quantize_int8_rows(np.asarray(a, np.float64).astype(np.float32))
+
+
+def moe_forward_w8a8(x, q13, s13, q2, s2, topk_w, topk_ids, weight_on_input=False, num_shared=0):
+    """The W8A8 layer: per assignment (t, e) with weight w,
+    x8, sx = quant(x_t) (or quant(w x_t) with ``weight_on_input``, w x_t rounded to fp32 first);
+    h = sx * s13[e] * (q13[e] x8) (exact integer sums); a = silu(h_gate) * h_up;
+    a8, sa = quant(fp32(a)); y = sa * s2[e] * (q2[e] a8); out_t += w y (1 with ``weight_on_input``).
+    fp64 apart from the two quantizations.  Options as ``moe_forward_w8``."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    E = q13.shape[0]
+    I = q13.shape[1] // 2
+    w, ids = _extend_routing(topk_w, topk_ids, E, num_shared)
+    ids = np.asarray(ids).reshape(T, -1)
+    w = np.asarray(w, np.float64).reshape(T, -1)
+    out = np.zeros((T, H), np.float64)
+    for e in np.unique(ids):
+        e = int(e)
+        if not 0 <= e < E:
+            continue
+        t_idx, j_idx = np.nonzero(ids == e)
+        wt = w[t_idx, j_idx][:, None]
+        xin = (wt * x[t_idx]).astype(np.float32) if weight_on_input else x[t_idx]
+        xq, sx = quantize_act_int8_rows(xin)
+        acc1 = xq.astype(np.int64) @ q13[e].astype(np.int64).T                  # exact
+        h = acc1.astype(np.float64) * sx.astype(np.float64)[:, None] * np.asarray(s13[e], np.float64)[None, :]
+        a = silu(h[:, :I]) * h[:, I:]
+        aq, sa = quantize_act_int8_rows(a)
+        acc2 = aq.astype(np.int64) @ q2[e].astype(np.int64).T
+        y = acc2.astype(np.float64) * sa.astype(np.float64)[:, None] * np.asarray(s2[e], np.float64)[None, :]
+        np.add.at(out, t_idx, y if weight_on_input else wt * y)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Weight-only fp8 (OCP e4m3fn) experts with per-tensor scales
 # ---------------------------------------------------------------------------
 # fp8 page (vllm ... quantization.fp8): ``Fp8MoEMethod.create_weights`` (w13 [E, 2I, H] and
