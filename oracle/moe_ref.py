@@ -490,6 +490,36 @@ def quantize_act_int8_rows(a) -> tuple:
     return quantize_int8_rows(np.asarray(a, np.float64).astype(np.float32))
 
 
+def _w8a8_expert_rows(xin, q13e, s13e, I):
+    """GEMM1 of one expert on int8 input codes and the quantized intermediate: (a8, sa)."""
+    xq, sx = quantize_act_int8_rows(xin)
+    acc1 = xq.astype(np.int64) @ q13e.astype(np.int64).T                        # exact
+    h = acc1.astype(np.float64) * sx.astype(np.float64)[:, None] * np.asarray(s13e, np.float64)[None, :]
+    a = silu(h[:, :I]) * h[:, I:]
+    return quantize_act_int8_rows(a)
+
+
+def moe_w8a8_intermediate_scales(x, q13, s13, topk_w, topk_ids, weight_on_input=False, num_shared=0):
+    """The per-assignment scales sa of the quantized intermediate in ``moe_forward_w8a8``, as [T, k + S]
+    (0 for dropped ids): one step of an intermediate code moves y by sa * W2[:, i]."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    E = q13.shape[0]
+    I = q13.shape[1] // 2
+    w, ids = _extend_routing(topk_w, topk_ids, E, num_shared)
+    ids = np.asarray(ids).reshape(T, -1)
+    w = np.asarray(w, np.float64).reshape(T, -1)
+    out = np.zeros(ids.shape, np.float64)
+    for e in np.unique(ids):
+        e = int(e)
+        if not 0 <= e < E:
+            continue
+        t_idx, j_idx = np.nonzero(ids == e)
+        xin = (w[t_idx, j_idx][:, None] * x[t_idx]).astype(np.float32) if weight_on_input else x[t_idx]
+        out[t_idx, j_idx] = _w8a8_expert_rows(xin, q13[e], s13[e], I)[1]
+    return out
+
+
 def moe_forward_w8a8(x, q13, s13, q2, s2, topk_w, topk_ids, weight_on_input=False, num_shared=0):
     """The W8A8 layer: per assignment (t, e) with weight w,
     x8, sx = quant(x_t) (or quant(w x_t) with ``weight_on_input``, w x_t rounded to fp32 first);
@@ -511,11 +541,7 @@ def moe_forward_w8a8(x, q13, s13, q2, s2, topk_w, topk_ids, weight_on_input=Fals
         t_idx, j_idx = np.nonzero(ids == e)
         wt = w[t_idx, j_idx][:, None]
         xin = (wt * x[t_idx]).astype(np.float32) if weight_on_input else x[t_idx]
-        xq, sx = quantize_act_int8_rows(xin)
-        acc1 = xq.astype(np.int64) @ q13[e].astype(np.int64).T                  # exact
-        h = acc1.astype(np.float64) * sx.astype(np.float64)[:, None] * np.asarray(s13[e], np.float64)[None, :]
-        a = silu(h[:, :I]) * h[:, I:]
-        aq, sa = quantize_act_int8_rows(a)
+        aq, sa = _w8a8_expert_rows(xin, q13[e], s13[e], I)
         acc2 = aq.astype(np.int64) @ q2[e].astype(np.int64).T
         y = acc2.astype(np.float64) * sa.astype(np.float64)[:, None] * np.asarray(s2[e], np.float64)[None, :]
         np.add.at(out, t_idx, y if weight_on_input else wt * y)

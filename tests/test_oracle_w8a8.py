@@ -91,3 +91,17 @@ def test_dense_masked_sum_and_options():
     shared = oracle.moe_forward_w8a8(x, q13, s13, q2, s2, np.ones((x.shape[0], 1)),
                                      np.full((x.shape[0], 1), E - 1, np.int32))
     np.testing.assert_allclose(both, routed + shared, rtol=1e-12, atol=1e-15)
+
+
+def test_intermediate_scales():
+    """The scales the W8A8 forward quantizes its intermediate with: y of one assignment is
+    sa * s2 * (q2 a8), so a routed token's output equals the sum over its assignments."""
+    g = _g()
+    sa = oracle.moe_w8a8_intermediate_scales(np.array(g["x"]), np.array(g["q13"], np.int8),
+                                             np.array(g["s13"], np.float32), np.ones((2, 1)),
+                                             np.zeros((2, 1), np.int32))
+    np.testing.assert_array_equal(sa[:, 0], [r["a_scale"] for r in g["rows"]])
+    x, q13, s13, q2, s2, w, ids = _layer(seed=8)
+    ids2 = ids.copy(); ids2[0, 1] = -1
+    sa = oracle.moe_w8a8_intermediate_scales(x, q13, s13, w, ids2)
+    assert sa[0, 1] == 0 and np.all(sa[1:] > 0)
