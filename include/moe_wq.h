@@ -473,6 +473,39 @@ int moe_wfp8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_
                       const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids, int64_t block_m,
                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * W8A8: the int8 experts above with int8 activations (fused_moe oracle/int8
+ * page, select_int8_moe_backend: default keys kInt8StaticChannelSym for the
+ * weights, kInt8DynamicTokenSym for the activations).  Both GEMM inputs are
+ * quantized per row (token / assignment) with the weights' rule:
+ * s = max|row| / 127, code = clamp(rint(v / s), -127, 127) in fp32 (IEEE
+ * divide, half to even; a zero row gets s = 0 and codes 0):
+ *   x8, sx = quant(x_t);  h = sx * w13_scale[e,n] * sum_c x8[c] w13[e,n,c] (exact int32)
+ *   a = silu(h_gate) * h_up (fp32);  a8, sa = quant(a)
+ *   y = sa * w2_scale[e,h] * sum_i a8[i] w2[e,h,i];  out_t = sum_j w_j y.
+ * moe_quantize_act_int8: the activation quantizer alone (x device bf16/fp16
+ * [T, H], H a multiple of 4; q device int8 [T, H], 4-byte aligned; scale
+ * device fp32 [T]).
+ * moe_w8a8_forward / moe_w8a8_apply: the layer, with arguments, options and
+ * requirements as moe_w8a16_forward_ex / moe_w8a16_apply_ex (the same int8
+ * weights and scales).  Workspace: moe_w8a8_workspace_bytes.
+ * ---------------------------------------------------------------------- */
+int moe_quantize_act_int8(const void* x, int act_dtype, int64_t T, int64_t H, int8_t* q, float* scale,
+                          hipStream_t stream);
+size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
+                                const moe_fused_opts* opts);
+int moe_w8a8_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                     const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                     const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                     const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* opts,
+                     int64_t block_m, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int moe_w8a8_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                   const float* router_logits, const moe_routing* routing,
+                   const int8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                   const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                   const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids, int64_t block_m,
+                   void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,10 @@ from .binding import (  # noqa: F401
     moe_wfp8a16_apply,
     moe_wfp8a16_forward,
     moe_wfp8a16_workspace_bytes,
+    moe_quantize_act_int8,
+    moe_w8a8_apply,
+    moe_w8a8_forward,
+    moe_w8a8_workspace_bytes,
     moe_w4_import,
     moe_wna16_group_size,
     moe_w4a16_apply,

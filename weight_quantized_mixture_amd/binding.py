@@ -51,6 +51,14 @@ SIGNATURES = {
                                  _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_w8a16_splits": (_c_i64, [_c_i64] * 6),
+    "moe_quantize_act_int8": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "moe_w8a8_workspace_bytes": (_c_size, [_c_i64] * 6 + [_c_p]),
+    "moe_w8a8_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
+                                  _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                  _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+    "moe_w8a8_apply": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
+                                _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64,
+                                _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
     "moe_quantize_weights_fp8": (_c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "moe_fp8_merge_w13_scales": (_c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "moe_wfp8a16_workspace_bytes": (_c_size, [_c_i64] * 6 + [_c_p]),
@@ -715,3 +723,59 @@ def moe_wfp8a16_apply(x, router_logits, w13, w13_scale, w2, w2_scale, topk_w, to
                                    _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), ctypes.byref(o), _ptr(topk_w),
                                    _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)), "moe_wfp8a16_apply")
+
+
+# ---------------------------------------------------------------------------
+# W8A8: int8 weights, int8 activations quantized per token
+# ---------------------------------------------------------------------------
+
+
+def moe_quantize_act_int8(x, q, scale, stream=None):
+    """Per-token int8 codes q int8 [T, H] and scales fp32 [T] of the bf16/fp16 activations x [T, H]."""
+    T, H, act = _need_act(x)
+    _need(q, torch.int8, (T, H), "q")
+    _need(scale, torch.float32, (T,), "scale")
+    _check(lib().moe_quantize_act_int8(_ptr(x), act, T, H, _ptr(q), _ptr(scale), _stream(stream)),
+           "moe_quantize_act_int8")
+
+
+def moe_w8a8_workspace_bytes(T, H, I, E, k, block_m=0, num_shared_experts=0, apply_router_weight_on_input=False):
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    return int(lib().moe_w8a8_workspace_bytes(T, H, I, E, k, block_m, ctypes.byref(o)))
+
+
+def moe_w8a8_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, workspace, num_shared_experts=0,
+                     apply_router_weight_on_input=False, block_m: int = 0, stream=None):
+    T, H, I, E, act, ld13, ld2 = _w8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
+    k = topk_ids.shape[1]
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    _need_bytes(workspace, moe_w8a8_workspace_bytes(T, H, I, E, k, block_m, num_shared_experts,
+                                                    apply_router_weight_on_input), "workspace")
+    _check(lib().moe_w8a8_forward(_ptr(x), act, T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13, _ptr(w2),
+                                  _ptr(w2_scale), ld2, _ptr(topk_w), _ptr(topk_ids), ctypes.byref(o), block_m,
+                                  _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)), "moe_w8a8_forward")
+
+
+def moe_w8a8_apply(x, router_logits, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, workspace,
+                   renormalize=True, scoring="softmax", num_expert_group=0, topk_group=0, e_score_correction_bias=None,
+                   routed_scaling_factor=1.0, num_shared_experts=0, apply_router_weight_on_input=False,
+                   block_m: int = 0, stream=None):
+    T, H, I, E, act, ld13, ld2 = _w8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
+    k = topk_ids.shape[1]
+    _need(router_logits, torch.float32, (T, E), "router_logits")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(topk_ids, torch.int32, (T, k), "topk_ids")
+    _need(out, x.dtype, (T, H), "out")
+    r = routing_struct(E, renormalize, scoring, num_expert_group, topk_group, e_score_correction_bias,
+                       routed_scaling_factor)
+    o = fused_opts(num_shared_experts, apply_router_weight_on_input)
+    _need_bytes(workspace, moe_w8a8_workspace_bytes(T, H, I, E, k, block_m, num_shared_experts,
+                                                    apply_router_weight_on_input), "workspace")
+    _check(lib().moe_w8a8_apply(_ptr(x), act, T, H, I, E, k, _ptr(router_logits), ctypes.byref(r), _ptr(w13),
+                                _ptr(w13_scale), ld13, _ptr(w2), _ptr(w2_scale), ld2, ctypes.byref(o), _ptr(topk_w),
+                                _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)), "moe_w8a8_apply")

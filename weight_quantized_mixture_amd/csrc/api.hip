@@ -241,7 +241,35 @@ hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, h
   return moe::launch_gemm2_q16(p, gemm2_nt(T, p.H, E, k, p.block_m), q.hi, q.lo, q.scale, stream);
 }
 
-enum class Fmt { W8, W4, FP8 };
+enum class Fmt { W8, W4, FP8, W8A8 };
+
+// W8A8 intermediate: the GEMM1 input's int8 codes [xrows, H] and scales
+// [xrows], the fp32 intermediate a [cap, I], its codes [cap, I] and scales [cap].
+struct A8 {
+  int8_t* qx;
+  float* sx;
+  float* a;
+  int8_t* qa;
+  float* sa;
+};
+
+size_t w8a8_bytes(int64_t cap, int64_t I, int64_t xrows, int64_t H) {
+  const size_t c = static_cast<size_t>(cap), r = static_cast<size_t>(xrows);
+  return align_up(r * static_cast<size_t>(H)) + align_up(r * 4) + align_up(c * static_cast<size_t>(I) * 4) +
+         align_up(c * static_cast<size_t>(I)) + align_up(c * 4);
+}
+
+A8 w8a8_at(float* base, int64_t cap, int64_t I, int64_t xrows, int64_t H) {
+  char* b = reinterpret_cast<char*>(base);
+  const size_t c = static_cast<size_t>(cap), r = static_cast<size_t>(xrows);
+  A8 v{};
+  v.qx = reinterpret_cast<int8_t*>(b);  b += align_up(r * static_cast<size_t>(H));
+  v.sx = reinterpret_cast<float*>(b);   b += align_up(r * 4);
+  v.a = reinterpret_cast<float*>(b);    b += align_up(c * static_cast<size_t>(I) * 4);
+  v.qa = reinterpret_cast<int8_t*>(b);  b += align_up(c * static_cast<size_t>(I));
+  v.sa = reinterpret_cast<float*>(b);
+  return v;
+}
 
 struct Layout {
   int64_t cap, nblocks, splits;
@@ -263,7 +291,8 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm,
   L.off_sorted = o; o += align_up(static_cast<size_t>(L.cap) * 4);
   L.off_block = o;  o += align_up(static_cast<size_t>(L.nblocks) * 4);
   L.off_npad = o;   o += align_up(4);
-  L.off_a = o;      o += intermediate_bytes(L.cap, I, bm, fmt == Fmt::W8);
+  L.off_a = o;
+  o += fmt == Fmt::W8A8 ? w8a8_bytes(L.cap, I, woi ? T * k : T, H) : intermediate_bytes(L.cap, I, bm, fmt == Fmt::W8);
   L.off_y = o;      o += align_up(static_cast<size_t>(splits) * Tk * static_cast<size_t>(H) * 4);
   if (expand) {
     L.off_ids_ext = o; o += align_up(Tk * 4);
@@ -358,7 +387,7 @@ Opts opts_of(const moe_fused_opts* fo) {
 int64_t splits_fmt(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
   if (fmt == Fmt::W8) return splits_for(T, H, I, E, k, bm);
   if (fmt == Fmt::W4) return w4_splits(T, H, I, E, k, bm);
-  return gemm2_splits(T, H, I, E, k, bm, true);     // fp8: the tiled GEMM2, equal parts
+  return gemm2_splits(T, H, I, E, k, bm, true);     // fp8, W8A8: the tiled GEMM2, equal parts
 }
 
 // Workspace of a layer call; 0 for bad sizes.
@@ -1035,6 +1064,93 @@ int moe_wfp8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_
   if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
   return forward_fp8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w2, w2_scale, router_logits, routing, topk_w,
                      topk_ids, nullptr, nullptr, opts, block_m, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// W8A8: int8 weights, int8 activations quantized per token
+// ---------------------------------------------------------------------------
+
+namespace {
+
+int forward_w8a8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                 const int8_t* w13, const float* w13_scale, int64_t w13_row_stride, const int8_t* w2,
+                 const float* w2_scale, int64_t w2_row_stride, const float* logits, const moe_routing* routing,
+                 float* topk_w_out, int32_t* topk_ids_out, const float* topk_w, const int32_t* topk_ids,
+                 const moe_fused_opts* fo, int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  const int64_t ld13 = w13_row_stride ? w13_row_stride : H;
+  const int64_t ld2 = w2_row_stride ? w2_row_stride : I;
+  if (ld13 < H || ld13 % 16 || ld2 < I || ld2 % 16)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "row strides must cover the row and be multiples of 16");
+  if (T > 0 && (!w13 || !w13_scale || !w2 || !w2_scale || !out)) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (T > 0 && (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 8)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w13, w2 16-byte and out 8-byte alignment required");
+  Front F{};
+  int st = layer_front(Fmt::W8A8, x, act_dtype, T, H, I, E, k, fo, logits, routing, topk_w_out, topk_ids_out, topk_w,
+                       topk_ids, block_m, workspace, workspace_bytes, stream, &F);
+  if (st != MOE_OK || F.T == 0) return st;
+  const A8 v = w8a8_at(F.a, F.cap, I, F.Tg, H);
+  hipError_t e = moe::launch_act_quant(F.x, act_dtype == MOE_FP16 ? 1 : 0, F.Tg, H, nullptr, nullptr, 0, v.qx, v.sx,
+                                       stream);
+  if (e != hipSuccess) return hip_status(e, "quantize x");
+  moe::Gemm1Args p1{};
+  p1.x = F.x; p1.f16 = act_dtype == MOE_FP16; p1.T = F.Tg; p1.H = H; p1.I = I; p1.k = F.kg; p1.Tk = F.Tk;
+  p1.w13 = w13; p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = F.sorted; p1.block_expert = F.blocks;
+  p1.num_padded = F.npad; p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap; p1.a = v.a;
+  if ((e = moe::launch_gemm1_w8a8(p1, v.qx, v.sx, stream)) != hipSuccess) return hip_status(e, "gemm1_w8a8");
+  e = moe::launch_act_quant(v.a, 2, F.cap, I, F.sorted, F.npad, F.Tk, v.qa, v.sa, stream);
+  if (e != hipSuccess) return hip_status(e, "quantize a");
+  moe::Gemm2Args p2{};
+  p2.a = v.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = w2; p2.s2 = w2_scale; p2.ldw = ld2;
+  p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
+  p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y;
+  if ((e = moe::launch_gemm2_w8a8(p2, v.qa, v.sa, stream)) != hipSuccess) return hip_status(e, "gemm2_w8a8");
+  return layer_back(F, H, act_dtype, out, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_quantize_act_int8(const void* x, int act_dtype, int64_t T, int64_t H, int8_t* q, float* scale,
+                          hipStream_t stream) {
+  int st;
+  if ((st = check_act(act_dtype)) != MOE_OK) return st;
+  if (T < 0 || H < 1 || H % 4) return fail(MOE_ERR_INVALID_ARGUMENT, "need T >= 0 and H a positive multiple of 4");
+  if (T == 0) return ok();
+  if (!x || !q || !scale) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "q must be 4-byte aligned");
+  return hip_status(moe::launch_act_quant(x, act_dtype == MOE_FP16 ? 1 : 0, T, H, nullptr, nullptr, 0, q, scale,
+                                          stream),
+                    "quantize_act_int8");
+}
+
+size_t moe_w8a8_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
+                                const moe_fused_opts* opts) {
+  return workspace_for(Fmt::W8A8, T, H, I, E, k, block_m, opts);
+}
+
+int moe_w8a8_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                     const int8_t* w13, const float* w13_scale, int64_t w13_row_stride, const int8_t* w2,
+                     const float* w2_scale, int64_t w2_row_stride, const float* topk_w, const int32_t* topk_ids,
+                     const moe_fused_opts* opts, int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  return forward_w8a8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                      nullptr, nullptr, nullptr, nullptr, topk_w, topk_ids, opts, block_m, out, workspace,
+                      workspace_bytes, stream);
+}
+
+int moe_w8a8_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                   const float* router_logits, const moe_routing* routing, const int8_t* w13, const float* w13_scale,
+                   int64_t w13_row_stride, const int8_t* w2, const float* w2_scale, int64_t w2_row_stride,
+                   const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids, int64_t block_m, void* out,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
+  return forward_w8a8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                      router_logits, routing, topk_w, topk_ids, nullptr, nullptr, opts, block_m, out, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"
