@@ -274,31 +274,29 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * f = sorted_ids[r] < T*k, t = f / k, e = block_expert[r / block_m]:
  *   v[r, i] = silu(h_i) * h_{I+i},  h_n = w13_scale[e,n] * sum_c x[t,c] w13[e,n,c]
  * `a` is the intermediate, device memory of moe_w8a16_intermediate_bytes
- * bytes (16-byte aligned; passed as float*).  gemm1 writes its first part,
- * two bf16 planes [2, cap, I] (hi plane first), hi = rne(v) and
- * lo = rne(v - hi) (16 significant bits), cap = moe_align_capacity.  Padding
- * rows of a block that holds rows get v = 0; 16-row groups made only of
- * padding may be left unwritten (GEMM2 never reads them).
- * Exception: block_m = 256 with H a multiple of 256 and (T+1)*H*2 < 2^32
- * (the prefill form): gemm1 writes the 16-bit fixed-point form described
- * under moe_w8a16_requant directly, starting at byte offset 0 of `a`, and
- * no planes.
+ * bytes (16-byte aligned; passed as float*), cap = moe_align_capacity.  The
+ * 16-bit fixed-point form of v is: int8 hi codes [cap, I], then int8 lo codes
+ * [cap, I] (each region rounded up to 256 bytes), then fp32 scales
+ * [cap, I/g], with v ~= s[r, i/g] * (256 * hi + lo), s = max |v| over the
+ * g-column group / 32639 and |error| <= s/2.  What gemm1 writes:
+ *   block_m 16 or 32: the fixed-point form with g = 64, at offset 0;
+ *   block_m 256 with H a multiple of 256 and (T+1)*H*2 < 2^32 (the prefill
+ *     form): the fixed-point form with g = 128, at offset 0;
+ *   otherwise: two bf16 planes [2, cap, I] (hi plane first), hi = rne(v) and
+ *     lo = rne(v - hi) (16 significant bits).
+ * Padding rows of a block that holds rows get v = 0; 16-row groups made only
+ * of padding may be left unwritten (GEMM2 never reads them).
  *
- * moe_w8a16_requant: for block_m in [32, 64] (a no-op otherwise) turns the
- * planes into the 16-bit fixed-point form the integer GEMM2 reads, stored
- * right after them (at byte offset round_up(4*cap*I, 256)): int8 hi codes
- * [cap, I], then int8 lo codes [cap, I] (each region rounded up to 256
- * bytes), then fp32 scales [cap, I/128], with
- * v ~= s[r, i/128] * (256 * hi + lo), s = max |v| over the 128-column group
- * / 32639 and |error| <= s/2 (the same rows as gemm1).
+ * moe_w8a16_requant: for block_m in (32, 64] (a no-op otherwise) turns the
+ * planes into the fixed-point form with g = 128, stored right after them (at
+ * byte offset round_up(4*cap*I, 256)), for the same rows as gemm1.
  *
  * moe_w8a16_gemm2: for every valid padded row r (f = sorted_ids[r] < T*k),
  * split s < splits, h < H:
  *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} v[r, i] w2[e,h,i]
  * with v as moe_w8a16_gemm1 and moe_w8a16_requant left it in `a` (the
- * fixed-point form for block_m in [32, 64] and for the prefill form of
- * block_m = 256; the hi + lo planes otherwise, which for block_m = 16 GEMM2
- * rounds to the same fixed-point form itself).  The K range [0, I) is cut
+ * fixed-point form for block_m up to 64 and for the prefill form of
+ * block_m = 256; the hi + lo planes otherwise).  The K range [0, I) is cut
  * into `splits` parts of whole 128-wide steps (1 <= splits <= I/128; part z
  * covers steps [z*(I/128)/splits, (z+1)*(I/128)/splits) in integer division;
  * block_m > 64 needs equal parts, so splits must divide I/128, except for

@@ -127,20 +127,26 @@ def test_other_argument_errors():
     assert L.moe_w8a16_requant(p(FAKE), 4, 500, 8, 2, p(FAKE), p(FAKE), 32, None) == \
         B.MOE_ERR_INVALID_ARGUMENT                         # I not a multiple of 128
     assert L.moe_w8a16_requant(p(FAKE), 4, 512, 8, 2, p(FAKE), p(FAKE), 40, None) == B.MOE_ERR_UNSUPPORTED
-    assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 32, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 64, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 32, None) == B.MOE_OK    # GEMM1 wrote the form
     assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 128, None) == B.MOE_OK   # nothing to do at 128
     assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 16, None) == B.MOE_OK    # nor at 16
     assert L.moe_w8a16_requant(None, 0, 512, 8, 2, None, None, 32, None) == B.MOE_OK
 
 
 def test_intermediate_bytes():
-    """bf16 planes, plus the fixed-point codes and scales for blocks of 32 to 64 rows."""
+    """Blocks of 16 / 32 rows: the fixed-point codes and scales per 64 columns only; 48 / 64 rows:
+    bf16 planes plus the fixed-point codes and scales per 128 columns; other sizes: the planes."""
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    for T, E, k, bm, I in [(4, 8, 2, 16, 512), (64, 8, 2, 32, 14336), (300, 8, 2, 128, 1024), (9, 64, 6, 64, 1408)]:
+    for T, E, k, bm, I in [(4, 8, 2, 16, 512), (64, 8, 2, 32, 14336), (300, 8, 2, 128, 1024), (9, 64, 6, 64, 1408),
+                           (40, 8, 2, 48, 768)]:
         cap = B.moe_align_capacity(T, k, E, bm)
-        want = up(4 * cap * I)
-        if 32 <= bm <= 64:
-            want += 2 * up(cap * I) + up(cap * (I // 128) * 4)
+        if bm in (16, 32):
+            want = 2 * up(cap * I) + up(cap * (I // 64) * 4)
+        else:
+            want = up(4 * cap * I)
+            if 32 < bm <= 64:
+                want += 2 * up(cap * I) + up(cap * (I // 128) * 4)
         assert B.moe_w8a16_intermediate_bytes(T, 4096, I, E, k, bm) == want
     assert B.moe_w8a16_intermediate_bytes(0, 4096, 512, 8, 2, 16) == 0
 

@@ -209,7 +209,7 @@ def test_gemm1_q16_blocks_of_256(act):
     assert checked == T * k
 
 
-@pytest.mark.parametrize("act,bm", [("bf16", 16), ("fp16", 32), ("bf16", 64), ("bf16", 48)])
+@pytest.mark.parametrize("act,bm", [("bf16", 16), ("fp16", 32), ("fp16", 16), ("bf16", 64), ("bf16", 48)])
 def test_gemm1_intermediate(act, bm):
     E, k, H, I, T = 8, 2, 384, 640, 29
     log(f"[gemm1] act={act} bm={bm} E={E} H={H} I={I} T={T}")
@@ -231,11 +231,39 @@ def test_gemm1_intermediate(act, bm):
     torch.cuda.synchronize()
     sr, br, nr = oracle.align_block(ids_ref, E, bm)
     raw = a.cpu().numpy().view(np.uint8)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    xf = oracle.act_bits_to_f64(xb, act)
+    if bm in (16, 32):
+        # GEMM1 writes the 16-bit fixed-point form itself, groups of 64 columns, at offset 0
+        qh = raw[:cap * I].view(np.int8).reshape(cap, I).astype(np.int64)
+        ql = raw[up(cap * I):up(cap * I) + cap * I].view(np.int8).reshape(cap, I).astype(np.int64)
+        o = 2 * up(cap * I)
+        qs = raw[o:o + cap * (I // 64) * 4].view(np.float32).reshape(cap, I // 64).astype(np.float64)
+        assert qh.min() >= -127 and qh.max() <= 127
+        checked = 0
+        for blk in range(nr // bm):
+            W13 = oracle.dequant_int8_rows(W.q13[br[blk]], W.hs13[br[blk]])
+            rows = sr[blk * bm:(blk + 1) * bm]
+            for r_local in range(16 * ((np.sum(rows < T * k) + 15) // 16)):
+                r = blk * bm + r_local
+                f = rows[r_local]
+                if f >= T * k:
+                    assert np.all(qh[r] == 0) and np.all(ql[r] == 0) and np.all(qs[r] == 0.0)
+                    continue
+                ref = oracle.moe_expert_intermediate(xf[f // k][None], W13, I)[0]
+                gmax = np.abs(ref).reshape(-1, 64).max(axis=1)
+                assert np.allclose(qs[r], gmax / 32639.0, rtol=1e-4, atol=0.0), (blk, r_local)
+                sc = np.repeat(qs[r], 64)
+                vq = sc * (256.0 * qh[r] + ql[r])
+                tol = 0.51 * sc + 2e-5 * np.abs(ref).max() + 1e-4 * np.abs(ref)
+                assert np.all(np.abs(vq - ref) <= tol), (blk, r_local, np.abs(vq - ref).max())
+                checked += 1
+        assert checked == T * k
+        return
     planes = raw[:4 * cap * I].view(np.uint16).reshape(2, cap, I)
     a_g = oracle.bf16_bits_to_f64(planes[0]) + oracle.bf16_bits_to_f64(planes[1])
-    if 32 <= bm <= 64:
+    if 32 < bm <= 64:
         # the 16-bit fixed-point form after the planes: v ~= s * (256 hi + lo) per (row, 128 columns)
-        up = lambda v: (v + 255) // 256 * 256  # noqa: E731
         o = up(4 * cap * I)
         qh = raw[o:o + cap * I].view(np.int8).reshape(cap, I).astype(np.int64)
         o += up(cap * I)
@@ -252,7 +280,6 @@ def test_gemm1_intermediate(act, bm):
                 assert np.allclose(qs[r], gmax / 32639.0, rtol=1e-6, atol=0.0), (blk, r_local)
                 vq = sc * (256.0 * qh[r] + ql[r])
                 assert np.all(np.abs(vq - a_g[r]) <= 0.51 * sc + 1e-30), (blk, r_local)
-    xf = oracle.act_bits_to_f64(xb, act)
     for blk in range(nr // bm):
         e = br[blk]
         W13 = oracle.dequant_int8_rows(W.q13[e], W.hs13[e])

@@ -65,13 +65,20 @@ int64_t auto_block_m(int64_t T, int64_t E, int64_t k) {
 
 bool use_prefill(int64_t bm) { return bm == 256; }
 
-// 16-row blocks quantize inside GEMM2; 32 to 64 rows read the requantized form.
-bool needs_requant(int64_t bm) { return bm >= 32 && bm <= 64; }
+// Blocks of 16 and 32 rows: GEMM1 (the DMA-fed kernel) writes the 16-bit
+// fixed-point form itself, in groups of 64 columns.  48 and 64 rows: GEMM1
+// writes bf16 planes and a requant pass turns them into groups of 128.
+bool q16_from_gemm1(int64_t bm) { return bm == 16 || bm == 32; }
+bool needs_requant(int64_t bm) { return bm > 32 && bm <= 64; }
 
-// The intermediate: bf16 hi/lo planes [2, cap, I]; for blocks of 32 to 64
-// rows followed by the int8 hi codes [cap, I], lo codes [cap, I] and fp32
-// scales [cap, I/128] the integer GEMM2 reads.  With prefill_q16 (256-row
-// blocks) that fixed-point form alone sits at offset 0, in the planes' space.
+// The intermediate of the int8 path:
+//   blocks of 16 / 32 rows: int8 hi codes [cap, I], lo codes [cap, I], fp32
+//     scales [cap, I/64] at offset 0;
+//   48 / 64 rows: bf16 hi/lo planes [2, cap, I] followed by hi codes, lo codes
+//     and scales [cap, I/128];
+//   256-row blocks with prefill_q16: hi, lo codes and scales [cap, I/128] at
+//     offset 0, in the planes' space;
+//   otherwise (and for the other weight formats) the bf16 planes.
 struct Q16 {
   int8_t* hi;
   int8_t* lo;
@@ -81,6 +88,9 @@ struct Q16 {
 size_t planes_bytes(int64_t cap, int64_t I) { return align_up(static_cast<size_t>(cap) * static_cast<size_t>(I) * 4); }
 
 size_t intermediate_bytes(int64_t cap, int64_t I, int64_t bm, bool w8) {
+  if (w8 && q16_from_gemm1(bm))
+    return 2 * align_up(static_cast<size_t>(cap) * static_cast<size_t>(I)) +
+           align_up(static_cast<size_t>(cap) * static_cast<size_t>(I / 64) * 4);
   size_t b = planes_bytes(cap, I);
   if (w8 && needs_requant(bm)) {
     b += 2 * align_up(static_cast<size_t>(cap) * static_cast<size_t>(I));
@@ -138,7 +148,10 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
     return moe::launch_gemm1_w8_big(p, nullptr, nullptr, nullptr, stream);
   }
   if (!use_stream(p.block_m)) return moe::launch_gemm1_w8(p, stream);
-  if (p.block_m == 16 || p.block_m == 32) return moe::launch_gemm1_w8_dma(p, stream);
+  if (q16_from_gemm1(p.block_m)) {
+    const Q16 q = q16_at(p.a, p.cap, p.I, 0);
+    return moe::launch_gemm1_w8_dma(p, q.hi, q.lo, q.scale, stream);
+  }
   if (p.block_m == 64) return moe::launch_gemm1_w8_lds(p, 1, 1, stream);
   return moe::launch_gemm1_w8_stream(p, gemm1_kways(T, p.H, p.I, E, p.k, p.block_m), stream);
 }
@@ -237,8 +250,13 @@ hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, h
     return moe::launch_gemm2_w8_big_q16(p, q.hi, q.lo, q.scale, stream);
   }
   if (!gemm2_int8(p.block_m)) return moe::launch_gemm2_w8(p, stream);
+  const int nt = gemm2_nt(T, p.H, E, k, p.block_m);
+  if (q16_from_gemm1(p.block_m)) {
+    const Q16 q = q16_at(p.a, p.cap, p.I, 0);
+    return moe::launch_gemm2_q16(p, nt, 64, q.hi, q.lo, q.scale, stream);
+  }
   const Q16 q = q16_at(p.a, p.cap, p.I, planes_bytes(p.cap, p.I));
-  return moe::launch_gemm2_q16(p, gemm2_nt(T, p.H, E, k, p.block_m), q.hi, q.lo, q.scale, stream);
+  return moe::launch_gemm2_q16(p, nt, 128, q.hi, q.lo, q.scale, stream);
 }
 
 enum class Fmt { W8, W4, FP8, W8A8 };
@@ -1013,7 +1031,8 @@ int forward_fp8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, i
   p1.w13 = reinterpret_cast<const int8_t*>(w13); p1.s13 = w13_scale; p1.ldw = H; p1.sorted_ids = F.sorted;
   p1.block_expert = F.blocks; p1.num_padded = F.npad; p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap;
   p1.a = F.a; p1.fp8 = 1;
-  hipError_t e = (F.bm == 16 || F.bm == 32) ? moe::launch_gemm1_w8_dma(p1, stream) : moe::launch_gemm1_w8(p1, stream);
+  hipError_t e = (F.bm == 16 || F.bm == 32) ? moe::launch_gemm1_w8_dma(p1, nullptr, nullptr, nullptr, stream)
+                                            : moe::launch_gemm1_w8(p1, stream);
   if (e != hipSuccess) return hip_status(e, "gemm1_fp8");
   moe::Gemm2Args p2{};
   p2.a = F.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = reinterpret_cast<const int8_t*>(w2); p2.s2 = w2_scale;

@@ -4,8 +4,11 @@
 //
 // experts_int8 page, ExpertsInt8MoEMethod.create_weights / apply ->
 // fused_experts(use_int8_w8a16): h = x dequant(w13[e])^T with the per-row
-// scale on the fp32 accumulator, a = silu(h_gate) * h_up, written as bf16
-// hi/lo planes (hi = rne(a), lo = rne(a - hi)).
+// scale on the fp32 accumulator, a = silu(h_gate) * h_up, written either as
+// 16-bit fixed point for the integer GEMM2 (the workgroup's 64 columns are
+// one scale group: a ~= s (256 hi + lo), s = max |a over the 64| / 32639,
+// the waves exchanging their row maxima through LDS), or as bf16 hi/lo planes
+// (hi = rne(a), lo = rne(a - hi)) for the 16-bit GEMM2.
 //
 // A workgroup is one align block (MT 16-row tiles) and 64 output columns;
 // each of its 4 waves owns 16 gate rows and the matching 16 up rows of w13.
@@ -45,7 +48,8 @@ struct DecodeRing {
 
 // FP8: w13 holds e4m3fn codes with one scale per expert (fp8 page, weight-only path).
 template <int MT, bool F16, bool FP8>
-__global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p) {
+__global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p, int8_t* __restrict__ qhi,
+                                                             int8_t* __restrict__ qlo, float* __restrict__ qscale) {
   using R = DecodeRing<MT>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing * R::kStage];
 
@@ -155,20 +159,70 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p) 
     run(std::integral_constant<int, 1>{});
   }
 
-  uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.a);
-  uint16_t* a_lo = a_hi + p.cap * I;
   const int64_t n = n0 + col;
   const float sg = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + n];
   const float su = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
+  float v[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = row0 + mt * 16 + kg * 4 + i;
+      v[mt][i] = mt < ntiles && p.sorted_ids[r] < Tk ? silu_mul(accg[mt][i] * sg, accu[mt][i] * su) : 0.0f;
+    }
+  if (qhi) {
+    // row maxima over the wave's 16 columns (the 16 lanes of one kg), then over the 4 waves
+    constexpr int kQMax = 32639;                 // 256 * 127 + 127
+    float* red = reinterpret_cast<float*>(smem);  // [4 waves][16 MT rows]
+    float m[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = fabsf(v[mt][i]);
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) x = fmaxf(x, __shfl_xor(x, d, kWave));
+        m[mt][i] = x;
+      }
+    __syncthreads();                              // every wave is done with the ring
+    if (col == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave * 16 * MT + mt * 16 + kg * 4 + i] = m[mt][i];
+    }
+    __syncthreads();
+    const int64_t G = I / 64;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt < ntiles) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = mt * 16 + kg * 4 + i;
+          const float gm = fmaxf(fmaxf(red[rl], red[16 * MT + rl]), fmaxf(red[32 * MT + rl], red[48 * MT + rl]));
+          const float inv = gm > 0.0f ? static_cast<float>(kQMax) / gm : 0.0f;
+          int q = static_cast<int>(__builtin_rintf(v[mt][i] * inv));
+          q = q < -kQMax ? -kQMax : (q > kQMax ? kQMax : q);
+          const int h = (q + 128) >> 8;
+          const int64_t r = row0 + rl;
+          qhi[r * I + n] = static_cast<int8_t>(h);
+          qlo[r * I + n] = static_cast<int8_t>(q - 256 * h);
+          if (wave == 0 && col == 0) qscale[r * G + blockIdx.x] = gm / static_cast<float>(kQMax);
+        }
+      }
+    }
+    return;
+  }
+  uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.a);
+  uint16_t* a_lo = a_hi + p.cap * I;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt < ntiles) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t r = row0 + mt * 16 + kg * 4 + i;
-        const float v = p.sorted_ids[r] < Tk ? silu_mul(accg[mt][i] * sg, accu[mt][i] * su) : 0.0f;
-        const uint32_t hi = pack_bf16_rne(v, 0.0f) & 0xffffu;
-        const uint32_t lo = pack_bf16_rne(v - __uint_as_float(hi << 16), 0.0f) & 0xffffu;
+        const uint32_t hi = pack_bf16_rne(v[mt][i], 0.0f) & 0xffffu;
+        const uint32_t lo = pack_bf16_rne(v[mt][i] - __uint_as_float(hi << 16), 0.0f) & 0xffffu;
         a_hi[r * I + n] = static_cast<uint16_t>(hi);
         a_lo[r * I + n] = static_cast<uint16_t>(lo);
       }
@@ -177,26 +231,27 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p) 
 }
 
 template <int MT>
-hipError_t dma_launch(const Gemm1Args& p, hipStream_t stream) {
+hipError_t dma_launch(const Gemm1Args& p, int8_t* qhi, int8_t* qlo, float* qscale, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(p.I / 64), static_cast<unsigned>(p.cap / p.block_m));
   if (p.fp8) {
     if (p.f16)
-      hipLaunchKernelGGL((gemm1_dma_kernel<MT, true, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((gemm1_dma_kernel<MT, true, true>), grid, dim3(kThreads), 0, stream, p, qhi, qlo, qscale);
     else
-      hipLaunchKernelGGL((gemm1_dma_kernel<MT, false, true>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((gemm1_dma_kernel<MT, false, true>), grid, dim3(kThreads), 0, stream, p, qhi, qlo, qscale);
   } else {
     if (p.f16)
-      hipLaunchKernelGGL((gemm1_dma_kernel<MT, true, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((gemm1_dma_kernel<MT, true, false>), grid, dim3(kThreads), 0, stream, p, qhi, qlo, qscale);
     else
-      hipLaunchKernelGGL((gemm1_dma_kernel<MT, false, false>), grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((gemm1_dma_kernel<MT, false, false>), grid, dim3(kThreads), 0, stream, p, qhi, qlo, qscale);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm1_w8_dma(const Gemm1Args& p, hipStream_t stream) {
-  return p.block_m == 16 ? dma_launch<1>(p, stream) : dma_launch<2>(p, stream);
+hipError_t launch_gemm1_w8_dma(const Gemm1Args& p, int8_t* qhi, int8_t* qlo, float* qscale, hipStream_t stream) {
+  if (p.I % 64 || p.H % kStep || (p.block_m != 16 && p.block_m != 32)) return hipErrorInvalidValue;
+  return p.block_m == 16 ? dma_launch<1>(p, qhi, qlo, qscale, stream) : dma_launch<2>(p, qhi, qlo, qscale, stream);
 }
 
 }  // namespace moe

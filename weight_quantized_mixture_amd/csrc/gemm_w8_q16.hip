@@ -14,11 +14,12 @@
 // the hi and lo planes into two int32 accumulators (exact), then folds
 // s_row * (256 hi_acc + lo_acc) into its fp32 accumulator.
 //
-// requant_q16_kernel turns the bf16 hi/lo planes GEMM1 writes into this form
-// (16 lanes per (row, group)); rows of 16-row tiles made only of padding are
-// skipped, like everywhere else.  Blocks of 16 rows skip that pass: their
-// GEMM2 quantizes the (one tile of) planes while staging them in LDS, which
-// costs less than a launch when a block holds so few rows.
+// requant_q16_kernel turns the bf16 hi/lo planes GEMM1 writes for blocks of
+// 48 and 64 rows into this form (16 lanes per (row, group of 128)); rows of
+// 16-row tiles made only of padding are skipped, like everywhere else.  For
+// blocks of 16 and 32 rows GEMM1 writes the form itself with groups of 64
+// columns (its workgroup's width), which GEMM2 reads with one scale per half
+// step.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -93,16 +94,20 @@ __global__ __launch_bounds__(kThreads) void requant_q16_kernel(const uint16_t* _
 // parts of whole 128-wide steps (grid z).  The block's hi/lo rows and their
 // scales for one step are staged in LDS (double-buffered, one barrier per
 // step); lane (col, kg) feeds K [16kg, 16kg+16) and [64+16kg, 64+16kg+16) of
-// the step to the two MFMAs of each plane, for both operands.
-template <int MT, int NT, bool FQ>
+// the step to the two MFMAs of each plane, for both operands.  GW is the
+// width of a scale group of the intermediate: 128 (one scale per row and
+// step, the two MFMAs of a plane chained) or 64 (one per half step: each half
+// accumulates and folds on its own).
+template <int MT, int NT, int GW>
 __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, const int8_t* __restrict__ qhi,
                                                              const int8_t* __restrict__ qlo,
                                                              const float* __restrict__ qscale) {
   constexpr int ROWS = 16 * MT;
   constexpr int PITCH = kStep + 16;                  // bytes per LDS row (16-byte pad)
   constexpr int CPR = kStep / 16;                    // 16-byte chunks per row and plane
+  constexpr int SPS = kStep / GW;                    // scales per row and step
   __shared__ __attribute__((aligned(16))) int8_t As[2][2][ROWS * PITCH];
-  __shared__ __attribute__((aligned(16))) float Ss[2][ROWS];
+  __shared__ __attribute__((aligned(16))) float Ss[2][ROWS * SPS];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -118,96 +123,49 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
     if (p.sorted_ids[row0 + mt * 16] < p.Tk) ntiles = mt + 1;
   const int nrows = ntiles * 16;
 
-  const int64_t I = p.I, H = p.H, G = I / kStep;
+  const int64_t I = p.I, H = p.H, G = I / GW;
   const int64_t h0 = static_cast<int64_t>(blockIdx.x) * (16 * NT * 4) + wave * 16 * NT;
-  const int total = static_cast<int>(G);
+  const int total = static_cast<int>(I / kStep);
   const int ib = static_cast<int>(blockIdx.z) * total / p.splits;
   const int iters = (static_cast<int>(blockIdx.z) + 1) * total / p.splits - ib;
   const int8_t* wbase = p.w2 + (static_cast<int64_t>(e) * H + h0 + col) * p.ldw + static_cast<int64_t>(ib) * kStep + kg * 16;
   const int64_t tstride = 16 * p.ldw;
 
-  // cooperative copy of one step of the block's rows into LDS.
-  //   FQ = false: chunk c = (plane, row, 16 codes) of the fixed-point form;
-  //   FQ = true:  chunk c = (row, 8 values) of the bf16 planes, quantized on
-  //   the way (the 16 lanes of a row find its group maximum by shuffles).
-  constexpr int NCH = FQ ? ROWS * 16 : 2 * ROWS * CPR;
+  // cooperative copy of one step of the block's rows into LDS: chunk c =
+  // (plane, row, 16 codes) of the fixed-point form
+  constexpr int NCH = 2 * ROWS * CPR;
   constexpr int CPT = (NCH + kThreads - 1) / kThreads;
   int64_t srco[CPT];
   int dsto[CPT];
   bool cv[CPT];
   const int8_t* srcp[CPT];
-  const uint16_t* planes = reinterpret_cast<const uint16_t*>(p.a);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ci = tid + c * kThreads;
-    if constexpr (FQ) {
-      const int r = ci / 16, q = ci % 16;
-      cv[c] = ci < NCH && r < nrows;
-      srcp[c] = nullptr;
-      srco[c] = (row0 + r) * I + static_cast<int64_t>(ib) * kStep + q * 8;
-      dsto[c] = r * PITCH + q * 8;
-    } else {
-      const int pl = ci / (ROWS * CPR), rem = ci % (ROWS * CPR);
-      const int r = rem / CPR, q = rem % CPR;
-      cv[c] = ci < NCH && r < nrows;
-      srcp[c] = pl == 0 ? qhi : qlo;
-      srco[c] = (row0 + r) * I + static_cast<int64_t>(ib) * kStep + q * 16;
-      dsto[c] = (pl * ROWS + r) * PITCH + q * 16;
-    }
+    const int pl = ci / (ROWS * CPR), rem = ci % (ROWS * CPR);
+    const int r = rem / CPR, q = rem % CPR;
+    cv[c] = ci < NCH && r < nrows;
+    srcp[c] = pl == 0 ? qhi : qlo;
+    srco[c] = (row0 + r) * I + static_cast<int64_t>(ib) * kStep + q * 16;
+    dsto[c] = (pl * ROWS + r) * PITCH + q * 16;
   }
-  constexpr int NREG = FQ ? 2 * CPT : CPT;
-  auto load_a = [&](int it, u32x4* regs, float& sreg) {
+  auto load_a = [&](int it, u32x4* regs, float* sreg) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      if constexpr (FQ) {
-        regs[2 * c] = u32x4{0u, 0u, 0u, 0u};
-        regs[2 * c + 1] = u32x4{0u, 0u, 0u, 0u};
-        if (cv[c]) {
-          regs[2 * c] = ld16(planes + srco[c] + static_cast<int64_t>(it) * kStep);
-          regs[2 * c + 1] = ld16(planes + p.cap * I + srco[c] + static_cast<int64_t>(it) * kStep);
-        }
-      } else {
-        if (cv[c]) regs[c] = ld16(srcp[c] + srco[c] + static_cast<int64_t>(it) * kStep);
-      }
+    for (int c = 0; c < CPT; ++c)
+      if (cv[c]) regs[c] = ld16(srcp[c] + srco[c] + static_cast<int64_t>(it) * kStep);
+    if (tid < nrows) {
+#pragma unroll
+      for (int j = 0; j < SPS; ++j) sreg[j] = qscale[(row0 + tid) * G + (ib + it) * SPS + j];
     }
-    if (!FQ && tid < nrows) sreg = qscale[(row0 + tid) * G + ib + it];
   };
-  auto store_a = [&](int buf, const u32x4* regs, float sreg) {
+  auto store_a = [&](int buf, const u32x4* regs, const float* sreg) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      if constexpr (FQ) {
-        float v[8];
+    for (int c = 0; c < CPT; ++c)
+      if (cv[c]) *reinterpret_cast<u32x4*>(&As[buf][0][dsto[c]]) = regs[c];
+    if (tid < nrows) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t hw = regs[2 * c][i], lw = regs[2 * c + 1][i];
-          v[2 * i] = __uint_as_float(hw << 16) + __uint_as_float(lw << 16);
-          v[2 * i + 1] = __uint_as_float(hw & 0xffff0000u) + __uint_as_float(lw & 0xffff0000u);
-        }
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
-        const float inv = m > 0.0f ? static_cast<float>(kQMax) / m : 0.0f;
-        uint32_t hb[2] = {0u, 0u}, lb[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          int q = static_cast<int>(__builtin_rintf(v[i] * inv));
-          q = q < -kQMax ? -kQMax : (q > kQMax ? kQMax : q);
-          const int h = (q + 128) >> 8;
-          hb[i / 4] |= static_cast<uint32_t>(h & 0xff) << (8 * (i % 4));
-          lb[i / 4] |= static_cast<uint32_t>((q - 256 * h) & 0xff) << (8 * (i % 4));
-        }
-        if (cv[c]) {
-          *reinterpret_cast<u32x2*>(&As[buf][0][dsto[c]]) = u32x2{hb[0], hb[1]};
-          *reinterpret_cast<u32x2*>(&As[buf][1][dsto[c]]) = u32x2{lb[0], lb[1]};
-          if ((tid & 15) == 0) Ss[buf][(tid + c * kThreads) / 16] = m / static_cast<float>(kQMax);
-        }
-      } else {
-        if (cv[c]) *reinterpret_cast<u32x4*>(&As[buf][0][dsto[c]]) = regs[c];
-      }
+      for (int j = 0; j < SPS; ++j) Ss[buf][tid * SPS + j] = sreg[j];
     }
-    if (!FQ && tid < nrows) Ss[buf][tid] = sreg;
   };
 
   f32x4 acc[MT][NT];
@@ -216,8 +174,10 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 areg[NREG];
-  float sreg = 0.0f;
+  u32x4 areg[CPT];
+  float sreg[SPS];
+#pragma unroll
+  for (int j = 0; j < SPS; ++j) sreg[j] = 0.0f;
   if (iters > 0) load_a(0, areg, sreg);
   u32x4 w0[NT], w1[NT];
 #pragma unroll
@@ -246,17 +206,34 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
         const u32x4 ah1 = *reinterpret_cast<const u32x4*>(&As[buf][0][o + 64]);
         const u32x4 al0 = *reinterpret_cast<const u32x4*>(&As[buf][1][o]);
         const u32x4 al1 = *reinterpret_cast<const u32x4*>(&As[buf][1][o + 64]);
-        const f32x4 sr = *reinterpret_cast<const f32x4*>(&Ss[buf][mt * 16 + kg * 4]);
+        const int so = (mt * 16 + kg * 4) * SPS;
+        if constexpr (GW == 128) {
+          const f32x4 sr = *reinterpret_cast<const f32x4*>(&Ss[buf][so]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const i32x4 z = {0, 0, 0, 0};
-          i32x4 ih = mfma_i8(ah0, w0[j], z);
-          ih = mfma_i8(ah1, w1[j], ih);
-          i32x4 il = mfma_i8(al0, w0[j], z);
-          il = mfma_i8(al1, w1[j], il);
+          for (int j = 0; j < NT; ++j) {
+            const i32x4 z = {0, 0, 0, 0};
+            i32x4 ih = mfma_i8(ah0, w0[j], z);
+            ih = mfma_i8(ah1, w1[j], ih);
+            i32x4 il = mfma_i8(al0, w0[j], z);
+            il = mfma_i8(al1, w1[j], il);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[mt][j][i] += sr[i] * static_cast<float>(ih[i] * 256 + il[i]);
+            for (int i = 0; i < 4; ++i) acc[mt][j][i] += sr[i] * static_cast<float>(ih[i] * 256 + il[i]);
+          }
+        } else {
+          // scales (row, half) of rows kg*4 + i: [2 i], [2 i + 1]
+          const f32x4 sa = *reinterpret_cast<const f32x4*>(&Ss[buf][so]);
+          const f32x4 sb = *reinterpret_cast<const f32x4*>(&Ss[buf][so + 4]);
+          const float s0[4] = {sa.x, sa.z, sb.x, sb.z}, s1[4] = {sa.y, sa.w, sb.y, sb.w};
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            const i32x4 z = {0, 0, 0, 0};
+            const i32x4 ih0 = mfma_i8(ah0, w0[j], z), ih1 = mfma_i8(ah1, w1[j], z);
+            const i32x4 il0 = mfma_i8(al0, w0[j], z), il1 = mfma_i8(al1, w1[j], z);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[mt][j][i] += s0[i] * static_cast<float>(ih0[i] * 256 + il0[i]) +
+                               s1[i] * static_cast<float>(ih1[i] * 256 + il1[i]);
+          }
         }
       }
     }
@@ -298,21 +275,24 @@ hipError_t launch_requant_q16(const float* a, int64_t cap, int64_t I, const int3
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, const int8_t* qhi, const int8_t* qlo, const float* qscale,
-                            hipStream_t stream) {
+hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, int gw, const int8_t* qhi, const int8_t* qlo,
+                            const float* qscale, hipStream_t stream) {
   const int mt = p.block_m / 16;
-  if ((nt != 2 && nt != 4) || p.H % (64 * nt) != 0 || mt < 1 || mt > 4) return hipErrorInvalidValue;
+  if ((nt != 2 && nt != 4) || (gw != 64 && gw != 128) || p.H % (64 * nt) != 0 || p.I % kStep != 0 || mt < 1 ||
+      mt > 4 || p.block_m % 16 != 0)
+    return hipErrorInvalidValue;
   const unsigned by = static_cast<unsigned>(p.cap / p.block_m), bz = static_cast<unsigned>(p.splits);
-#define Q16(MT, NT, FQ)                                                                                   \
-  hipLaunchKernelGGL((gemm2_q16_kernel<MT, NT, FQ>), dim3(static_cast<unsigned>(p.H / (64 * NT)), by, bz), \
+#define Q16(MT, NT, GW)                                                                                   \
+  hipLaunchKernelGGL((gemm2_q16_kernel<MT, NT, GW>), dim3(static_cast<unsigned>(p.H / (64 * NT)), by, bz), \
                      dim3(kThreads), 0, stream, p, qhi, qlo, qscale)
-  if (nt == 4) {
-    if (mt == 4) Q16(4, 4, false); else if (mt == 3) Q16(3, 4, false); else if (mt == 2) Q16(2, 4, false);
-    else Q16(1, 4, true);
+#define Q16_MT(NT, GW)                                                                                    \
+  if (mt == 4) Q16(4, NT, GW); else if (mt == 3) Q16(3, NT, GW); else if (mt == 2) Q16(2, NT, GW); else Q16(1, NT, GW)
+  if (gw == 64) {
+    if (nt == 4) { Q16_MT(4, 64); } else { Q16_MT(2, 64); }
   } else {
-    if (mt == 4) Q16(4, 2, false); else if (mt == 3) Q16(3, 2, false); else if (mt == 2) Q16(2, 2, false);
-    else Q16(1, 2, true);
+    if (nt == 4) { Q16_MT(4, 128); } else { Q16_MT(2, 128); }
   }
+#undef Q16_MT
 #undef Q16
   return hipGetLastError();
 }

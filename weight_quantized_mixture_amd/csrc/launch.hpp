@@ -72,16 +72,19 @@ struct Gemm2Args {
 hipError_t launch_gemm2_w8(const Gemm2Args& p, hipStream_t stream);
 // LDS-staged GEMM1 for blocks of 32 or 64 rows (kw <= 2 at 32, 1 at 64; ng = 16-column groups per wave).
 hipError_t launch_gemm1_w8_lds(const Gemm1Args& p, int kw, int ng, hipStream_t stream);
-// GEMM1 for blocks of 16 or 32 rows on a 3-step LDS ring of direct global -> LDS copies.
-hipError_t launch_gemm1_w8_dma(const Gemm1Args& p, hipStream_t stream);
+// GEMM1 for blocks of 16 or 32 rows on a 3-step LDS ring of direct global -> LDS copies; with qhi the
+// intermediate goes out as 16-bit fixed point in groups of 64 columns (hi, lo codes [cap, I], scales
+// [cap, I/64]), else as bf16 hi/lo planes into p.a.
+hipError_t launch_gemm1_w8_dma(const Gemm1Args& p, int8_t* qhi, int8_t* qlo, float* qscale, hipStream_t stream);
 // Intermediate as 16-bit fixed point per (row, 128 columns) for the integer-MFMA GEMM2 (blocks of
 // at most 64 rows): requant turns GEMM1's bf16 hi/lo planes into hi/lo int8 codes and scales;
 // nt = 16-column tiles per wave (2 or 4).
 hipError_t launch_requant_q16(const float* a, int64_t cap, int64_t I, const int32_t* sorted_ids,
                               const int32_t* num_padded, int64_t Tk, int8_t* qhi, int8_t* qlo, float* qscale,
                               hipStream_t stream);
-hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, const int8_t* qhi, const int8_t* qlo, const float* qscale,
-                            hipStream_t stream);
+// gw = columns per scale group of the fixed-point intermediate (64 or 128).
+hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, int gw, const int8_t* qhi, const int8_t* qlo,
+                            const float* qscale, hipStream_t stream);
 // block_m == 256 GEMMs with both operands copied straight into a 3-stage LDS ring
 // (GEMM2 needs H to be a multiple of 256).
 // the 256-row GEMM1 addresses x with 32-bit byte offsets ((T + 1) * H * 2 < 2^32)
