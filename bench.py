@@ -7,6 +7,9 @@ quantization runs once at set-up and is not part of a step.
 
 Default workload: the Mixtral-shaped decode batch (E=8, top-2, H=4096,
 I=14336, int8 per-channel weights, bf16 activations) at T=64 tokens.
+--weights fp8 (e4m3fn weights, moe_wfp8a16_apply) and --weights w8a8 (int8
+weights and per-token int8 activations, moe_w8a8_apply) measure the other
+expert formats on the same workloads.
 
 Prints one JSON line with the throughput (tokens/s), the roofline of the
 dominant kernel (from HIP events on the launch stream) and the CPU oracle
@@ -30,6 +33,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "weight_quantized_mixture_amd", "csrc")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published
 
 
 def log(msg):
@@ -44,6 +48,10 @@ def parse():
     ap.add_argument("--workload", default="mixtral_decode",
                     choices=["tiny", "mixtral_decode", "mixtral_prefill", "fine_grained", "w4a16"])
     ap.add_argument("--tokens", type=int, default=None, help="T (default: the workload's headline size)")
+    ap.add_argument("--weights", default="int8", choices=["int8", "fp8", "w8a8"],
+                    help="expert format of the int8 workloads: int8 per-channel weights with 16-bit activations "
+                         "(the default), fp8 e4m3fn weights with one scale per expert and matrix, or int8 "
+                         "weights with int8 activations quantized per token (W8A8)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
@@ -230,10 +238,12 @@ def _rnd(v, n=5):
     return v
 
 
-def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True):
+def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True, fmt="int8"):
     """Time `args.steps` layer calls (logits -> output) of workload `wl` at T tokens on the layer's
     resident weights, with a read flush of `args.flush_mb` MB before each step (outside the timed
-    events), then time each stage once per repetition for the dominant kernel's roofline."""
+    events), then (int8 weights with 16-bit activations) time each stage once per repetition for the
+    dominant kernel's roofline; the other formats report the whole layer against the roofline of
+    their arithmetic."""
     import numpy as np
     E, k, H, I = wl.E, wl.k, wl.H, wl.I
     w4 = wl.weights == "w4"
@@ -246,7 +256,9 @@ def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True):
     ti = torch.empty(T, k, dtype=torch.int32, device=dev)
     block_m = pkg.moe_w8a16_block_m(T, H, I, E, k)
     splits = pkg.moe_w8a16_splits(T, H, I, E, k, block_m)
-    ws_bytes = (pkg.moe_w4a16_workspace_bytes if w4 else pkg.moe_w8a16_workspace_bytes)(T, H, I, E, k, 0)
+    ws_fn = {"int8": pkg.moe_w8a16_workspace_bytes, "fp8": pkg.moe_wfp8a16_workspace_bytes,
+             "w8a8": pkg.moe_w8a8_workspace_bytes}[fmt]
+    ws_bytes = (pkg.moe_w4a16_workspace_bytes if w4 else ws_fn)(T, H, I, E, k, 0)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -256,6 +268,12 @@ def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True):
             pkg.moe_w4a16_apply(x, logits, wl.renormalize, layer.w13_qweight, layer.w13_scales, layer.w13_qzeros,
                                 layer.w2_qweight, layer.w2_scales, layer.w2_qzeros, wl.group_size, tw, ti, out, ws,
                                 0, stream)
+        elif fmt == "fp8":
+            pkg.moe_wfp8a16_apply(x, logits, layer.w13_weight, layer.w13_weight_scale, layer.w2_weight,
+                                  layer.w2_weight_scale, tw, ti, out, ws, renormalize=wl.renormalize, stream=stream)
+        elif fmt == "w8a8":
+            pkg.moe_w8a8_apply(x, logits, layer.w13_weight, layer.w13_scale, layer.w2_weight, layer.w2_scale, tw,
+                               ti, out, ws, renormalize=wl.renormalize, stream=stream)
         else:
             pkg.moe_w8a16_apply(x, logits, wl.renormalize, layer.w13_weight, layer.w13_scale, layer.w2_weight,
                                 layer.w2_scale, tw, ti, out, ws, 0, stream)
@@ -272,6 +290,9 @@ def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True):
         g = wl.group_size
         per_expert_w13 = (2 * I * H) // 2 + (2 * I * (H // g)) * 2 + (2 * I * (H // g)) // 2
         per_expert_w2 = (H * I) // 2 + (H * (I // g)) * 2 + (H * (I // g)) // 2
+    elif fmt == "fp8":
+        per_expert_w13 = 2 * I * H + 4
+        per_expert_w2 = H * I + 4
     else:
         per_expert_w13 = 2 * I * H + 2 * I * 4
         per_expert_w2 = H * I + H * 4
@@ -308,7 +329,7 @@ def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True):
 
     # per-kernel durations: the same kernels, one stage call at a time, HIP events on the launch stream
     stage_ms = {}
-    if not w4 and want_stages:
+    if not w4 and want_stages and fmt == "int8":
         cap = pkg.moe_align_capacity(T, k, E, block_m)
         s_ids = torch.empty(cap, dtype=torch.int32, device=dev)
         b_exp = torch.empty(cap // block_m, dtype=torch.int32, device=dev)
@@ -344,8 +365,11 @@ def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True):
         del a_buf, y_buf
 
     mfma_band = T >= 1024
+    # W8A8 multiplies int8 by int8 on the MFMA (int8 peak); the other formats decode the weights
+    # exactly into 16-bit MFMA operands (bf16/fp16 peak)
+    mfma_peak, mfma_unit = (INT8_PEAK_TOPS, "TOP/s") if fmt == "w8a8" else (BF16_PEAK_TFLOPS, "TFLOP/s")
     layer_hbm_frac = bytes_layer / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS
-    layer_mfma_frac = flops_layer / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS
+    layer_mfma_frac = flops_layer / (ms_per_step / 1e3) / 1e12 / mfma_peak
     if stage_ms:
         dur_s = stage_ms["gemm1"] / 1e3
         if mfma_band:
@@ -359,10 +383,16 @@ def measure(pkg, synthetic, torch, dev, layer, wl, T, args, want_stages=True):
         roof["kernel_ms"] = stage_ms["gemm1"]
     else:
         dur_s = ms_per_step / 1e3
-        roof = {"bound": "hbm", "achieved": bytes_layer / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": layer_hbm_frac, "traffic": None, "kernel": "whole layer"}
+        if mfma_band:
+            roof = {"bound": "mfma", "achieved": flops_layer / dur_s / 1e12, "peak": mfma_peak, "unit": mfma_unit,
+                    "frac": layer_mfma_frac, "traffic": None, "kernel": "whole layer"}
+        else:
+            roof = {"bound": "hbm", "achieved": bytes_layer / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": layer_hbm_frac, "traffic": None, "kernel": "whole layer"}
     # the whole layer (route .. combine) against the same peak as the dominant kernel
     roof["layer_frac"] = layer_mfma_frac if roof["bound"] == "mfma" else layer_hbm_frac
+    if fmt != "int8":
+        block_m = splits = None   # chosen inside the layer call by that format's own plan
     return {"T": T, "value": T / (ms_per_step / 1e3), "ms_per_step": ms_per_step,
             "ms_per_step_median": float(np.median(step_ms)), "wall_s": wall,
             "block_m": block_m, "splits": splits, "active_experts": n_active, "flush_mb": flush_mb,
@@ -407,10 +437,20 @@ def main():
     T = args.tokens or HEADLINE_T[args.workload]
     E, k, H, I = wl.E, wl.k, wl.H, wl.I
     w4 = wl.weights == "w4"
+    fmt = args.weights
+    if w4 and fmt != "int8":
+        print(f"--weights {fmt} applies to the int8 workloads; {wl.name} is the uint4 workload",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
 
     # ---- set-up: seeded weights quantized on the GPU (not part of a step) ----------
     t0 = time.time()
-    layer = pkg.W4A16MoE(E, H, I, wl.group_size, device=dev) if w4 else pkg.W8A16MoE(E, H, I, device=dev)
+    if w4:
+        layer = pkg.W4A16MoE(E, H, I, wl.group_size, device=dev)
+    elif fmt == "fp8":
+        layer = pkg.WFP8A16MoE(E, H, I, device=dev)
+    else:
+        layer = pkg.W8A16MoE(E, H, I, device=dev)
     for e in range(E):
         m13 = torch.from_numpy(synthetic.expert_master(wl, "w13", e, args.seed)).to(dev)
         m2 = torch.from_numpy(synthetic.expert_master(wl, "w2", e, args.seed)).to(dev)
@@ -419,24 +459,24 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] weights ready ({time.time() - t0:.1f}s) workload={wl.name} T={T}")
 
-    m = measure(pkg, synthetic, torch, dev, layer, wl, T, args)
+    m = measure(pkg, synthetic, torch, dev, layer, wl, T, args, fmt=fmt)
     log(f"[bench] {wl.name} T={T}: {m['ms_per_step'] * 1e3:.1f} us/step")
 
     # ---- the metric's other band: Mixtral prefill T=4096 on the same weights -----------
     prefill = None
     if wl.name == "mixtral_decode" and not args.no_prefill_band:
         pwl = synthetic.WORKLOADS["mixtral_prefill"]
-        pm = measure(pkg, synthetic, torch, dev, layer, pwl, PREFILL_BAND_T, args)
+        pm = measure(pkg, synthetic, torch, dev, layer, pwl, PREFILL_BAND_T, args, fmt=fmt)
         log(f"[bench] {pwl.name} T={PREFILL_BAND_T}: {pm['ms_per_step'] * 1e3:.1f} us/step")
         r = pm["roofline"]
         prefill = {"workload": pwl.name, "T": PREFILL_BAND_T, "value": pm["value"], "steps": args.steps,
                    "ms_per_step": pm["ms_per_step"], "mfma_frac": pm["mfma_frac"],
-                   "roofline": {"kernel": r["kernel"], "frac": r["frac"], "kernel_ms": r["kernel_ms"],
+                   "roofline": {"kernel": r["kernel"], "frac": r["frac"], "kernel_ms": r.get("kernel_ms"),
                                 "traffic": r["traffic"]}}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, T, m["xb"], m["logits_np"], args, m["active"])
+        cpu = cpu_baseline(wl, T, m["xb"], m["logits_np"], args, m["active"], fmt)
 
     res = {
         "metric": "MoE-layer tokens/s",
@@ -449,10 +489,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp16" if wl.act == "fp16" else "bf16") + (" x uint4" if w4 else " x int8"),
+        "dtype": "int8 x int8" if fmt == "w8a8" else
+                 ("fp16" if wl.act == "fp16" else "bf16") + (" x uint4" if w4 else " x fp8e4m3" if fmt == "fp8"
+                                                            else " x int8"),
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "E": E, "top_k": k, "H": H, "I": I,
-                   "weights": "uint4 g128 asym" if w4 else "int8 per-channel sym",
+                   "weights": "uint4 g128 asym" if w4 else {"int8": "int8 per-channel sym",
+                                                             "fp8": "fp8 e4m3fn per-tensor",
+                                                             "w8a8": "int8 per-channel sym, int8 per-token act"}[fmt],
                    "block_m": m["block_m"], "splits": m["splits"], "active_experts": m["active_experts"],
                    "flush_mb_between_steps": m["flush_mb"]},
         "stage_ms": m["stage_ms"],
@@ -478,18 +522,42 @@ def gemm1_kernel_name(block_m, H):
     return "gemm1_w8_kernel"
 
 
-def cpu_baseline(wl, T, xb, logits_np, args, active):
+def cpu_baseline(wl, T, xb, logits_np, args, active, fmt="int8"):
     """The fp64 oracle (as it stands) on the host cores: routing + quantized-expert forward."""
     import oracle
     from weight_quantized_mixture_amd import synthetic
 
     threads, blas = host_blas()
-    Ts = args.cpu_sample_tokens or min(T, 64)
+    # the W8A8 oracle sums in int64 numpy matmuls (no BLAS): a smaller sample keeps it to seconds
+    Ts = args.cpu_sample_tokens or min(T, 16 if fmt == "w8a8" else 64)
     rows = np.linspace(0, T - 1, Ts).astype(int)
     w_ref, ids_ref = oracle.route_softmax_topk(logits_np[rows], wl.k, wl.renormalize)
     used = np.unique(ids_ref)
     # the oracle quantizes its own weights (not timed: offline in the method too)
     t0 = time.time()
+    if wl.weights == "w8" and fmt != "int8":
+        # the format's own oracle forward over full-shape parameters (experts the sample never
+        # routes to stay zero)
+        E, H, I = wl.E, wl.H, wl.I
+        q_dt = np.uint8 if fmt == "fp8" else np.int8
+        q13 = np.zeros((E, 2 * I, H), q_dt)
+        q2 = np.zeros((E, H, I), q_dt)
+        s13 = np.zeros(E if fmt == "fp8" else (E, 2 * I), np.float32)
+        s2 = np.zeros(E if fmt == "fp8" else (E, H), np.float32)
+        quant = oracle.quantize_fp8_tensor if fmt == "fp8" else oracle.quantize_int8_rows
+        for e in used:
+            q13[e], s13[e] = quant(synthetic.expert_master(wl, "w13", e, args.seed))
+            q2[e], s2[e] = quant(synthetic.expert_master(wl, "w2", e, args.seed))
+        forward = oracle.moe_forward_fp8 if fmt == "fp8" else oracle.moe_forward_w8a8
+        log(f"[bench] oracle weights ready ({time.time() - t0:.1f}s)")
+        x = oracle.act_bits_to_f64(xb[rows], wl.act)
+        t1 = time.perf_counter()
+        w_ref, ids_ref = oracle.route_softmax_topk(logits_np[rows], wl.k, wl.renormalize)
+        forward(x, q13, s13, q2, s2, w_ref, ids_ref)
+        dt = time.perf_counter() - t1
+        return {"value": Ts / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                "seconds": round(dt, 3), "cpu": host_cpu_model(), "blas": blas,
+                "sample": f"{Ts}/{T} tokens: route + {fmt} oracle forward over {used.size} experts"}
     if wl.weights == "w8":
         q13 = {}; s13 = {}; q2 = {}; s2 = {}
         for e in used:
