@@ -157,11 +157,16 @@ def summarize_pmc(args):
         lines.append(f"| `{short}` | {fk:.0f} | {wk:.0f} | {mb:.1f} |")
     lines += ["", f"Kernel sources sha256[:16]: `{res['sources_sha']}` (all); per GEMM1 kernel: " +
               ", ".join(f"`{k}` `{v}`" for k, v in res["kernel_sources_sha"].items())]
-    stem = f"traffic_{args.workload}_T{res['T']}"
+    stem = f"traffic_{args.workload}_T{res['T']}{fmt_suffix(args)}"
     os.makedirs(PROFILES, exist_ok=True)
     json.dump(res, open(os.path.join(PROFILES, stem + ".json"), "w"), indent=1)
     open(os.path.join(PROFILES, stem + ".md"), "w").write("\n".join(lines) + "\n")
     print(json.dumps(res), flush=True)
+
+
+def fmt_suffix(args) -> str:
+    """File-name suffix of a summary: the expert format unless it is the default int8."""
+    return "" if args.weights == "int8" else f"_{args.weights}"
 
 
 def summarize_trace(args):
@@ -171,7 +176,7 @@ def summarize_trace(args):
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {args.summarize_trace}")
     T = args.tokens or HEADLINE_T[args.workload]
-    lines = [f"# Kernel times: {args.workload}, T={T}", "", f"Command: `{args.pmc_command}`", "",
+    lines = [f"# Kernel times: {args.workload}, T={T}, {args.weights} experts", "", f"Command: `{args.pmc_command}`", "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in csv.DictReader(open(files[0])):
         name = r["Name"].replace("moe::(anonymous namespace)::", "").replace("void ", "")
@@ -179,7 +184,7 @@ def summarize_trace(args):
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     lines += ["", f"Kernel sources sha256[:16]: `{sources_sha()}`"]
-    stem = f"kernels_{args.workload}_T{T}"
+    stem = f"kernels_{args.workload}_T{T}{fmt_suffix(args)}"
     os.makedirs(PROFILES, exist_ok=True)
     open(os.path.join(PROFILES, stem + ".md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
@@ -209,7 +214,7 @@ def summarize_counters(args):
                      f"{100 * m.get('SQ_ACTIVE_INST_VALU', 0.0) / wave:.1f}% | "
                      f"{100 * m.get('SQ_WAIT_INST_ANY', 0.0) / wave:.1f}% | {m.get('SQ_LDS_BANK_CONFLICT', 0.0):.3g} |")
     lines += ["", f"Kernel sources sha256[:16]: `{sources_sha()}`"]
-    stem = f"counters_{args.workload}_T{T}"
+    stem = f"counters_{args.workload}_T{T}{fmt_suffix(args)}"
     os.makedirs(PROFILES, exist_ok=True)
     open(os.path.join(PROFILES, stem + ".md"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)

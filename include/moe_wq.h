@@ -482,8 +482,8 @@ int moe_wfp8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_
  *   a = silu(h_gate) * h_up (fp32);  a8, sa = quant(a)
  *   y = sa * w2_scale[e,h] * sum_i a8[i] w2[e,h,i];  out_t = sum_j w_j y.
  * moe_quantize_act_int8: the activation quantizer alone (x device bf16/fp16
- * [T, H], H a multiple of 4; q device int8 [T, H], 4-byte aligned; scale
- * device fp32 [T]).
+ * [T, H], 8-byte aligned, H a multiple of 4; q device int8 [T, H], 4-byte
+ * aligned; scale device fp32 [T]).
  * moe_w8a8_forward / moe_w8a8_apply: the layer, with arguments, options and
  * requirements as moe_w8a16_forward_ex / moe_w8a16_apply_ex (the same int8
  * weights and scales).  Workspace: moe_w8a8_workspace_bytes.

@@ -102,3 +102,28 @@ def test_apply_equals_route_then_forward():
     pkg.moe_w8a8_apply(x, torch.from_numpy(logits).to(DEV), W.w13, W.s13, W.w2, W.s2, tw, ti, out, ws)
     torch.cuda.synchronize()
     assert np.array_equal(out.float().cpu().numpy().astype(np.float64), got)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [1024, 4096])
+def test_mixtral_prefill_w8a8_sampled(T):
+    """Mixtral prefill (uneven expert loads, 256-row blocks, the big int8 GEMMs): every output row depends
+    only on its own token, so the oracle checks a sample of 8 rows spread over the batch."""
+    wl = synthetic.WORKLOADS["mixtral_prefill"]
+    W = workload_weights(wl)
+    xb = synthetic.activations(wl, T)
+    logits = synthetic.router_logits(wl, T)
+    k = wl.k
+    assert pkg.moe_w8a16_block_m(T, wl.H, wl.I, wl.E, k) == 256
+    log(f"[w8a8] mixtral prefill T={T}")
+    tw, ti, w_ref, ids_ref = route_both(logits, k)
+    x = to_dev_act(xb, wl.act)
+    out = torch.empty_like(x)
+    ws = torch.empty(pkg.moe_w8a8_workspace_bytes(T, W.H, W.I, W.E, k), dtype=torch.uint8, device=DEV)
+    pkg.moe_w8a8_forward(x, W.w13, W.s13, W.w2, W.s2, tw, ti, out, ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, T - 1, 8).astype(int))
+    x64 = act_f64(xb[rows], wl.act)
+    ref = oracle.moe_forward_w8a8(x64, W.q13, W.hs13, W.q2, W.hs2, w_ref[rows], ids_ref[rows])
+    got = out.float().cpu().numpy().astype(np.float64)[rows]
+    assert_w8a8_close(got, ref, x64, W, w_ref[rows], ids_ref[rows], f"w8a8 mixtral prefill T={T} sampled rows")

@@ -262,19 +262,22 @@ hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, h
 enum class Fmt { W8, W4, FP8, W8A8 };
 
 // W8A8 intermediate: the GEMM1 input's int8 codes [xrows, H] and scales
-// [xrows], the fp32 intermediate a [cap, I], its codes [cap, I] and scales [cap].
+// [xrows], the fp32 intermediate a [cap, I], its codes [cap, I] and scales
+// [cap], and the rows' partial maxima of |a| [cap, I/64] (the 256-row GEMM1
+// writes them).
 struct A8 {
   int8_t* qx;
   float* sx;
   float* a;
   int8_t* qa;
   float* sa;
+  float* pmax;
 };
 
 size_t w8a8_bytes(int64_t cap, int64_t I, int64_t xrows, int64_t H) {
   const size_t c = static_cast<size_t>(cap), r = static_cast<size_t>(xrows);
   return align_up(r * static_cast<size_t>(H)) + align_up(r * 4) + align_up(c * static_cast<size_t>(I) * 4) +
-         align_up(c * static_cast<size_t>(I)) + align_up(c * 4);
+         align_up(c * static_cast<size_t>(I)) + align_up(c * 4) + align_up(c * static_cast<size_t>(I / 64) * 4);
 }
 
 A8 w8a8_at(float* base, int64_t cap, int64_t I, int64_t xrows, int64_t H) {
@@ -285,7 +288,8 @@ A8 w8a8_at(float* base, int64_t cap, int64_t I, int64_t xrows, int64_t H) {
   v.sx = reinterpret_cast<float*>(b);   b += align_up(r * 4);
   v.a = reinterpret_cast<float*>(b);    b += align_up(c * static_cast<size_t>(I) * 4);
   v.qa = reinterpret_cast<int8_t*>(b);  b += align_up(c * static_cast<size_t>(I));
-  v.sa = reinterpret_cast<float*>(b);
+  v.sa = reinterpret_cast<float*>(b);   b += align_up(c * 4);
+  v.pmax = reinterpret_cast<float*>(b);
   return v;
 }
 
@@ -402,9 +406,35 @@ Opts opts_of(const moe_fused_opts* fo) {
   return fo ? Opts{fo->num_shared_experts, fo->apply_router_weight_on_input != 0} : Opts{0, false};
 }
 
+// W8A8 with 256-row blocks: the big int8 GEMMs (the x codes may have T k rows
+// when the routing weight scales the input)
+bool w8a8_big(int64_t T, int64_t H, int64_t I, int64_t k, int64_t bm) {
+  return moe::w8a8_big_fits(T * k, H, I, bm);
+}
+
+// one 256 x 256 tile per workgroup and CU: when they fill at most two rounds
+// of 256 CUs, the K split (1, 2 or 4 parts) with the shortest run in rounds,
+// each extra part charged 5% for its partials' round trip through the combine
+int64_t w8a8_big_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
+  const int64_t wgs = blocks_estimate(T, E, k, bm) * (H / 256);
+  if (wgs > 512) return 1;
+  int64_t best = 1;
+  double best_t = 1e30;
+  for (int64_t sp = 1; sp <= 4 && sp <= I / 64; sp *= 2) {
+    const double t = std::ceil(static_cast<double>(wgs * sp) / 256.0) / static_cast<double>(sp) *
+                     (1.0 + 0.05 * static_cast<double>(sp - 1));
+    if (t < best_t) {
+      best_t = t;
+      best = sp;
+    }
+  }
+  return best;
+}
+
 int64_t splits_fmt(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
   if (fmt == Fmt::W8) return splits_for(T, H, I, E, k, bm);
   if (fmt == Fmt::W4) return w4_splits(T, H, I, E, k, bm);
+  if (fmt == Fmt::W8A8 && w8a8_big(T, H, I, k, bm)) return w8a8_big_splits(T, H, I, E, k, bm);
   return gemm2_splits(T, H, I, E, k, bm, true);     // fp8, W8A8: the tiled GEMM2, equal parts
 }
 
@@ -1111,21 +1141,29 @@ int forward_w8a8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, 
                        topk_ids, block_m, workspace, workspace_bytes, stream, &F);
   if (st != MOE_OK || F.T == 0) return st;
   const A8 v = w8a8_at(F.a, F.cap, I, F.Tg, H);
-  hipError_t e = moe::launch_act_quant(F.x, act_dtype == MOE_FP16 ? 1 : 0, F.Tg, H, nullptr, nullptr, 0, v.qx, v.sx,
-                                       stream);
+  hipError_t e = moe::launch_act_quant(F.x, act_dtype == MOE_FP16 ? 1 : 0, F.Tg, H, nullptr, nullptr, 0, nullptr, 0,
+                                       v.qx, v.sx, stream);
   if (e != hipSuccess) return hip_status(e, "quantize x");
   moe::Gemm1Args p1{};
   p1.x = F.x; p1.f16 = act_dtype == MOE_FP16; p1.T = F.Tg; p1.H = H; p1.I = I; p1.k = F.kg; p1.Tk = F.Tk;
   p1.w13 = w13; p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = F.sorted; p1.block_expert = F.blocks;
   p1.num_padded = F.npad; p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap; p1.a = v.a;
-  if ((e = moe::launch_gemm1_w8a8(p1, v.qx, v.sx, stream)) != hipSuccess) return hip_status(e, "gemm1_w8a8");
-  e = moe::launch_act_quant(v.a, 2, F.cap, I, F.sorted, F.npad, F.Tk, v.qa, v.sa, stream);
+  // the same choice as the split count of the workspace layout (row strides past 2^32 bytes per
+  // expert make the big launchers fail the call)
+  const bool big = w8a8_big(T, H, I, F.kx, F.bm);
+  // the 256-row GEMM1 also leaves the rows' partial maxima of |a|, so the quantizer of a makes one
+  // pass over it
+  e = big ? moe::launch_gemm1_w8a8_big(p1, v.qx, v.sx, v.pmax, stream) : moe::launch_gemm1_w8a8(p1, v.qx, v.sx, stream);
+  if (e != hipSuccess) return hip_status(e, "gemm1_w8a8");
+  e = moe::launch_act_quant(v.a, 2, F.cap, I, F.sorted, F.npad, F.Tk, big ? v.pmax : nullptr, I / 64, v.qa, v.sa,
+                            stream);
   if (e != hipSuccess) return hip_status(e, "quantize a");
   moe::Gemm2Args p2{};
   p2.a = v.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = w2; p2.s2 = w2_scale; p2.ldw = ld2;
   p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
   p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y;
-  if ((e = moe::launch_gemm2_w8a8(p2, v.qa, v.sa, stream)) != hipSuccess) return hip_status(e, "gemm2_w8a8");
+  e = big ? moe::launch_gemm2_w8a8_big(p2, v.qa, v.sa, stream) : moe::launch_gemm2_w8a8(p2, v.qa, v.sa, stream);
+  if (e != hipSuccess) return hip_status(e, "gemm2_w8a8");
   return layer_back(F, H, act_dtype, out, stream);
 }
 
@@ -1141,8 +1179,9 @@ int moe_quantize_act_int8(const void* x, int act_dtype, int64_t T, int64_t H, in
   if (T == 0) return ok();
   if (!x || !q || !scale) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
   if (!aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "q must be 4-byte aligned");
-  return hip_status(moe::launch_act_quant(x, act_dtype == MOE_FP16 ? 1 : 0, T, H, nullptr, nullptr, 0, q, scale,
-                                          stream),
+  if (!aligned(x, 8)) return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 8-byte aligned");
+  return hip_status(moe::launch_act_quant(x, act_dtype == MOE_FP16 ? 1 : 0, T, H, nullptr, nullptr, 0, nullptr, 0,
+                                          q, scale, stream),
                     "quantize_act_int8");
 }
 

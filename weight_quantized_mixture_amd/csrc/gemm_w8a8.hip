@@ -42,33 +42,83 @@ __device__ __forceinline__ float load_act(const void* p, int64_t i) {
   else return static_cast<const float*>(p)[i];
 }
 
+// four consecutive values from element i (a multiple of 4): one 16-byte load
+// of fp32, one 8-byte load of 16-bit values
+template <int SRC>
+__device__ __forceinline__ f32x4 load_act4(const void* p, int64_t i) {
+  if constexpr (SRC == 2) {
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+  } else {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+    const uint16_t h[4] = {static_cast<uint16_t>(w.x), static_cast<uint16_t>(w.x >> 16), static_cast<uint16_t>(w.y),
+                           static_cast<uint16_t>(w.y >> 16)};
+    f32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = SRC == 0 ? bf16_to_f32(h[j]) : f16_to_f32(h[j]);
+    return v;
+  }
+}
+
 // One wave per row.  With sorted_ids, row r is quantized only when it holds a
-// token (r < *num_padded and sorted_ids[r] < Tk); others are left alone.
+// token (r < *num_padded and sorted_ids[r] < Tk); others are left alone.  With
+// pmax, the row's max |v| is the max of its npart partial maxima pmax[r, :]
+// (written by the kernel that produced the rows) instead of a first pass over
+// the row.  Each lane takes 4 consecutive values per step, 4 steps of the
+// wave per loop turn.
 template <int SRC>
 __global__ __launch_bounds__(kQWaves * kWave) void act_quant_kernel(const void* __restrict__ src, int64_t rows,
                                                                    int64_t K, const int32_t* __restrict__ sorted_ids,
                                                                    const int32_t* __restrict__ num_padded, int64_t Tk,
+                                                                   const float* __restrict__ pmax, int64_t npart,
                                                                    int8_t* __restrict__ q, float* __restrict__ scale) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t r = static_cast<int64_t>(blockIdx.x) * kQWaves + threadIdx.x / kWave;
   if (r >= rows) return;                                   // uniform per wave
   if (sorted_ids && (r >= *num_padded || sorted_ids[r] >= Tk)) return;
   const int64_t base = r * K;
-  float m = 0.0f;
-  for (int64_t i = lane; i < K; i += kWave) m = fmaxf(m, fabsf(load_act<SRC>(src, base + i)));
-  m = wave_max(m);
+  constexpr int64_t kSpan = 4 * kWave;
+  float m;
+  if (pmax) {
+    m = 0.0f;
+    for (int64_t i = lane; i < npart; i += kWave) m = fmaxf(m, pmax[r * npart + i]);
+    m = wave_max(m);
+  } else {
+    float m4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t i = lane * 4;
+    for (; i + 3 * kSpan < K; i += 4 * kSpan) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 v = load_act4<SRC>(src, base + i + u * kSpan);
+        m4[u] = fmaxf(m4[u], fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      }
+    }
+    for (; i < K; i += kSpan) {
+      const f32x4 v = load_act4<SRC>(src, base + i);
+      m4[0] = fmaxf(m4[0], fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+    m = wave_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+  }
   const float s = m / 127.0f;
   if (lane == 0) scale[r] = s;
-  for (int64_t i = lane * 4; i < K; i += 4 * kWave) {
+  auto code4 = [&](f32x4 v) {
     uint32_t word = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float c = 0.0f;
-      if (s != 0.0f) c = fminf(fmaxf(rintf(load_act<SRC>(src, base + i + j) / s), -127.0f), 127.0f);
+      if (s != 0.0f) c = fminf(fmaxf(rintf(v[j] / s), -127.0f), 127.0f);
       word |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xffu) << (8 * j);
     }
-    *reinterpret_cast<uint32_t*>(q + base + i) = word;
+    return word;
+  };
+  int64_t i = lane * 4;
+  for (; i + 3 * kSpan < K; i += 4 * kSpan) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = load_act4<SRC>(src, base + i + u * kSpan);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<uint32_t*>(q + base + i + u * kSpan) = code4(v[u]);
   }
+  for (; i < K; i += kSpan) *reinterpret_cast<uint32_t*>(q + base + i) = code4(load_act4<SRC>(src, base + i));
 }
 
 template <int MT>
@@ -196,15 +246,19 @@ __global__ __launch_bounds__(kThreads) void gemm2_w8a8_kernel(const Gemm2Args p,
 }  // namespace
 
 hipError_t launch_act_quant(const void* src, int src_type, int64_t rows, int64_t K, const int32_t* sorted_ids,
-                            const int32_t* num_padded, int64_t Tk, int8_t* q, float* scale, hipStream_t stream) {
-  if (K % 4) return hipErrorInvalidValue;
+                            const int32_t* num_padded, int64_t Tk, const float* pmax, int64_t npart, int8_t* q,
+                            float* scale, hipStream_t stream) {
+  if (K % 4 || reinterpret_cast<uintptr_t>(src) % (src_type == 2 ? 16 : 8)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((rows + kQWaves - 1) / kQWaves)), block(kQWaves * kWave);
   if (src_type == 0)
-    hipLaunchKernelGGL(act_quant_kernel<0>, grid, block, 0, stream, src, rows, K, sorted_ids, num_padded, Tk, q, scale);
+    hipLaunchKernelGGL(act_quant_kernel<0>, grid, block, 0, stream, src, rows, K, sorted_ids, num_padded, Tk, pmax, npart,
+                       q, scale);
   else if (src_type == 1)
-    hipLaunchKernelGGL(act_quant_kernel<1>, grid, block, 0, stream, src, rows, K, sorted_ids, num_padded, Tk, q, scale);
+    hipLaunchKernelGGL(act_quant_kernel<1>, grid, block, 0, stream, src, rows, K, sorted_ids, num_padded, Tk, pmax, npart,
+                       q, scale);
   else
-    hipLaunchKernelGGL(act_quant_kernel<2>, grid, block, 0, stream, src, rows, K, sorted_ids, num_padded, Tk, q, scale);
+    hipLaunchKernelGGL(act_quant_kernel<2>, grid, block, 0, stream, src, rows, K, sorted_ids, num_padded, Tk, pmax, npart,
+                       q, scale);
   return hipGetLastError();
 }
 

@@ -158,12 +158,23 @@ hipError_t launch_quantize_fp8(const float* w, int64_t tensors, int64_t per_tens
 hipError_t launch_fp8_merge_w13(uint8_t* q13, const float* s_in, int64_t E, int64_t I, int64_t H, float* s_out,
                                 hipStream_t stream);
 
-// W8A8: per-row int8 quantization of a GEMM input (src_type 0 bf16, 1 fp16, 2 fp32; with sorted_ids only
-// the rows that hold a token), and the two int8 x int8 GEMMs.
+// W8A8: per-row int8 quantization of a GEMM input (src_type 0 bf16, 1 fp16, 2 fp32, src 8- / 16-byte
+// aligned, K a multiple of 4; with sorted_ids only the rows that hold a token; with pmax each row's
+// max |v| is the max of its npart partial maxima [rows, npart], written by the producer of the rows),
+// and the two int8 x int8 GEMMs.
 hipError_t launch_act_quant(const void* src, int src_type, int64_t rows, int64_t K, const int32_t* sorted_ids,
-                            const int32_t* num_padded, int64_t Tk, int8_t* q, float* scale, hipStream_t stream);
+                            const int32_t* num_padded, int64_t Tk, const float* pmax, int64_t npart, int8_t* q,
+                            float* scale, hipStream_t stream);
 hipError_t launch_gemm1_w8a8(const Gemm1Args& p, const int8_t* qx, const float* sx, hipStream_t stream);
 hipError_t launch_gemm2_w8a8(const Gemm2Args& p, const int8_t* qa, const float* sa, hipStream_t stream);
+// The W8A8 GEMMs for 256-row blocks (H a multiple of 256, I of 128): one align block x 256 weight rows
+// per workgroup on a 4-slot LDS ring of direct global -> LDS copies; GEMM2 over p.splits K parts of
+// whole 64-wide steps.  w8a8_big_fits: the shapes they take (T = rows of x's codes).
+bool w8a8_big_fits(int64_t T, int64_t H, int64_t I, int64_t bm);
+// pmax [cap, I/64]: max |a| of each row over each wave's 64 columns.
+hipError_t launch_gemm1_w8a8_big(const Gemm1Args& p, const int8_t* qx, const float* sx, float* pmax,
+                                 hipStream_t stream);
+hipError_t launch_gemm2_w8a8_big(const Gemm2Args& p, const int8_t* qa, const float* sa, hipStream_t stream);
 
 // Weighted top-k combine of the split partials.
 hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,
