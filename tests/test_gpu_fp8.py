@@ -126,3 +126,22 @@ def test_layer_apply_with_options():
     ref = oracle.moe_forward_fp8(act_f64(xb, "bf16"), W.q13, W.s13, W.q2, W.s2, w_ref, ids_ref,
                                  weight_on_input=True, num_shared=S)
     assert_layer_close(out.float().cpu().numpy().astype(np.float64), ref, "fp8 apply with options")
+
+
+@pytest.mark.timeout(900)
+def test_mixtral_prefill_fp8_sampled():
+    """Mixtral-sized experts at prefill size (256-row blocks: the 256-row GEMM1 with e4m3 decoding and the
+    planes GEMM2): each output row depends only on its own token, so the oracle checks 8 sampled rows."""
+    E, k, H, I, T = 8, 2, 4096, 14336, 1024
+    assert pkg.moe_w8a16_block_m(T, H, I, E, k) == 256
+    log(f"[fp8] mixtral prefill T={T}")
+    W = FP8Weights(E, H, I, seed=5)
+    xb = synthetic.random_activations(T, H, "bf16", seed=7)
+    logits = synthetic.random_logits(T, E, seed=8)
+    tw, ti, w_ref, ids_ref = route_both(logits, k)
+    out = W.layer.forward_topk(to_dev_act(xb, "bf16"), tw, ti)
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, T - 1, 8).astype(int))
+    ref = oracle.moe_forward_fp8(act_f64(xb[rows], "bf16"), W.q13, W.s13, W.q2, W.s2, w_ref[rows], ids_ref[rows])
+    got = out.float().cpu().numpy().astype(np.float64)[rows]
+    assert_layer_close(got, ref, f"fp8 mixtral prefill T={T} sampled rows")

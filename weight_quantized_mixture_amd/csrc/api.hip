@@ -412,10 +412,11 @@ bool w8a8_big(int64_t T, int64_t H, int64_t I, int64_t k, int64_t bm) {
   return moe::w8a8_big_fits(T * k, H, I, bm);
 }
 
-// one 256 x 256 tile per workgroup and CU: when they fill at most two rounds
-// of 256 CUs, the K split (1, 2 or 4 parts) with the shortest run in rounds,
-// each extra part charged 5% for its partials' round trip through the combine
-int64_t w8a8_big_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
+// GEMM2 kernels with one 256-row block x 256 columns per workgroup and CU
+// (W8A8 and fp8 prefill): when they fill at most two rounds of 256 CUs, the K
+// split (1, 2 or 4 parts) with the shortest run in rounds, each extra part
+// charged 5% for its partials' round trip through the combine
+int64_t big_tile_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
   const int64_t wgs = blocks_estimate(T, E, k, bm) * (H / 256);
   if (wgs > 512) return 1;
   int64_t best = 1;
@@ -434,7 +435,8 @@ int64_t w8a8_big_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, i
 int64_t splits_fmt(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t bm) {
   if (fmt == Fmt::W8) return splits_for(T, H, I, E, k, bm);
   if (fmt == Fmt::W4) return w4_splits(T, H, I, E, k, bm);
-  if (fmt == Fmt::W8A8 && w8a8_big(T, H, I, k, bm)) return w8a8_big_splits(T, H, I, E, k, bm);
+  if (fmt == Fmt::W8A8 && w8a8_big(T, H, I, k, bm)) return big_tile_splits(T, H, I, E, k, bm);
+  if (fmt == Fmt::FP8 && moe::gemm2_planes_fits(H, I, bm)) return big_tile_splits(T, H, I, E, k, bm);
   return gemm2_splits(T, H, I, E, k, bm, true);     // fp8, W8A8: the tiled GEMM2, equal parts
 }
 
@@ -1061,14 +1063,17 @@ int forward_fp8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, i
   p1.w13 = reinterpret_cast<const int8_t*>(w13); p1.s13 = w13_scale; p1.ldw = H; p1.sorted_ids = F.sorted;
   p1.block_expert = F.blocks; p1.num_padded = F.npad; p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap;
   p1.a = F.a; p1.fp8 = 1;
-  hipError_t e = (F.bm == 16 || F.bm == 32) ? moe::launch_gemm1_w8_dma(p1, nullptr, nullptr, nullptr, stream)
-                                            : moe::launch_gemm1_w8(p1, stream);
+  hipError_t e;
+  if (F.bm == 16 || F.bm == 32) e = moe::launch_gemm1_w8_dma(p1, nullptr, nullptr, nullptr, stream);
+  else if (use_prefill(F.bm) && moe::gemm1_w8_big_fits(p1)) e = moe::launch_gemm1_w8_big(p1, nullptr, nullptr, nullptr, stream);
+  else e = moe::launch_gemm1_w8(p1, stream);
   if (e != hipSuccess) return hip_status(e, "gemm1_fp8");
   moe::Gemm2Args p2{};
   p2.a = F.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = reinterpret_cast<const int8_t*>(w2); p2.s2 = w2_scale;
   p2.ldw = I; p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
   p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y; p2.fp8 = 1;
-  if ((e = moe::launch_gemm2_w8(p2, stream)) != hipSuccess) return hip_status(e, "gemm2_fp8");
+  e = moe::gemm2_planes_fits(H, I, F.bm) ? moe::launch_gemm2_w8_planes(p2, stream) : moe::launch_gemm2_w8(p2, stream);
+  if (e != hipSuccess) return hip_status(e, "gemm2_fp8");
   return layer_back(F, H, act_dtype, out, stream);
 }
 

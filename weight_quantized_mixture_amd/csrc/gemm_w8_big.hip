@@ -63,7 +63,9 @@ constexpr int k1ADma = kAStage / (k1Threads * 16);  // 16-byte copies per thread
 constexpr int k1BDma = kBStage / (k1Threads * 16);
 constexpr int k1Dma = k1ADma + k1BDma;
 
-template <bool F16, bool Q16>
+// FP8: w13 holds OCP e4m3fn codes with one scale per expert (fp8 page,
+// weight-only path), decoded in pairs by gfx950's conversion instruction.
+template <bool F16, bool Q16, bool FP8>
 __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p, int8_t* __restrict__ qhi,
                                                               int8_t* __restrict__ qlo, float* __restrict__ qscale) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
@@ -184,8 +186,14 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
       rw[j][1] = u32x2{v.z, v.w};
     };
     auto conv = [&](int j, int h) {
-      const u32x2 p0 = F16 ? i8x4_to_f16x4(rw[j][h].x) : i8x4_to_bf16x4(rw[j][h].x);
-      const u32x2 p1 = F16 ? i8x4_to_f16x4(rw[j][h].y) : i8x4_to_bf16x4(rw[j][h].y);
+      u32x2 p0, p1;
+      if constexpr (FP8) {
+        p0 = u32x2{fp8x2_to_16x2<F16, false>(rw[j][h].x), fp8x2_to_16x2<F16, true>(rw[j][h].x)};
+        p1 = u32x2{fp8x2_to_16x2<F16, false>(rw[j][h].y), fp8x2_to_16x2<F16, true>(rw[j][h].y)};
+      } else {
+        p0 = F16 ? i8x4_to_f16x4(rw[j][h].x) : i8x4_to_bf16x4(rw[j][h].x);
+        p1 = F16 ? i8x4_to_f16x4(rw[j][h].y) : i8x4_to_bf16x4(rw[j][h].y);
+      }
       cw[h][j] = u32x4{p0.x, p0.y, p1.x, p1.y};
     };
     // column tiles handled in row-tile slot m: [jlo(m), jlo(m + 1))
@@ -197,7 +205,8 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
     // row tiles 2 VALU per MFMA beats 1 or 3; partly filled blocks one less
     // than their conversions need per MFMA)
     auto interleave = []() {
-      constexpr int per = (12 * ((8 + MT1 - 1) / MT1) + 7) / 8 - (MT1 < 8 ? 1 : 0);
+      constexpr int kConv = FP8 ? 4 : 12;   // VALU per conversion of 8 codes
+      constexpr int per = (kConv * ((8 + MT1 - 1) / MT1) + 7) / 8 - (MT1 < 8 && !FP8 ? 1 : 0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
@@ -315,8 +324,8 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
   float sg[4], su[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    sg[j] = p.s13[static_cast<int64_t>(e) * 2 * I + n0 + j];
-    su[j] = p.s13[static_cast<int64_t>(e) * 2 * I + I + n0 + j];
+    sg[j] = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + n0 + j];
+    su[j] = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + I + n0 + j];
   }
   if constexpr (!Q16) {
     // bf16 hi/lo planes
@@ -611,8 +620,16 @@ hipError_t launch_gemm1_w8_big(const Gemm1Args& p, int8_t* qhi, int8_t* qlo, flo
   if (!gemm1_w8_big_fits(p)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.I / kOut), static_cast<unsigned>(p.cap / kRows));
   const bool q16 = qhi != nullptr;
-#define G1(F, Q) hipLaunchKernelGGL((gemm1_big_kernel<F, Q>), grid, dim3(k1Threads), 0, stream, p, qhi, qlo, qscale)
-  if (p.f16) {
+#define G1(F, Q) hipLaunchKernelGGL((gemm1_big_kernel<F, Q, false>), grid, dim3(k1Threads), 0, stream, p, qhi, qlo, \
+                                    qscale)
+#define G1F(F) hipLaunchKernelGGL((gemm1_big_kernel<F, false, true>), grid, dim3(k1Threads), 0, stream, p, qhi, qlo, \
+                                  qscale)
+  if (p.fp8) {
+    // bf16 planes only: the fixed-point form feeds the integer-MFMA GEMM2, which takes int8 w2
+    if (q16) return hipErrorInvalidValue;
+    if (p.f16) G1F(true);
+    else G1F(false);
+  } else if (p.f16) {
     if (q16) G1(true, true);
     else G1(true, false);
   } else {
@@ -620,6 +637,7 @@ hipError_t launch_gemm1_w8_big(const Gemm1Args& p, int8_t* qhi, int8_t* qlo, flo
     else G1(false, false);
   }
 #undef G1
+#undef G1F
   return hipGetLastError();
 }
 

@@ -171,6 +171,10 @@ hipError_t launch_gemm2_w8a8(const Gemm2Args& p, const int8_t* qa, const float* 
 // per workgroup on a 4-slot LDS ring of direct global -> LDS copies; GEMM2 over p.splits K parts of
 // whole 64-wide steps.  w8a8_big_fits: the shapes they take (T = rows of x's codes).
 bool w8a8_big_fits(int64_t T, int64_t H, int64_t I, int64_t bm);
+// GEMM2 for 256-row blocks on GEMM1's bf16 hi/lo planes with e4m3fn (p.fp8) or int8 w2 codes: one align
+// block x 256 output columns per workgroup, p.splits K parts of whole 32-wide steps.
+bool gemm2_planes_fits(int64_t H, int64_t I, int64_t bm);
+hipError_t launch_gemm2_w8_planes(const Gemm2Args& p, hipStream_t stream);
 // pmax [cap, I/64]: max |a| of each row over each wave's 64 columns.
 hipError_t launch_gemm1_w8a8_big(const Gemm1Args& p, const int8_t* qx, const float* sx, float* pmax,
                                  hipStream_t stream);
