@@ -302,6 +302,31 @@ def moe_forward_dense(x: np.ndarray, w13_of, w2_of, topk_w: np.ndarray, topk_ids
     return out
 
 
+def combine_topk(y_parts: np.ndarray, topk_w: np.ndarray, topk_ids: np.ndarray, E: int) -> np.ndarray:
+    """Routing-weighted combine of the experts' outputs.
+
+    experts_int8 page, ``ExpertsInt8MoEMethod.apply`` (``fused_experts`` with
+    ``apply_router_weight_on_input=False``): out_t = sum_j topk_w[t, j] * y_(t, j), where
+    y_(t, j) is the output of expert topk_ids[t, j] for token t, and ids outside [0, E)
+    contribute nothing.  Reading: the second product may be cut along its contraction
+    (I) into parts, so y_(t, j) = sum_s y_parts[s, t*k + j] (flat assignment index t*k + j,
+    the order of topk_ids.reshape(-1)).
+
+    y_parts: [splits, T*k, H]; topk_w, topk_ids: [T, k].  Returns float64 [T, H].
+    """
+    y = np.asarray(y_parts, np.float64)
+    ids = np.asarray(topk_ids)
+    T, k = ids.shape
+    w = np.asarray(topk_w, np.float64)
+    out = np.zeros((T, y.shape[2]), np.float64)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if 0 <= e < E:
+                out[t] += w[t, j] * y[:, t * k + j, :].sum(axis=0)
+    return out
+
+
 def with_shared_experts(topk_w: np.ndarray, topk_ids: np.ndarray, E: int, num_shared: int):
     """Routing extended by shared experts.
 

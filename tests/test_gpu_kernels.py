@@ -324,3 +324,39 @@ def test_gemm2_blocks_of_256_splits(splits):
     ok, detail = oracle.layer_within_tolerance(got, oracle.moe_forward_w8(
         oracle.bf16_bits_to_f64(xb), W.q13, W.hs13, W.q2, W.hs2, w_ref, ids_ref))
     assert ok, f"splits={splits}: {detail}"
+
+
+# (T, k, splits, H, act): every register shape of the few-token combine
+# (k <= 2 with 1, 2, 3-4 and 5-16 parts; k <= 8 with 1, 2, 3-4 parts), k = 1,
+# and the general kernel (k = 3 with 5 parts; more than 256 workgroups with
+# one part and with 12 parts)
+@pytest.mark.parametrize("T,k,splits,H,act", [
+    (1, 2, 1, 4096, "bf16"), (3, 2, 2, 4096, "bf16"), (1, 2, 3, 4096, "fp16"), (1, 2, 16, 4096, "bf16"),
+    (5, 2, 9, 512, "bf16"), (1, 1, 16, 512, "fp16"), (2, 6, 1, 2048, "bf16"), (4, 8, 2, 2048, "fp16"),
+    (3, 6, 4, 2048, "bf16"), (2, 3, 5, 512, "bf16"), (40, 2, 12, 4096, "bf16"), (300, 2, 1, 4096, "bf16"),
+    (70, 2, 12, 4096, "fp16")])
+def test_combine_topk(T, k, splits, H, act):
+    log(f"[combine] T={T} k={k} splits={splits} H={H} act={act}")
+    E = 8
+    rng = np.random.default_rng(T * 1000 + k * 100 + splits)
+    y = rng.standard_normal((splits, T * k, H)).astype(np.float32)
+    w = rng.uniform(0.0, 1.0, (T, k)).astype(np.float32)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    ids[0, k - 1] = -1                     # a dropped assignment
+    if T > 1:
+        ids[1, 0] = E                      # an id past the experts
+    out = torch.empty(T, H, dtype=torch.bfloat16 if act == "bf16" else torch.float16, device=DEV)
+    pkg.moe_combine_topk(torch.from_numpy(y).to(DEV), splits, torch.from_numpy(w).to(DEV),
+                         torch.from_numpy(ids).to(DEV), E, out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = oracle.combine_topk(y, w, ids, E)
+    # fp32 sums of splits parts and k weighted slots (relative error of each
+    # step 2^-24, bounded by the sum of magnitudes), then one rounding to the
+    # output type (half an ulp: 2^-8 relative for bf16, 2^-11 for fp16)
+    valid = ((ids >= 0) & (ids < E)).astype(np.float64)
+    mag = np.einsum("tj,tjh->th", np.abs(w) * valid, np.abs(y).sum(axis=0).reshape(T, k, H))
+    u_out = 2.0 ** -8 if act == "bf16" else 2.0 ** -11
+    tol = u_out * np.abs(ref) + (splits + k + 1) * 2.0 ** -23 * mag + 2.0 ** -24
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), (float(err.max()), float((err - tol).max()))

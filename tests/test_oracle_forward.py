@@ -180,3 +180,36 @@ def test_shared_experts_add_a_gated_mlp_for_every_token():
     routed_i = oracle.moe_forward_w8(x, q13[:E_routed], s13[:E_routed], q2[:E_routed], s2[:E_routed], w, ids,
                                      weight_on_input=True)
     np.testing.assert_allclose(out_i, routed_i + shared, rtol=1e-12, atol=1e-15)
+
+
+def test_combine_handworked():
+    g = json.load(open(os.path.join(GOLD, "combine_handworked.json")))
+    out = oracle.combine_topk(np.array(g["y_parts"]), np.array(g["topk_w"]), np.array(g["topk_ids"]), g["E"])
+    np.testing.assert_array_equal(out, np.array(g["out"]))
+
+
+def test_combine_of_expert_outputs_equals_layer():
+    # the per-assignment expert outputs, split into three parts (two random
+    # ones and the remainder), combine to the layer's output
+    x, q13, s13, q2, s2, w, ids = _tiny_layer(E=5, k=3, T=7, seed=3)
+    E, I = q13.shape[0], q13.shape[1] // 2
+    ids = ids.copy()
+    ids[2, 1] = -1                      # a dropped assignment
+    ids[4, 0] = E                       # an id past the experts
+    T, k = ids.shape
+    y = np.zeros((T * k, x.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if 0 <= e < E:
+                a = oracle.moe_expert_intermediate(x[t][None], oracle.dequant_int8_rows(q13[e], s13[e]), I)[0]
+                y[t * k + j] = oracle.dequant_int8_rows(q2[e], s2[e]) @ a
+    rng = np.random.default_rng(5)
+    r1, r2 = rng.standard_normal(y.shape), rng.standard_normal(y.shape)
+    parts = np.stack([y - r1 - r2, r1, r2])
+    got = oracle.combine_topk(parts, w, ids, E)
+    ref = oracle.moe_forward_w8(x, q13, s13, q2, s2, w, ids)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # the flat index is t*k + j: a transposed (j*T + t) reading fails
+    bad = oracle.combine_topk(parts.reshape(3, T, k, -1).transpose(0, 2, 1, 3).reshape(3, T * k, -1), w, ids, E)
+    assert not np.allclose(bad, ref, rtol=1e-6)

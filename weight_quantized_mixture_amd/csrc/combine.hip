@@ -63,6 +63,64 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + t * H + h) = packed;
 }
 
+// Few tokens (decode): the latency of one dependent load is most of the
+// kernel, so every partial of the thread's 4 outputs and every slot's id and
+// weight are requested before the first is used.  KMAX x SMAX <= 32 register
+// slots cover k <= KMAX slots of splits <= SMAX partials; slots past (k,
+// splits) re-read a valid partial and are not added, so the loads need no
+// branches.  Same sums, in the same order, as combine_kernel.
+template <bool F16, int KMAX, int SMAX>
+__global__ __launch_bounds__(256) void combine_few_kernel(const float* __restrict__ y, int splits,
+                                                          int64_t T, int k, int64_t H, int E,
+                                                          const float* __restrict__ topk_w,
+                                                          const int32_t* __restrict__ topk_ids,
+                                                          void* __restrict__ out) {
+  const int64_t H4 = H / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= T * H4) return;
+  const int64_t t = idx / H4;
+  const int64_t h = (idx % H4) * 4;
+  const int64_t Tk = T * k;
+  float4 v[KMAX][SMAX];
+  int eid[KMAX];
+  float wk[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int64_t f = t * k + (j < k ? j : 0);
+    eid[j] = topk_ids[f];
+    wk[j] = topk_w[f];
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int64_t sl = s < splits ? s : 0;
+      v[j][s] = *reinterpret_cast<const float4*>(y + (sl * Tk + f) * H + h);
+    }
+  }
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    float4 ys = v[j][0];
+#pragma unroll
+    for (int s = 1; s < SMAX; ++s) {
+      if (s < splits) {
+        ys.x += v[j][s].x; ys.y += v[j][s].y; ys.z += v[j][s].z; ys.w += v[j][s].w;
+      }
+    }
+    if (j < k && eid[j] >= 0 && eid[j] < E) {
+      const float wj = wk[j];
+      acc.x += wj * ys.x; acc.y += wj * ys.y; acc.z += wj * ys.z; acc.w += wj * ys.w;
+    }
+  }
+  uint2 packed;
+  if constexpr (F16) {
+    packed.x = static_cast<uint32_t>(f32_to_f16(acc.x)) | (static_cast<uint32_t>(f32_to_f16(acc.y)) << 16);
+    packed.y = static_cast<uint32_t>(f32_to_f16(acc.z)) | (static_cast<uint32_t>(f32_to_f16(acc.w)) << 16);
+  } else {
+    packed.x = pack_bf16_rne(acc.x, acc.y);
+    packed.y = pack_bf16_rne(acc.z, acc.w);
+  }
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + t * H + h) = packed;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,
@@ -70,6 +128,27 @@ hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t 
                           hipStream_t stream) {
   const int64_t n = T * (H / 4);
   const int64_t blocks = (n + 255) / 256;
+  if (blocks <= 256) {
+    // few tokens: the first (KMAX, SMAX) shape that holds (k, splits)
+#define FEW(KM, SM)                                                                                         \
+  if (k <= KM && splits <= SM) {                                                                           \
+    if (f16)                                                                                                \
+      hipLaunchKernelGGL((combine_few_kernel<true, KM, SM>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, \
+                         stream, y, splits, T, k, H, E, topk_w, topk_ids, out);                             \
+    else                                                                                                    \
+      hipLaunchKernelGGL((combine_few_kernel<false, KM, SM>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, \
+                         stream, y, splits, T, k, H, E, topk_w, topk_ids, out);                             \
+    return hipGetLastError();                                                                               \
+  }
+    FEW(2, 1)
+    FEW(2, 2)
+    FEW(2, 4)
+    FEW(2, 16)
+    FEW(8, 1)
+    FEW(8, 2)
+    FEW(8, 4)
+#undef FEW
+  }
 #define COMBINE(F, B)                                                                                    \
   hipLaunchKernelGGL((combine_kernel<F, B>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y, splits, \
                      T, k, H, E, topk_w, topk_ids, out)
