@@ -175,6 +175,7 @@ bool gemm2_int8(int64_t bm) { return bm <= 64; }
 // 256; otherwise two tiles (128 columns, which every H the layer accepts fills).
 int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
   if (H % 256 != 0) return 2;
+  if (moe::gemm2_q16_dma_fits(H, 128, bm, 16)) return 2;   // the LDS-ring kernel: 2 tiles per wave
   if (bm == 64) return H >= 4096 ? 4 : 2;
   const double miss = std::pow(1.0 - static_cast<double>(k) / static_cast<double>(E), static_cast<double>(T));
   const double hit = static_cast<double>(E) * (1.0 - miss);
@@ -253,6 +254,8 @@ hipError_t run_gemm2(const moe::Gemm2Args& p, int64_t T, int64_t E, int64_t k, h
   const int nt = gemm2_nt(T, p.H, E, k, p.block_m);
   if (q16_from_gemm1(p.block_m)) {
     const Q16 q = q16_at(p.a, p.cap, p.I, 0);
+    if (moe::gemm2_q16_dma_fits(p.H, p.I, p.block_m, p.ldw))
+      return moe::launch_gemm2_q16_dma(p, q.hi, q.lo, q.scale, stream);
     return moe::launch_gemm2_q16(p, nt, 64, q.hi, q.lo, q.scale, stream);
   }
   const Q16 q = q16_at(p.a, p.cap, p.I, planes_bytes(p.cap, p.I));

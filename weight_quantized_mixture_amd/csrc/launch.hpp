@@ -85,6 +85,13 @@ hipError_t launch_requant_q16(const float* a, int64_t cap, int64_t I, const int3
 // gw = columns per scale group of the fixed-point intermediate (64 or 128).
 hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, int gw, const int8_t* qhi, const int8_t* qlo,
                             const float* qscale, hipStream_t stream);
+// Blocks of 16 or 32 rows, intermediate in the 16-bit fixed-point form with
+// 64-column scale groups (written by the 16/32-row GEMM1): w2 and the planes
+// streamed through an LDS ring by global -> LDS copies, 128 columns per
+// workgroup.  Same sums, in the same order, as launch_gemm2_q16 with gw 64.
+bool gemm2_q16_dma_fits(int64_t H, int64_t I, int64_t block_m, int64_t ldw);
+hipError_t launch_gemm2_q16_dma(const Gemm2Args& p, const int8_t* qhi, const int8_t* qlo, const float* qscale,
+                                hipStream_t stream);
 // block_m == 256 GEMMs with both operands copied straight into a 3-stage LDS ring
 // (GEMM2 needs H to be a multiple of 256).
 // the 256-row GEMM1 addresses x with 32-bit byte offsets ((T + 1) * H * 2 < 2^32)
