@@ -128,6 +128,33 @@ def test_layer_apply_with_options():
     assert_layer_close(out.float().cpu().numpy().astype(np.float64), ref, "fp8 apply with options")
 
 
+_MIXTRAL_FP8 = {}
+
+
+def _mixtral_fp8_weights():
+    if not _MIXTRAL_FP8:
+        _MIXTRAL_FP8["w"] = FP8Weights(8, 4096, 14336, seed=5)
+    return _MIXTRAL_FP8["w"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [1, 64])
+def test_mixtral_decode_fp8(T):
+    """Mixtral-sized experts at decode size (blocks of 16 and 32 rows: the streaming GEMM1 with e4m3
+    decoding and the streaming fp8 GEMM2, K cut into several parts); every row against the oracle."""
+    E, k, H, I = 8, 2, 4096, 14336
+    assert pkg.moe_w8a16_block_m(T, H, I, E, k) in (16, 32)
+    log(f"[fp8] mixtral decode T={T}")
+    W = _mixtral_fp8_weights()
+    xb = synthetic.random_activations(T, H, "bf16", seed=9 + T)
+    logits = synthetic.random_logits(T, E, seed=10 + T)
+    tw, ti, w_ref, ids_ref = route_both(logits, k)
+    out = W.layer.forward_topk(to_dev_act(xb, "bf16"), tw, ti)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward_fp8(act_f64(xb, "bf16"), W.q13, W.s13, W.q2, W.s2, w_ref, ids_ref)
+    assert_layer_close(out.float().cpu().numpy().astype(np.float64), ref, f"fp8 mixtral decode T={T}")
+
+
 @pytest.mark.timeout(900)
 def test_mixtral_prefill_fp8_sampled():
     """Mixtral-sized experts at prefill size (256-row blocks: the 256-row GEMM1 with e4m3 decoding and the
@@ -135,7 +162,7 @@ def test_mixtral_prefill_fp8_sampled():
     E, k, H, I, T = 8, 2, 4096, 14336, 1024
     assert pkg.moe_w8a16_block_m(T, H, I, E, k) == 256
     log(f"[fp8] mixtral prefill T={T}")
-    W = FP8Weights(E, H, I, seed=5)
+    W = _mixtral_fp8_weights()
     xb = synthetic.random_activations(T, H, "bf16", seed=7)
     logits = synthetic.random_logits(T, E, seed=8)
     tw, ti, w_ref, ids_ref = route_both(logits, k)

@@ -440,6 +440,7 @@ int64_t splits_fmt(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t 
   if (fmt == Fmt::W4) return w4_splits(T, H, I, E, k, bm);
   if (fmt == Fmt::W8A8 && w8a8_big(T, H, I, k, bm)) return big_tile_splits(T, H, I, E, k, bm);
   if (fmt == Fmt::FP8 && moe::gemm2_planes_fits(H, I, bm)) return big_tile_splits(T, H, I, E, k, bm);
+  if (fmt == Fmt::FP8 && moe::gemm2_fp8_dma_fits(H, I, bm)) return gemm2_splits(T, H, I, E, k, bm);
   return gemm2_splits(T, H, I, E, k, bm, true);     // fp8, W8A8: the tiled GEMM2, equal parts
 }
 
@@ -1075,7 +1076,9 @@ int forward_fp8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, i
   p2.a = F.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = reinterpret_cast<const int8_t*>(w2); p2.s2 = w2_scale;
   p2.ldw = I; p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
   p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y; p2.fp8 = 1;
-  e = moe::gemm2_planes_fits(H, I, F.bm) ? moe::launch_gemm2_w8_planes(p2, stream) : moe::launch_gemm2_w8(p2, stream);
+  e = moe::gemm2_planes_fits(H, I, F.bm)       ? moe::launch_gemm2_w8_planes(p2, stream)
+      : moe::gemm2_fp8_dma_fits(H, I, F.bm) ? moe::launch_gemm2_fp8_dma(p2, stream)
+                                             : moe::launch_gemm2_w8(p2, stream);
   if (e != hipSuccess) return hip_status(e, "gemm2_fp8");
   return layer_back(F, H, act_dtype, out, stream);
 }

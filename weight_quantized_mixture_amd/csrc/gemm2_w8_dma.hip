@@ -1,5 +1,6 @@
-// Weight-streaming GEMM2 for int8 experts with align blocks of 16 or 32 rows
-// (decode-sized batches), fed by direct global -> LDS copies, gfx950.
+// Weight-streaming GEMM2 for align blocks of 16 or 32 rows (decode-sized
+// batches), fed by direct global -> LDS copies, gfx950: int8 experts
+// (gemm2_q16_dma_kernel) and weight-only fp8 experts (gemm2_fp8_dma_kernel).
 //
 // experts_int8 page, ExpertsInt8MoEMethod.apply -> fused_experts
 // (use_int8_w8a16): y = a dequant(w2[e])^T with the per-row scale of w2 on
@@ -19,6 +20,8 @@
 // while step s is multiplied; the waits count copies (every lane issues the
 // same number per step), so no load result passes through registers and
 // nothing waits for a load issued after the one it needs.
+#include <type_traits>
+
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
@@ -210,7 +213,186 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_dma_kernel(const Gemm2Args
   }
 }
 
+// fp8 page, Fp8MoEMethod (weight-only path): y = a dequant(w2[e])^T with one
+// fp32 scale per expert.  The intermediate comes from the 16/32-row GEMM1 as
+// two bf16 planes (hi = rne(a), lo = rne(a - hi)); the e4m3fn codes decode
+// exactly into bf16 operands (two per conversion instruction) and both planes
+// accumulate into one fp32 accumulator, scaled once at the end.
+//
+// Same workgroup shape as the int8 kernel (one block, 4 waves x 32 columns,
+// one K part), with K steps of 64 through a 4-deep ring: per step every wave
+// copies its 32 code rows (64 bytes each, 2 KB) and the workgroup both planes
+// of the block's rows (128 bytes per row and plane).  Lane (col, kg) takes
+// K [16 kg, 16 kg + 16) of the step: one 16-byte chunk of codes (two MFMA
+// operands of 8) against chunks 2 kg and 2 kg + 1 of each plane row.
+constexpr int kFStep = 64;                          // K per step
+constexpr int kFRing = 4;
+constexpr int kFWWave = kWRows * kFStep;            // 2 KB of codes per wave and step
+constexpr int kFWStage = 4 * kFWWave;               // 8 KB
+constexpr int kFWDma = kFWWave / (kWave * 16);      // 2 copies per lane and step
+
+template <int MT>
+struct PlaneRing {
+  static constexpr int kARow = kFStep * 2;                     // bf16 bytes per row, plane and step
+  static constexpr int kAStage = 2 * 16 * MT * kARow;          // both planes of the block's rows
+  static constexpr int kADma = kAStage / (kThreads * 16);      // = MT
+  static constexpr int kStage = kFWStage + kAStage;
+  static constexpr int kPer = kFWDma + kADma;                  // copies per lane and step
+};
+
+template <int MT>
+__global__ __launch_bounds__(kThreads) void gemm2_fp8_dma_kernel(const Gemm2Args p) {
+  using R = PlaneRing<MT>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kFRing * R::kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * (16 * MT);
+  if (row0 >= *p.num_padded) return;
+  const int e = p.block_expert[blockIdx.y];
+  int ntiles = 0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    if (p.sorted_ids[row0 + mt * 16] < p.Tk) ntiles = mt + 1;
+
+  const int64_t I = p.I, H = p.H;
+  const int64_t h0 = static_cast<int64_t>(blockIdx.x) * (4 * kWRows) + wave * kWRows;
+  const int total = static_cast<int>(I / kFStep);
+  const int ib = static_cast<int>(blockIdx.z) * total / p.splits;
+  const int iters = (static_cast<int>(blockIdx.z) + 1) * total / p.splits - ib;
+
+  // code copies: row r = 16 i + lane/4 of the wave's 32, LDS slot lane%4
+  // holds chunk (lane%4) ^ swz_b(r)
+  const int8_t* wsrc[kFWDma];
+#pragma unroll
+  for (int i = 0; i < kFWDma; ++i) {
+    const int r = 16 * i + (lane >> 2);
+    const int c = (lane & 3) ^ swz_b(r);
+    wsrc[i] = p.w2 + (static_cast<int64_t>(e) * H + h0 + r) * p.ldw + static_cast<int64_t>(ib) * kFStep + c * 16;
+  }
+  // plane copies: 8-row group g = wave + 4 q (plane g / (2 MT), rows
+  // 8 (g % 2MT) + lane/8), chunk (lane%8) ^ swz_a(row)
+  const uint16_t* a_hi = reinterpret_cast<const uint16_t*>(p.a);
+  const uint16_t* a_lo = a_hi + p.cap * I;
+  const uint16_t* asrc[R::kADma];
+#pragma unroll
+  for (int q = 0; q < R::kADma; ++q) {
+    const int g = wave + 4 * q;
+    const int r = 8 * (g % (2 * MT)) + (lane >> 3);
+    const int c = (lane & 7) ^ swz_a(r);
+    asrc[q] = (g < 2 * MT ? a_hi : a_lo) + (row0 + r) * I + static_cast<int64_t>(ib) * kFStep + c * 8;
+  }
+  auto issue = [&](int s, int slot) {
+    uint8_t* base = smem + slot * R::kStage;
+#pragma unroll
+    for (int i = 0; i < kFWDma; ++i)
+      dma16(wsrc[i] + static_cast<int64_t>(s) * kFStep, base + wave * kFWWave + i * 1024);
+#pragma unroll
+    for (int q = 0; q < R::kADma; ++q)
+      dma16(asrc[q] + static_cast<int64_t>(s) * kFStep, base + kFWStage + (wave + 4 * q) * 1024);
+  };
+
+  int woff[kNT];
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) {
+    const int r = 16 * j + col;
+    woff[j] = wave * kFWWave + r * kFStep + 16 * (kg ^ swz_b(r));
+  }
+  int aoff[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = 16 * mt + col;
+    aoff[mt][0] = kFWStage + r * R::kARow + 16 * ((2 * kg) ^ swz_a(r));
+    aoff[mt][1] = kFWStage + r * R::kARow + 16 * ((2 * kg + 1) ^ swz_a(r));
+  }
+  constexpr int kLoPlane = 16 * MT * R::kARow;
+
+  f32x4 acc[MT][kNT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto run = [&](auto tiles) {
+    constexpr int NTL = decltype(tiles)::value;
+#pragma unroll
+    for (int j = 0; j < kFRing - 1; ++j)
+      if (j < iters) issue(j, j);
+    int slot = 0;
+    for (int s = 0; s < iters; ++s) {
+      // steps s+1 .. min(s+kFRing-2, iters-1) may stay in flight
+      const int ahead = iters - 1 - s;
+      if (ahead >= kFRing - 2) wait_vmcnt<(kFRing - 2) * R::kPer>();
+      else if (ahead == 1) wait_vmcnt<R::kPer>();
+      else wait_vmcnt<0>();
+      stage_barrier();
+      if (s + kFRing - 1 < iters) issue(s + kFRing - 1, slot == 0 ? kFRing - 1 : slot - 1);
+      const uint8_t* st = smem + slot * R::kStage;
+      u32x4 b0[kNT], b1[kNT];
+#pragma unroll
+      for (int j = 0; j < kNT; ++j)
+        fp8x16_to_operands<false>(*reinterpret_cast<const u32x4*>(st + woff[j]), b0[j], b1[j]);
+#pragma unroll
+      for (int mt = 0; mt < NTL; ++mt) {
+        const u32x4 ah0 = *reinterpret_cast<const u32x4*>(st + aoff[mt][0]);
+        const u32x4 ah1 = *reinterpret_cast<const u32x4*>(st + aoff[mt][1]);
+        const u32x4 al0 = *reinterpret_cast<const u32x4*>(st + kLoPlane + aoff[mt][0]);
+        const u32x4 al1 = *reinterpret_cast<const u32x4*>(st + kLoPlane + aoff[mt][1]);
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) {
+          acc[mt][j] = mfma16_bf16(ah0, b0[j], acc[mt][j]);
+          acc[mt][j] = mfma16_bf16(al0, b0[j], acc[mt][j]);
+          acc[mt][j] = mfma16_bf16(ah1, b1[j], acc[mt][j]);
+          acc[mt][j] = mfma16_bf16(al1, b1[j], acc[mt][j]);
+        }
+      }
+      slot = slot == kFRing - 1 ? 0 : slot + 1;
+    }
+  };
+  if constexpr (MT == 2) {
+    if (ntiles > 1) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 1>{});
+  }
+
+  const float sw = p.s2[e];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt < ntiles) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = p.sorted_ids[row0 + mt * 16 + kg * 4 + i];
+        if (f < p.Tk) {
+          float* yr = p.y + (static_cast<int64_t>(blockIdx.z) * p.Tk + f) * H + h0 + col;
+#pragma unroll
+          for (int j = 0; j < kNT; ++j) yr[16 * j] = acc[mt][j][i] * sw;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
+
+bool gemm2_fp8_dma_fits(int64_t H, int64_t I, int64_t block_m) {
+  return (block_m == 16 || block_m == 32) && H % (4 * kWRows) == 0 && I % kFStep == 0;
+}
+
+hipError_t launch_gemm2_fp8_dma(const Gemm2Args& p, hipStream_t stream) {
+  if (!gemm2_fp8_dma_fits(p.H, p.I, p.block_m) || p.ldw % 16 != 0 || p.splits < 1 || p.splits > p.I / kFStep)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(p.H / (4 * kWRows)), static_cast<unsigned>(p.cap / p.block_m),
+                  static_cast<unsigned>(p.splits));
+  if (p.block_m == 16)
+    hipLaunchKernelGGL((gemm2_fp8_dma_kernel<1>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm2_fp8_dma_kernel<2>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 bool gemm2_q16_dma_fits(int64_t H, int64_t I, int64_t block_m, int64_t ldw) {
   return (block_m == 16 || block_m == 32) && H % (4 * kWRows) == 0 && I % kStep == 0 && ldw % 16 == 0;

@@ -92,6 +92,10 @@ hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, int gw, const int8_t* qh
 bool gemm2_q16_dma_fits(int64_t H, int64_t I, int64_t block_m, int64_t ldw);
 hipError_t launch_gemm2_q16_dma(const Gemm2Args& p, const int8_t* qhi, const int8_t* qlo, const float* qscale,
                                 hipStream_t stream);
+// Weight-only fp8, blocks of 16 or 32 rows: the bf16 planes GEMM1 writes and
+// the e4m3fn codes of w2 streamed the same way (any split count up to I/64).
+bool gemm2_fp8_dma_fits(int64_t H, int64_t I, int64_t block_m);
+hipError_t launch_gemm2_fp8_dma(const Gemm2Args& p, hipStream_t stream);
 // block_m == 256 GEMMs with both operands copied straight into a 3-stage LDS ring
 // (GEMM2 needs H to be a multiple of 256).
 // the 256-row GEMM1 addresses x with 32-bit byte offsets ((T + 1) * H * 2 < 2^32)
