@@ -21,7 +21,8 @@ def _need_gpu():
     pkg.lib()
 
 
-@pytest.mark.parametrize("act,T,H", [("bf16", 37, 512), ("fp16", 5, 4096), ("bf16", 1000, 2048)])
+# rows of up to 4096 values: one workgroup per row; 8192: a wave per row (no partial maxima)
+@pytest.mark.parametrize("act,T,H", [("bf16", 37, 512), ("fp16", 5, 4096), ("bf16", 1000, 2048), ("bf16", 3, 8192)])
 def test_activation_codes_bit_exact(act, T, H):
     xb = synthetic.random_activations(T, H, act, seed=T)
     xb[0] = 0                                              # a zero row: scale 0, codes 0

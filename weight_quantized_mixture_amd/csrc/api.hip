@@ -439,6 +439,7 @@ int64_t splits_fmt(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_t 
   if (fmt == Fmt::W8) return splits_for(T, H, I, E, k, bm);
   if (fmt == Fmt::W4) return w4_splits(T, H, I, E, k, bm);
   if (fmt == Fmt::W8A8 && w8a8_big(T, H, I, k, bm)) return big_tile_splits(T, H, I, E, k, bm);
+  if (fmt == Fmt::W8A8 && moe::w8a8_dma_fits(H, I, bm)) return gemm2_splits(T, H, I, E, k, bm);
   if (fmt == Fmt::FP8 && moe::gemm2_planes_fits(H, I, bm)) return big_tile_splits(T, H, I, E, k, bm);
   if (fmt == Fmt::FP8 && moe::gemm2_fp8_dma_fits(H, I, bm)) return gemm2_splits(T, H, I, E, k, bm);
   return gemm2_splits(T, H, I, E, k, bm, true);     // fp8, W8A8: the tiled GEMM2, equal parts
@@ -1162,18 +1163,23 @@ int forward_w8a8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, 
   // the same choice as the split count of the workspace layout (row strides past 2^32 bytes per
   // expert make the big launchers fail the call)
   const bool big = w8a8_big(T, H, I, F.kx, F.bm);
-  // the 256-row GEMM1 also leaves the rows' partial maxima of |a|, so the quantizer of a makes one
-  // pass over it
-  e = big ? moe::launch_gemm1_w8a8_big(p1, v.qx, v.sx, v.pmax, stream) : moe::launch_gemm1_w8a8(p1, v.qx, v.sx, stream);
+  const bool dma = !big && moe::w8a8_dma_fits(H, I, F.bm);
+  // the 256-row and the 16/32-row GEMM1 also leave the rows' partial maxima of |a|, so the
+  // quantizer of a makes one pass over it
+  e = big   ? moe::launch_gemm1_w8a8_big(p1, v.qx, v.sx, v.pmax, stream)
+      : dma ? moe::launch_gemm1_w8a8_dma(p1, v.qx, v.sx, v.pmax, stream)
+            : moe::launch_gemm1_w8a8(p1, v.qx, v.sx, stream);
   if (e != hipSuccess) return hip_status(e, "gemm1_w8a8");
-  e = moe::launch_act_quant(v.a, 2, F.cap, I, F.sorted, F.npad, F.Tk, big ? v.pmax : nullptr, I / 64, v.qa, v.sa,
-                            stream);
+  e = moe::launch_act_quant(v.a, 2, F.cap, I, F.sorted, F.npad, F.Tk, big || dma ? v.pmax : nullptr, I / 64, v.qa,
+                            v.sa, stream);
   if (e != hipSuccess) return hip_status(e, "quantize a");
   moe::Gemm2Args p2{};
   p2.a = v.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = w2; p2.s2 = w2_scale; p2.ldw = ld2;
   p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
   p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y;
-  e = big ? moe::launch_gemm2_w8a8_big(p2, v.qa, v.sa, stream) : moe::launch_gemm2_w8a8(p2, v.qa, v.sa, stream);
+  e = big   ? moe::launch_gemm2_w8a8_big(p2, v.qa, v.sa, stream)
+      : dma ? moe::launch_gemm2_w8a8_dma(p2, v.qa, v.sa, stream)
+            : moe::launch_gemm2_w8a8(p2, v.qa, v.sa, stream);
   if (e != hipSuccess) return hip_status(e, "gemm2_w8a8");
   return layer_back(F, H, act_dtype, out, stream);
 }

@@ -121,6 +121,58 @@ __global__ __launch_bounds__(kQWaves * kWave) void act_quant_kernel(const void* 
   for (; i < K; i += kSpan) *reinterpret_cast<uint32_t*>(q + base + i) = code4(load_act4<SRC>(src, base + i));
 }
 
+// One workgroup per (row, chunk of 1024 U values): the same scale and codes
+// as act_quant_kernel with every load of the chunk in flight at once (a wave
+// walking a whole row pays one memory latency per loop turn).  The row
+// maximum comes from pmax or, when one chunk covers the row, from the chunk.
+template <int SRC, int U>
+__global__ __launch_bounds__(kThreads) void act_quant_rows_kernel(const void* __restrict__ src, int64_t K,
+                                                                  const int32_t* __restrict__ sorted_ids,
+                                                                  const int32_t* __restrict__ num_padded, int64_t Tk,
+                                                                  const float* __restrict__ pmax, int64_t npart,
+                                                                  int8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ float red[kThreads / kWave];
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  if (sorted_ids && (r >= *num_padded || sorted_ids[r] >= Tk)) return;   // uniform per workgroup
+  const int64_t base = r * K;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * (1024 * U);
+  f32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = c0 + (u * kThreads + tid) * 4;
+    v[u] = i < K ? load_act4<SRC>(src, base + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m = 0.0f;
+  if (pmax) {
+    for (int64_t i = tid; i < npart; i += kThreads) m = fmaxf(m, pmax[r * npart + i]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+  }
+  m = wave_max(m);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = m / 127.0f;
+  if (blockIdx.y == 0 && tid == 0) scale[r] = s;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = c0 + (u * kThreads + tid) * 4;
+    if (i < K) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float c = 0.0f;
+        if (s != 0.0f) c = fminf(fmaxf(rintf(v[u][j] / s), -127.0f), 127.0f);
+        word |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xffu) << (8 * j);
+      }
+      *reinterpret_cast<uint32_t*>(q + base + i) = word;
+    }
+  }
+}
+
 template <int MT>
 __global__ __launch_bounds__(kThreads) void gemm1_w8a8_kernel(const Gemm1Args p, const int8_t* __restrict__ qx,
                                                               const float* __restrict__ sx) {
@@ -249,6 +301,19 @@ hipError_t launch_act_quant(const void* src, int src_type, int64_t rows, int64_t
                             const int32_t* num_padded, int64_t Tk, const float* pmax, int64_t npart, int8_t* q,
                             float* scale, hipStream_t stream) {
   if (K % 4 || reinterpret_cast<uintptr_t>(src) % (src_type == 2 ? 16 : 8)) return hipErrorInvalidValue;
+  constexpr int kU = 4;
+  if (rows <= 0) return hipSuccess;
+  if (pmax || K <= 1024 * kU) {
+    const dim3 g(static_cast<unsigned>(rows), static_cast<unsigned>((K + 1024 * kU - 1) / (1024 * kU)));
+#define AQR(S)                                                                                                   \
+  hipLaunchKernelGGL((act_quant_rows_kernel<S, kU>), g, dim3(kThreads), 0, stream, src, K, sorted_ids, num_padded, \
+                     Tk, pmax, npart, q, scale)
+    if (src_type == 0) AQR(0);
+    else if (src_type == 1) AQR(1);
+    else AQR(2);
+#undef AQR
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((rows + kQWaves - 1) / kQWaves)), block(kQWaves * kWave);
   if (src_type == 0)
     hipLaunchKernelGGL(act_quant_kernel<0>, grid, block, 0, stream, src, rows, K, sorted_ids, num_padded, Tk, pmax, npart,

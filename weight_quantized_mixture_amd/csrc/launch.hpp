@@ -178,6 +178,13 @@ hipError_t launch_act_quant(const void* src, int src_type, int64_t rows, int64_t
                             float* scale, hipStream_t stream);
 hipError_t launch_gemm1_w8a8(const Gemm1Args& p, const int8_t* qx, const float* sx, hipStream_t stream);
 hipError_t launch_gemm2_w8a8(const Gemm2Args& p, const int8_t* qa, const float* sa, hipStream_t stream);
+// W8A8 with blocks of 16 or 32 rows: weights and activation codes streamed
+// through an LDS ring (same results as the two launchers above); GEMM1 also
+// leaves the rows' partial maxima of |a| over 64 columns in pmax [cap, I/64].
+bool w8a8_dma_fits(int64_t H, int64_t I, int64_t block_m);
+hipError_t launch_gemm1_w8a8_dma(const Gemm1Args& p, const int8_t* qx, const float* sx, float* pmax,
+                                 hipStream_t stream);
+hipError_t launch_gemm2_w8a8_dma(const Gemm2Args& p, const int8_t* qa, const float* sa, hipStream_t stream);
 // The W8A8 GEMMs for 256-row blocks (H a multiple of 256, I of 128): one align block x 256 weight rows
 // per workgroup on a 4-slot LDS ring of direct global -> LDS copies; GEMM2 over p.splits K parts of
 // whole 64-wide steps.  w8a8_big_fits: the shapes they take (T = rows of x's codes).
