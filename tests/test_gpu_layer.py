@@ -231,12 +231,16 @@ def test_fine_grained(T):
     assert_layer_close(got, ref_w8(W, xb, wl.act, w_ref, ids_ref), f"fine-grained T={T}")
 
 
+# fused routing + align up to 8 tokens (8 x 1024 on the arg-max router at the limit), separate launches
+# past it (9 x 1024, 16 x 64, 64 x 128, 65 tokens, 300 and 600 tokens)
 @pytest.mark.parametrize("T,E,k,act", [(1, 8, 2, "bf16"), (8, 64, 6, "fp16"), (37, 8, 2, "fp16"),
                                        (300, 16, 4, "bf16"), (600, 8, 2, "bf16"), (5, 128, 8, "fp16"),
-                                       (20, 96, 4, "bf16")])
+                                       (20, 96, 4, "bf16"), (64, 8, 2, "bf16"), (16, 64, 6, "bf16"),
+                                       (64, 128, 8, "fp16"), (8, 1024, 4, "bf16"), (65, 8, 2, "bf16"),
+                                       (9, 1024, 2, "bf16")])
 def test_apply_from_logits_matches_route_then_forward(T, E, k, act):
     """moe_w8a16_apply (routing fused with align up to 8 tokens) equals route + forward bit for bit."""
-    H, I = 256, 384
+    H, I = (256, 384) if E <= 128 else (128, 128)
     W = small_w8(E, H, I, seed=51, pad=True)
     xb = synthetic.random_activations(T, H, act, seed=52)
     logits = synthetic.random_logits(T, E, seed=53)
