@@ -103,6 +103,22 @@ def test_layer(act, T, bm):
     assert_layer_close(out.float().cpu().numpy().astype(np.float64), ref, f"fp8 {act} T={T} bm={bm}")
 
 
+@pytest.mark.parametrize("T,bm", [(3, 16), (40, 32)])
+def test_layer_odd_shapes(T, bm):
+    """The 16/32-row streaming GEMMs with H = 3 x 128 (three column tiles) and I = 10 x 64 (K parts of
+    uneven length)."""
+    E, k, H, I = 8, 2, 384, 640
+    log(f"[fp8] odd shapes T={T} block_m={bm}")
+    W = FP8Weights(E, H, I, seed=6)
+    xb = synthetic.random_activations(T, H, "bf16", seed=T + 3)
+    logits = synthetic.random_logits(T, E, seed=T + 4)
+    tw, ti, w_ref, ids_ref = route_both(logits, k)
+    out = W.layer.forward_topk(to_dev_act(xb, "bf16"), tw, ti, block_m=bm)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward_fp8(act_f64(xb, "bf16"), W.q13, W.s13, W.q2, W.s2, w_ref, ids_ref)
+    assert_layer_close(out.float().cpu().numpy().astype(np.float64), ref, f"fp8 odd shapes T={T} bm={bm}")
+
+
 def test_layer_apply_with_options():
     """Routing from logits with grouped sigmoid routing, a shared expert and the weight on the input."""
     E, k, H, I, T, S = 8, 2, 256, 512, 45, 1

@@ -65,6 +65,19 @@ def test_layer_small(act, T, bm, pad):
     check(f"w8a8 {act} T={T} bm={bm}")
 
 
+@pytest.mark.parametrize("T,bm", [(3, 16), (40, 32)])
+def test_layer_odd_shapes(T, bm):
+    """The 16/32-row streaming GEMMs with H = 3 x 128 (three column tiles) and I = 5 x 128 (K parts of
+    uneven length)."""
+    E, k, H, I = 8, 2, 384, 640
+    log(f"[w8a8] odd shapes T={T} block_m={bm}")
+    W = small_w8(E, H, I, seed=17, pad=True)
+    xb = synthetic.random_activations(T, H, "bf16", seed=T + 7)
+    logits = synthetic.random_logits(T, E, seed=T + 8)
+    got, ref, check = _run(W, xb, "bf16", logits, k, bm)
+    check(f"w8a8 odd shapes T={T} bm={bm}")
+
+
 def test_layer_options():
     E, k, H, I, T, S = 8, 3, 256, 384, 40, 1
     W = small_w8(E + S, H, I, seed=17, pad=True)
