@@ -158,11 +158,108 @@ __device__ __forceinline__ void align_body(
   }
 }
 
+// At most one id per thread (T*k <= 512), the decode case: the same result
+// as align_body with fewer dependent steps.  Lanes with the same expert find
+// each other with ballots over the id bits once; the leader of each group
+// writes the wave's count, and one pass per expert turns the waves' counts
+// into the expert's total and exclusive per-wave offsets (no LDS atomics);
+// after the scan every thread writes its own assignment's row, and the
+// sentinels and the block table are written per row and per block from an
+// LDS table of each used block's expert (no loops over an expert's rows).
+__device__ __forceinline__ void align_small(const int32_t* __restrict__ ids, int Tk, int E, int bm, int64_t cap,
+                                            int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+                                            int32_t* __restrict__ num_padded) {
+  __shared__ int s_wc[kAlignWaves][kMaxExperts];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts];
+  __shared__ int s_blk[kAlignThreads];   // used blocks <= sum of ceil(count / bm) <= T*k
+  __shared__ int s_used;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int raw = tid < Tk ? ids[tid] : -1;
+  const int e = (raw >= 0 && raw < E) ? raw : -1;
+#pragma unroll
+  for (int w = 0; w < kAlignWaves; ++w)
+    for (int x = tid; x < E; x += kAlignThreads) s_wc[w][x] = 0;
+  __syncthreads();
+
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const bool active = e >= 0;
+  uint64_t mask = __ballot(active);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = active && ((e >> b) & 1);
+    const uint64_t bal = __ballot(bit);
+    mask &= bit ? bal : ~bal;
+  }
+  const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int rank = __popcll(mask & lower);
+  if (active && rank == 0) s_wc[wave][e] = __popcll(mask);
+  __syncthreads();
+
+  for (int x = tid; x < E; x += kAlignThreads) {
+    int pre = 0;
+#pragma unroll
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int c = s_wc[w][x];
+      s_wc[w][x] = pre;
+      pre += c;
+    }
+    s_cnt[x] = pre;
+  }
+  __syncthreads();
+
+  // exclusive scan of the padded counts (wave 0, 64 experts per step)
+  if (wave == 0) {
+    int carry = 0;
+    for (int base = 0; base < E; base += kWave) {
+      const int x = base + lane;
+      const int c = (x < E) ? s_cnt[x] : 0;
+      const int pc = (c + bm - 1) / bm * bm;
+      int incl = pc;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += n;
+      }
+      if (x < E) s_off[x] = carry + incl - pc;
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+      s_used = carry;
+      *num_padded = carry;
+    }
+  }
+  __syncthreads();
+
+  for (int x = tid; x < E; x += kAlignThreads) {
+    const int nb = (s_cnt[x] + bm - 1) / bm;
+    for (int b = 0; b < nb; ++b) s_blk[s_off[x] / bm + b] = x;
+  }
+  if (active) sorted_ids[s_off[e] + s_wc[wave][e] + rank] = tid;
+  __syncthreads();
+  const int64_t ublocks = s_used / bm;
+  const int sentinel = Tk;
+  for (int64_t b = tid; b < cap / bm; b += kAlignThreads) block_expert[b] = b < ublocks ? s_blk[b] : -1;
+  for (int64_t r = tid; r < cap; r += kAlignThreads) {
+    const int64_t b = r / bm;
+    if (b >= ublocks) {
+      sorted_ids[r] = sentinel;
+    } else {
+      const int x = s_blk[b];
+      if (r - s_off[x] >= s_cnt[x]) sorted_ids[r] = sentinel;   // padding row of expert x's last block
+    }
+  }
+}
+
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int64_t Tk, int E, int bm, int64_t cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded) {
-  if (Tk <= static_cast<int64_t>(kIdsInRegs) * kAlignThreads)
+  if (Tk <= kAlignThreads)
+    align_small(ids, static_cast<int>(Tk), E, bm, cap, sorted_ids, block_expert, num_padded);
+  else if (Tk <= static_cast<int64_t>(kIdsInRegs) * kAlignThreads)
     align_body<true>(ids, Tk, E, bm, cap, sorted_ids, block_expert, num_padded);
   else
     align_body<false>(ids, Tk, E, bm, cap, sorted_ids, block_expert, num_padded);
@@ -180,7 +277,10 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
   for (int64_t t = wave; t < T; t += kAlignWaves)
     route_token(logits + t * E, E, k, renormalize, topk_w + t * k, topk_ids + t * k, keys[wave]);
   __syncthreads();
-  align_body<true>(topk_ids, T * k, E, bm, cap, sorted_ids, block_expert, num_padded);
+  if (T * k <= kAlignThreads)
+    align_small(topk_ids, static_cast<int>(T * k), E, bm, cap, sorted_ids, block_expert, num_padded);
+  else
+    align_body<true>(topk_ids, T * k, E, bm, cap, sorted_ids, block_expert, num_padded);
 }
 
 }  // namespace
