@@ -3,7 +3,8 @@
 // The pages only call the fused expert kernel that consumes this grouping
 // (experts_int8 page, ExpertsInt8MoEMethod.apply); the definition is in
 // moe_wq.h.  One workgroup of 8 waves does all of it, with no atomics on
-// positions, so the result is the unique stable order:
+// positions, so the result is the unique stable order.  Up to 512
+// assignments align_small below takes them one per thread; otherwise:
 //   1. histogram of valid ids (LDS integer atomics: counts are order free);
 //   2. wave 0 scans the padded counts into block offsets and writes the
 //      block -> expert table; all threads write the padding sentinels;
