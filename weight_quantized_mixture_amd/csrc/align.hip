@@ -30,6 +30,21 @@ constexpr int kMaxExperts = 1024;
 // uses would pay one memory latency per 512 ids, twice).
 constexpr int kIdsInRegs = 16;
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4 and 8 lanes inside each row of 16 (lanes shifted in from outside the row
+// read 0), then lane 15 of rows 0 and 2 added to rows 1 and 3 and lane 31 to
+// rows 2 and 3 (row broadcasts).  Six dependent adds instead of six
+// LDS-path shuffles.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 template <bool REGS>
 __device__ __forceinline__ void align_body(
     const int32_t* __restrict__ ids, int64_t Tk, int E, int bm, int64_t cap,
@@ -90,12 +105,7 @@ __device__ __forceinline__ void align_body(
       const int e = base + lane;
       const int c = (e < E) ? cnt[e] : 0;
       const int p = (c + bm - 1) / bm * bm;
-      int incl = p;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += n;
-      }
+      const int incl = wave_incl_scan(p);
       if (e < E) off[e] = carry + incl - p;
       carry += __shfl(incl, kWave - 1, kWave);
     }
@@ -218,12 +228,7 @@ __device__ __forceinline__ void align_small(const int32_t* __restrict__ ids, int
       const int x = base + lane;
       const int c = (x < E) ? s_cnt[x] : 0;
       const int pc = (c + bm - 1) / bm * bm;
-      int incl = pc;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += n;
-      }
+      const int incl = wave_incl_scan(pc);
       if (x < E) s_off[x] = carry + incl - pc;
       carry += __shfl(incl, kWave - 1, kWave);
     }

@@ -56,13 +56,23 @@ __device__ __forceinline__ void route_token_rank(const float* __restrict__ lr, i
   int rank[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) rank[i] = 0;
+  // 8 pairs of keys per turn, all read before the first comparison (read one
+  // at a time, each pair costs a full LDS latency: 64 turns at E = 128).
+  // Turns past E read the zero keys the lanes wrote after the last expert
+  // (they write all 64 NPL slots, a multiple of the 16 keys a turn reads),
+  // which no key exceeds.
   const int epairs = (E + 1) / 2;
-  for (int q = 0; q < epairs; ++q) {
-    const u32x4 kk = *reinterpret_cast<const u32x4*>(keys + 2 * q);
-    const uint64_t k0 = (static_cast<uint64_t>(kk.y) << 32) | kk.x;
-    const uint64_t k1 = (static_cast<uint64_t>(kk.w) << 32) | kk.z;
+  for (int q = 0; q < epairs; q += 8) {
+    u32x4 kk[8];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) rank[i] += (k0 > key[i] ? 1 : 0) + (k1 > key[i] ? 1 : 0);
+    for (int j = 0; j < 8; ++j) kk[j] = *reinterpret_cast<const u32x4*>(keys + 2 * (q + j));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t k0 = (static_cast<uint64_t>(kk[j].y) << 32) | kk[j].x;
+      const uint64_t k1 = (static_cast<uint64_t>(kk[j].w) << 32) | kk[j].z;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) rank[i] += (k0 > key[i] ? 1 : 0) + (k1 > key[i] ? 1 : 0);
+    }
   }
   float pc[NPL];
   float psum = 0.0f;
