@@ -166,7 +166,9 @@ def test_mixtral_decode_fp8(T):
     logits = synthetic.random_logits(T, E, seed=10 + T)
     tw, ti, w_ref, ids_ref = route_both(logits, k)
     out = W.layer.forward_topk(to_dev_act(xb, "bf16"), tw, ti)
+    again = W.layer.forward_topk(to_dev_act(xb, "bf16"), tw, ti)
     torch.cuda.synchronize()
+    assert torch.equal(out, again), "two runs differ bitwise"
     ref = oracle.moe_forward_fp8(act_f64(xb, "bf16"), W.q13, W.s13, W.q2, W.s2, w_ref, ids_ref)
     assert_layer_close(out.float().cpu().numpy().astype(np.float64), ref, f"fp8 mixtral decode T={T}")
 

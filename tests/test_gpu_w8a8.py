@@ -97,6 +97,8 @@ def test_mixtral_decode_w8a8(T):
     logits = synthetic.router_logits(wl, T)
     got, ref, check = _run(W, xb, wl.act, logits, wl.k)
     check(f"w8a8 mixtral decode T={T}")
+    again, _, _ = _run(W, xb, wl.act, logits, wl.k)
+    assert np.array_equal(got, again), "two runs differ bitwise"
     # the allowance is for a few code steps: almost every element meets the plain layer tolerance
     base = 2e-2 * np.abs(ref) + 1e-3
     assert (np.abs(got - ref) > base).mean() < 1e-3
