@@ -176,7 +176,7 @@ bool gemm2_int8(int64_t bm) { return bm <= 64; }
 int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
   if (H % 256 != 0) return 2;
   if (moe::gemm2_q16_dma_fits(H, 128, bm, 16)) return 2;   // the LDS-ring kernel: 2 tiles per wave
-  if (bm == 64) return H >= 4096 ? 4 : 2;
+  if (bm >= 48) return 2;   // 48/64-row blocks: four tiles would leave one wave per SIMD
   const double miss = std::pow(1.0 - static_cast<double>(k) / static_cast<double>(E), static_cast<double>(T));
   const double hit = static_cast<double>(E) * (1.0 - miss);
   return static_cast<double>(T * k) / (hit > 1.0 ? hit : 1.0) > 2.5 ? 2 : 4;

@@ -21,6 +21,7 @@
 // columns (its workgroup's width), which GEMM2 reads with one scale per half
 // step.
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace moe {
@@ -132,9 +133,12 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
   const int64_t tstride = 16 * p.ldw;
 
   // cooperative copy of one step of the block's rows into LDS: chunk c =
-  // (plane, row, 16 codes) of the fixed-point form
+  // (plane, row, 16 codes) of the fixed-point form.  Chunks of rows past the
+  // block's tokens load row 0's chunk again (never stored): every thread
+  // issues the same loads each step, so the waits stay exact.
   constexpr int NCH = 2 * ROWS * CPR;
   constexpr int CPT = (NCH + kThreads - 1) / kThreads;
+  static_assert(NCH % kThreads == 0, "every thread copies whole chunks");
   int64_t srco[CPT];
   int dsto[CPT];
   bool cv[CPT];
@@ -144,27 +148,46 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
     const int ci = tid + c * kThreads;
     const int pl = ci / (ROWS * CPR), rem = ci % (ROWS * CPR);
     const int r = rem / CPR, q = rem % CPR;
-    cv[c] = ci < NCH && r < nrows;
+    cv[c] = r < nrows;
     srcp[c] = pl == 0 ? qhi : qlo;
-    srco[c] = (row0 + r) * I + static_cast<int64_t>(ib) * kStep + q * 16;
+    srco[c] = (row0 + (cv[c] ? r : 0)) * I + static_cast<int64_t>(ib) * kStep + q * 16;
     dsto[c] = (pl * ROWS + r) * PITCH + q * 16;
   }
-  auto load_a = [&](int it, u32x4* regs, float* sreg) {
+  const int srow = tid < nrows ? tid : 0;
+
+  // Weights, and the block's rows and scales, of step s+2 are requested
+  // while step s is multiplied.  They live in rings of three register sets
+  // and the loop is unrolled by three, so the rings turn by renaming: copying
+  // a register that a load is still filling would wait for that load.  (A
+  // fourth set costs more in occupancy than it gains in depth.)
+  struct WSet {
+    u32x4 w0[NT], w1[NT];
+  };
+  struct ASet {
+    u32x4 r[CPT];
+    float s[SPS];
+  };
+  auto wload = [&](int it, WSet& v) {
+    const int64_t kn = static_cast<int64_t>(it) * kStep;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      if (cv[c]) regs[c] = ld16(srcp[c] + srco[c] + static_cast<int64_t>(it) * kStep);
-    if (tid < nrows) {
-#pragma unroll
-      for (int j = 0; j < SPS; ++j) sreg[j] = qscale[(row0 + tid) * G + (ib + it) * SPS + j];
+    for (int j = 0; j < NT; ++j) {
+      v.w0[j] = ld16(wbase + j * tstride + kn);
+      v.w1[j] = ld16(wbase + j * tstride + kn + 64);
     }
   };
-  auto store_a = [&](int buf, const u32x4* regs, const float* sreg) {
+  auto aload = [&](int it, ASet& v) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) v.r[c] = ld16(srcp[c] + srco[c] + static_cast<int64_t>(it) * kStep);
+#pragma unroll
+    for (int j = 0; j < SPS; ++j) v.s[j] = qscale[(row0 + srow) * G + (ib + it) * SPS + j];
+  };
+  auto astore = [&](int buf, const ASet& v) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
-      if (cv[c]) *reinterpret_cast<u32x4*>(&As[buf][0][dsto[c]]) = regs[c];
+      if (cv[c]) *reinterpret_cast<u32x4*>(&As[buf][0][dsto[c]]) = v.r[c];
     if (tid < nrows) {
 #pragma unroll
-      for (int j = 0; j < SPS; ++j) Ss[buf][tid * SPS + j] = sreg[j];
+      for (int j = 0; j < SPS; ++j) Ss[buf][tid * SPS + j] = v.s[j];
     }
   };
 
@@ -174,30 +197,13 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 areg[CPT];
-  float sreg[SPS];
-#pragma unroll
-  for (int j = 0; j < SPS; ++j) sreg[j] = 0.0f;
-  if (iters > 0) load_a(0, areg, sreg);
-  u32x4 w0[NT], w1[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    w0[j] = iters > 0 ? ld16(wbase + j * tstride) : u32x4{0u, 0u, 0u, 0u};
-    w1[j] = iters > 0 ? ld16(wbase + j * tstride + 64) : u32x4{0u, 0u, 0u, 0u};
-  }
-  if (iters > 0) store_a(0, areg, sreg);
-  __syncthreads();
-  for (int it = 0; it < iters; ++it) {
+  auto step = [&](int it, const WSet& cur, WSet& ahead, const ASet& anext, ASet& aahead) {
     const int buf = it & 1;
-    const bool more = it + 1 < iters;
-    if (more) load_a(it + 1, areg, sreg);
-    const int64_t kn = static_cast<int64_t>(more ? it + 1 : it) * kStep;
-    u32x4 n0[NT], n1[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      n0[j] = ld16(wbase + j * tstride + kn);
-      n1[j] = ld16(wbase + j * tstride + kn + 64);
-    }
+    // step it+2, or the last step again near the end (same addresses, never
+    // used): a fixed load count per step
+    const int sa = it + 2 < iters ? it + 2 : iters - 1;
+    aload(sa, aahead);
+    wload(sa, ahead);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (mt < ntiles) {
@@ -212,23 +218,23 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
 #pragma unroll
           for (int j = 0; j < NT; ++j) {
             const i32x4 z = {0, 0, 0, 0};
-            i32x4 ih = mfma_i8(ah0, w0[j], z);
-            ih = mfma_i8(ah1, w1[j], ih);
-            i32x4 il = mfma_i8(al0, w0[j], z);
-            il = mfma_i8(al1, w1[j], il);
+            i32x4 ih = mfma_i8(ah0, cur.w0[j], z);
+            ih = mfma_i8(ah1, cur.w1[j], ih);
+            i32x4 il = mfma_i8(al0, cur.w0[j], z);
+            il = mfma_i8(al1, cur.w1[j], il);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mt][j][i] += sr[i] * static_cast<float>(ih[i] * 256 + il[i]);
           }
         } else {
           // scales (row, half) of rows kg*4 + i: [2 i], [2 i + 1]
-          const f32x4 sa = *reinterpret_cast<const f32x4*>(&Ss[buf][so]);
-          const f32x4 sb = *reinterpret_cast<const f32x4*>(&Ss[buf][so + 4]);
-          const float s0[4] = {sa.x, sa.z, sb.x, sb.z}, s1[4] = {sa.y, sa.w, sb.y, sb.w};
+          const f32x4 sa4 = *reinterpret_cast<const f32x4*>(&Ss[buf][so]);
+          const f32x4 sb4 = *reinterpret_cast<const f32x4*>(&Ss[buf][so + 4]);
+          const float s0[4] = {sa4.x, sa4.z, sb4.x, sb4.z}, s1[4] = {sa4.y, sa4.w, sb4.y, sb4.w};
 #pragma unroll
           for (int j = 0; j < NT; ++j) {
             const i32x4 z = {0, 0, 0, 0};
-            const i32x4 ih0 = mfma_i8(ah0, w0[j], z), ih1 = mfma_i8(ah1, w1[j], z);
-            const i32x4 il0 = mfma_i8(al0, w0[j], z), il1 = mfma_i8(al1, w1[j], z);
+            const i32x4 ih0 = mfma_i8(ah0, cur.w0[j], z), ih1 = mfma_i8(ah1, cur.w1[j], z);
+            const i32x4 il0 = mfma_i8(al0, cur.w0[j], z), il1 = mfma_i8(al1, cur.w1[j], z);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               acc[mt][j][i] += s0[i] * static_cast<float>(ih0[i] * 256 + il0[i]) +
@@ -237,14 +243,28 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      w0[j] = n0[j];
-      w1[j] = n1[j];
-    }
-    if (more) store_a(buf ^ 1, areg, sreg);
-    __syncthreads();
+    if (it + 1 < iters) astore(buf ^ 1, anext);
+    // LDS writes done, then the barrier; the loads of later steps stay in
+    // flight across it (a full __syncthreads would wait for them too)
+    wait_lgkm0();
+    stage_barrier();
+  };
+  WSet q[3];
+  ASet ar[3];
+  if (iters > 0) {
+    aload(0, ar[0]);
+    wload(0, q[0]);
+    wload(iters > 1 ? 1 : 0, q[1]);
+    astore(0, ar[0]);
+    aload(iters > 1 ? 1 : 0, ar[1]);
   }
+  __syncthreads();
+  for (int it = 0; it < iters; it += 3) {
+    step(it, q[0], q[2], ar[1], ar[2]);
+    if (it + 1 < iters) step(it + 1, q[1], q[0], ar[2], ar[0]);
+    if (it + 2 < iters) step(it + 2, q[2], q[1], ar[0], ar[1]);
+  }
+  wait_vmcnt<0>();   // the last steps' repeat loads land before the registers are reused
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
