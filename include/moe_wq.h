@@ -167,8 +167,8 @@ int moe_align_block(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, in
  *   w2         device int8 [E, H, w2_row_stride]    (0 means I)
  *   w2_scale   device fp32 [E, H]
  *   topk_w     device fp32 [T, k];  topk_ids device int32 [T, k]
- *   block_m    rows per align block: 0 = moe_w8a16_block_m(...), else 16, 32 or 64
- *              (multiples of 16 up to 256 use the large-tile path)
+ *   block_m    rows per align block: 0 = moe_w8a16_block_m(...), else 16, 32, 64 or 128
+ *              (other multiples of 16 up to 256 use the large-tile path)
  *   out        device bf16/fp16 [T, H]; may be the same buffer as x (inplace=True)
  *   workspace  device, at least moe_w8a16_workspace_bytes(...) bytes, 256-byte aligned
  * Requirements: H and I multiples of 128; row strides multiples of 16 and
@@ -287,7 +287,7 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * Padding rows of a block that holds rows get v = 0; 16-row groups made only
  * of padding may be left unwritten (GEMM2 never reads them).
  *
- * moe_w8a16_requant: for block_m in (32, 64] (a no-op otherwise) turns the
+ * moe_w8a16_requant: for block_m in (32, 64] or 128 (a no-op otherwise) turns the
  * planes into the fixed-point form with g = 128, stored right after them (at
  * byte offset round_up(4*cap*I, 256)), for the same rows as gemm1.
  *
@@ -295,7 +295,7 @@ int moe_w8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t 
  * split s < splits, h < H:
  *   y[s, f, h] = w2_scale[e,h] * sum_{i in split s} v[r, i] w2[e,h,i]
  * with v as moe_w8a16_gemm1 and moe_w8a16_requant left it in `a` (the
- * fixed-point form for block_m up to 64 and for the prefill form of
+ * fixed-point form for block_m up to 64, 128 and for the prefill form of
  * block_m = 256; the hi + lo planes otherwise).  The K range [0, I) is cut
  * into `splits` parts of whole 128-wide steps (1 <= splits <= I/128; part z
  * covers steps [z*(I/128)/splits, (z+1)*(I/128)/splits) in integer division;

@@ -115,7 +115,7 @@ def test_other_argument_errors():
     assert r == B.MOE_ERR_UNSUPPORTED                       # group 64 not implemented by the forward
     assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 16, 5,
                              p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # more splits than 128-wide steps
-    assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 128, 3,
+    assert L.moe_w8a16_gemm2(p(FAKE), 4, 256, 512, 8, 2, p(FAKE), p(FAKE), 0, p(FAKE), p(FAKE), p(FAKE), 96, 3,
                              p(FAKE), None) == B.MOE_ERR_INVALID_ARGUMENT   # tiled kernels need equal splits
     # 256-row blocks: the fixed-point GEMM2 (H a multiple of 256) takes uneven parts of whole groups
     # (T = 0 stops after the argument checks), the tiled kernel (H = 384) does not
@@ -129,7 +129,8 @@ def test_other_argument_errors():
     assert L.moe_w8a16_requant(p(FAKE), 4, 512, 8, 2, p(FAKE), p(FAKE), 40, None) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 64, None) == B.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 32, None) == B.MOE_OK    # GEMM1 wrote the form
-    assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 128, None) == B.MOE_OK   # nothing to do at 128
+    assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 128, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 96, None) == B.MOE_OK    # nothing to do at 96
     assert L.moe_w8a16_requant(None, 4, 512, 8, 2, None, None, 16, None) == B.MOE_OK    # nor at 16
     assert L.moe_w8a16_requant(None, 0, 512, 8, 2, None, None, 32, None) == B.MOE_OK
 
@@ -145,7 +146,7 @@ def test_intermediate_bytes():
             want = 2 * up(cap * I) + up(cap * (I // 64) * 4)
         else:
             want = up(4 * cap * I)
-            if 32 < bm <= 64:
+            if 32 < bm <= 64 or bm == 128:
                 want += 2 * up(cap * I) + up(cap * (I // 128) * 4)
         assert B.moe_w8a16_intermediate_bytes(T, 4096, I, E, k, bm) == want
     assert B.moe_w8a16_intermediate_bytes(0, 4096, 512, 8, 2, 16) == 0

@@ -163,10 +163,11 @@ def test_bad_shapes_raise():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("T,bm", [(1, 0), (8, 0), (32, 0), (64, 0), (64, 64)])
+@pytest.mark.parametrize("T,bm", [(1, 0), (8, 0), (32, 0), (64, 0), (64, 64), (256, 0)])
 def test_mixtral_decode(T, bm):
     """Every token against the oracle; a second run must give the same bytes (the integer GEMM2 of
-    16/32/64-row blocks with its split-K partials summed in a fixed order)."""
+    16/32/64/128-row blocks with its split-K partials summed in a fixed order; T = 256 takes 128-row
+    blocks, GEMM2 on their 64-row halves)."""
     wl = synthetic.WORKLOADS["mixtral_decode"]
     W = workload_weights(wl)
     assert W.mismatch == 0, "GPU int8 codes or scales differ from the oracle"

@@ -52,30 +52,37 @@ int64_t capacity(int64_t T, int64_t k, int64_t E, int64_t bm) {
 // Rows per align block.  Batches whose experts hold at most about 64 rows
 // take the weight-streaming kernels: the block (16, 32 or 64 rows) is sized
 // to cover the expected largest expert (mean + 3 sigma of a binomial count),
-// so each expert's weights are read once.  Experts with 128 rows or more on
-// average take 256-row blocks of the MFMA-tiled kernels.
-int64_t auto_block_m(int64_t T, int64_t E, int64_t k) {
+// so each expert's weights are read once; large int8 experts (w13 of 32 MiB
+// or more) expected past 80 rows take 128-row blocks, still streamed.
+// Experts with 128 rows or more on average take 256-row blocks of the
+// MFMA-tiled kernels.
+int64_t auto_block_m(int64_t T, int64_t E, int64_t k, bool w8 = false, int64_t H = 0, int64_t I = 0) {
   const double avg = static_cast<double>(T) * k / E;
   if (avg >= 128.0) return 256;                 // MFMA-bound: large tiles
   const double need = avg + 3.0 * std::sqrt(avg) + 1.0;
   if (need <= 16.0) return 16;
   if (need <= 32.0) return 32;
-  return 64;
+  // Well past 64 rows a 128-row block reads each weight row once for two
+  // 64-row blocks' worth of tokens: measured 8-14% faster for Mixtral T=256
+  // and 384 (117 MB of w13 per expert), 23% slower at T=192 (most experts
+  // still fit 64 rows), 3-10% slower for the fine-grained shape (5.8 MB per
+  // expert, whose second reads mostly hit the 256 MB Infinity Cache)
+  return w8 && need > 80.0 && 2 * H * I >= (int64_t{1} << 25) ? 128 : 64;
 }
 
 bool use_prefill(int64_t bm) { return bm == 256; }
 
 // Blocks of 16 and 32 rows: GEMM1 (the DMA-fed kernel) writes the 16-bit
-// fixed-point form itself, in groups of 64 columns.  48 and 64 rows: GEMM1
-// writes bf16 planes and a requant pass turns them into groups of 128.
+// fixed-point form itself, in groups of 64 columns.  48, 64 and 128 rows:
+// GEMM1 writes bf16 planes and a requant pass turns them into groups of 128.
 bool q16_from_gemm1(int64_t bm) { return bm == 16 || bm == 32; }
-bool needs_requant(int64_t bm) { return bm > 32 && bm <= 64; }
+bool needs_requant(int64_t bm) { return (bm > 32 && bm <= 64) || bm == 128; }
 
 // The intermediate of the int8 path:
 //   blocks of 16 / 32 rows: int8 hi codes [cap, I], lo codes [cap, I], fp32
 //     scales [cap, I/64] at offset 0;
-//   48 / 64 rows: bf16 hi/lo planes [2, cap, I] followed by hi codes, lo codes
-//     and scales [cap, I/128];
+//   48 / 64 / 128 rows: bf16 hi/lo planes [2, cap, I] followed by hi codes, lo
+//     codes and scales [cap, I/128];
 //   256-row blocks with prefill_q16: hi, lo codes and scales [cap, I/128] at
 //     offset 0, in the planes' space;
 //   otherwise (and for the other weight formats) the bf16 planes.
@@ -114,7 +121,9 @@ bool prefill_q16(int64_t T, int64_t H, int64_t bm) {
   return use_prefill(bm) && H % 256 == 0 && (T + 1) * H * 2 < (int64_t{1} << 32);
 }
 
-bool use_stream(int64_t bm) { return bm <= 64; }
+// Weight-streaming kernels: blocks of up to 64 rows, and 128 (GEMM1 with eight
+// row tiles, GEMM2 on each 64-row half).
+bool use_stream(int64_t bm) { return bm <= 64 || bm == 128; }
 
 // Rough count of align blocks that hold rows (the exact count stays on the
 // device): the blocks the assignments fill, plus half a block of padding for
@@ -152,7 +161,7 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
     const Q16 q = q16_at(p.a, p.cap, p.I, 0);
     return moe::launch_gemm1_w8_dma(p, q.hi, q.lo, q.scale, stream);
   }
-  if (p.block_m == 64) return moe::launch_gemm1_w8_lds(p, 1, 1, stream);
+  if (p.block_m == 64 || p.block_m == 128) return moe::launch_gemm1_w8_lds(p, 1, 1, stream);
   return moe::launch_gemm1_w8_stream(p, gemm1_kways(T, p.H, p.I, E, p.k, p.block_m), stream);
 }
 
@@ -162,15 +171,15 @@ hipError_t run_gemm1(const moe::Gemm1Args& p, int64_t T, int64_t E, hipStream_t 
 // into `splits` parts so that about 512 workgroups are in flight.  256-row
 // blocks: the LDS-ring kernel on the bf16 planes.  Other block sizes: the
 // generic tiled kernel (equal splits of whole 128-wide steps).
-bool gemm2_int8(int64_t bm) { return bm <= 64; }
+bool gemm2_int8(int64_t bm) { return bm <= 64 || bm == 128; }
 
 
 // Expected rows per active expert above 2.5: narrower waves (more
 // workgroups) stream better; with fewer rows, 4 column tiles per wave.
 // Measured on the Mixtral decode shape (E 8, H 4096): 2 tiles faster by 8%
 // at 3 to 6 rows per expert, 4 tiles by 1-8% at 1.5 to 2.2 rows.  Blocks of
-// 64 rows: 4 tiles for H >= 4096 (Mixtral T = 96 and 128: 4-9% faster), 2
-// below (the fine-grained shape, H 2048, T = 128 and 512: 1-4% faster).
+// 48 rows and more: 2 tiles (with three register sets of loads in flight, 4
+// tiles take 384 registers and leave one wave per SIMD).
 // Four tiles cover 256 columns per workgroup, so they need H a multiple of
 // 256; otherwise two tiles (128 columns, which every H the layer accepts fills).
 int gemm2_nt(int64_t T, int64_t H, int64_t E, int64_t k, int64_t bm) {
@@ -215,7 +224,8 @@ int64_t gemm2_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int6
       if (steps % sp == 0) best = sp;
     return best;
   }
-  const int64_t groups = (H / (64 * gemm2_nt(T, H, E, k, bm))) * blocks;
+  // GEMM2 runs 128-row blocks as two 64-row halves
+  const int64_t groups = (H / (64 * gemm2_nt(T, H, E, k, bm))) * blocks * (bm > 64 ? bm / 64 : 1);
   int64_t sp = 1;
   while (sp * 2 <= 16 && sp * 2 <= steps && groups * sp * 2 <= 512) sp *= 2;
   return sp;
@@ -451,7 +461,7 @@ size_t workspace_for(Fmt fmt, int64_t T, int64_t H, int64_t I, int64_t E, int64_
   const Opts o = opts_of(fo);
   if (T <= 0 || H < 1 || I < 1 || E < 1 || k < 1 || o.S < 0) return 0;
   const int64_t Ex = E + o.S, kx = k + o.S;
-  if (bm == 0) bm = auto_block_m(T, Ex, kx);
+  if (bm == 0) bm = auto_block_m(T, Ex, kx, fmt == Fmt::W8, H, I);
   if (bm < 16 || bm > 256 || bm % 16) return 0;
   return layout(T, H, I, Ex, kx, bm, splits_fmt(fmt, T, H, I, Ex, kx, bm), fmt, o.S > 0 || o.woi, o.woi).total;
 }
@@ -485,7 +495,7 @@ int layer_front(Fmt fmt, const void* x, int act, int64_t T, int64_t H, int64_t I
   if (Ex > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "routed plus shared experts above %lld", (long long)kMaxExperts);
   if ((st = check_act(act)) != MOE_OK) return st;
   if (logits && (st = check_routing(T, E, k, r)) != MOE_OK) return st;
-  const int64_t bm = block_m == 0 ? auto_block_m(T, Ex, kx) : block_m;
+  const int64_t bm = block_m == 0 ? auto_block_m(T, Ex, kx, fmt == Fmt::W8, H, I) : block_m;
   if ((st = check_block_m(bm)) != MOE_OK) return st;
   F->T = 0;
   if (T == 0) return ok();
@@ -625,15 +635,13 @@ int moe_align_block(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, in
 }
 
 int64_t moe_w8a16_block_m(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
-  (void)H;
-  (void)I;
   if (T < 0 || E < 1 || k < 1) return 16;
-  return auto_block_m(T, E, k);
+  return auto_block_m(T, E, k, true, H, I);
 }
 
 int64_t moe_w8a16_splits(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m) {
   if (T <= 0 || H < 128 || I < 128 || E < 1 || k < 1) return 1;
-  if (block_m == 0) block_m = auto_block_m(T, E, k);
+  if (block_m == 0) block_m = auto_block_m(T, E, k, true, H, I);
   return splits_for(T, H, I, E, k, block_m);
 }
 
@@ -648,9 +656,8 @@ size_t moe_w8a16_workspace_bytes_ex(int64_t T, int64_t H, int64_t I, int64_t E, 
 }
 
 size_t moe_w8a16_intermediate_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m) {
-  (void)H;
   if (T <= 0 || I < 1 || E < 1 || k < 1) return 0;
-  if (block_m == 0) block_m = auto_block_m(T, E, k);
+  if (block_m == 0) block_m = auto_block_m(T, E, k, true, H, I);
   if (block_m < 16 || block_m > 256 || block_m % 16) return 0;
   return intermediate_bytes(capacity(T, k, E, block_m), I, block_m, true);
 }
@@ -870,7 +877,7 @@ int moe_w8a16_forward_noalloc(const void* x, int act_dtype, int64_t T, int64_t H
                               hipStream_t stream) {
   int st;
   if ((st = check_layer_dims(T, H, I, E, k)) != MOE_OK) return st;
-  const int64_t bm = block_m == 0 ? auto_block_m(T, E, k) : block_m;
+  const int64_t bm = block_m == 0 ? auto_block_m(T, E, k, true, H, I) : block_m;
   if ((st = check_block_m(bm)) != MOE_OK) return st;
   if (T == 0) return ok();
   const size_t need = workspace_for(Fmt::W8, T, H, I, E, k, bm, nullptr);

@@ -1,5 +1,5 @@
 // Weight-streaming grouped GEMM1 with the activation tile staged in LDS
-// (align blocks of 32 or 64 rows: the gathered activations are shared by the
+// (align blocks of 32, 64 or 128 rows: the gathered activations are shared by the
 // four waves of a workgroup instead of being fetched once per wave).
 //
 // experts_int8 page, ExpertsInt8MoEMethod.create_weights / apply ->
@@ -205,7 +205,11 @@ __global__ __launch_bounds__(kThreads) void gemm1_lds_kernel(const Gemm1Args p) 
 
 template <bool F16>
 hipError_t g1l(const Gemm1Args& p, int mt, int kw, int ng, hipStream_t stream) {
-  // LDS per workgroup: 2 x 16*MT x (KW*128 + 8) bf16 -> keep (MT, KW) in {(1,1..4), (2,1..2), (4,1)}
+  // LDS per workgroup: 2 x 16*MT x (KW*128 + 8) bf16 -> keep (MT, KW) in {(1,1..4), (2,1..2), (4,1), (8,1)}
+  if (mt == 8) {
+    G1L(8, 1, 1, F16);
+    return hipGetLastError();
+  }
   if (mt == 4) kw = 1;
   if (mt == 2 && kw > 2) kw = 2;
   if (ng == 2) {

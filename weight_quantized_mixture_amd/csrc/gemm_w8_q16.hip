@@ -1,5 +1,5 @@
-// GEMM2 on integer MFMAs for blocks of at most 64 rows (decode-sized
-// batches), gfx950.
+// GEMM2 on integer MFMAs for blocks of at most 64 rows, and 128-row blocks
+// as two halves of 64 (decode- and mid-sized batches), gfx950.
 //
 // experts_int8 page, ExpertsInt8MoEMethod.apply -> fused_experts
 // (use_int8_w8a16): y = a dequant(w2[e])^T with the per-row scale of w2 on
@@ -15,7 +15,7 @@
 // s_row * (256 hi_acc + lo_acc) into its fp32 accumulator.
 //
 // requant_q16_kernel turns the bf16 hi/lo planes GEMM1 writes for blocks of
-// 48 and 64 rows into this form (16 lanes per (row, group of 128)); rows of
+// 48, 64 and 128 rows into this form (16 lanes per (row, group of 128)); rows of
 // 16-row tiles made only of padding are skipped, like everywhere else.  For
 // blocks of 16 and 32 rows GEMM1 writes the form itself with groups of 64
 // columns (its workgroup's width), which GEMM2 reads with one scale per half
@@ -115,13 +115,15 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
   const int wave = tid / kWave;
   const int col = lane & 15;
   const int kg = lane >> 4;
+  // ROWS rows of an align block (all of it, or one half of a 128-row block)
   const int64_t row0 = static_cast<int64_t>(blockIdx.y) * ROWS;
   if (row0 >= *p.num_padded) return;
-  const int e = p.block_expert[blockIdx.y];
+  const int e = p.block_expert[row0 / p.block_m];
   int ntiles = 0;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     if (p.sorted_ids[row0 + mt * 16] < p.Tk) ntiles = mt + 1;
+  if (ntiles == 0) return;                           // the padding half of a 128-row block
   const int nrows = ntiles * 16;
 
   const int64_t I = p.I, H = p.H, G = I / GW;
@@ -297,11 +299,13 @@ hipError_t launch_requant_q16(const float* a, int64_t cap, int64_t I, const int3
 
 hipError_t launch_gemm2_q16(const Gemm2Args& p, int nt, int gw, const int8_t* qhi, const int8_t* qlo,
                             const float* qscale, hipStream_t stream) {
-  const int mt = p.block_m / 16;
+  // blocks of up to 64 rows whole, 128-row blocks as two workgroups of 64 rows
+  const int rows = p.block_m == 128 ? 64 : p.block_m;
+  const int mt = rows / 16;
   if ((nt != 2 && nt != 4) || (gw != 64 && gw != 128) || p.H % (64 * nt) != 0 || p.I % kStep != 0 || mt < 1 ||
-      mt > 4 || p.block_m % 16 != 0)
+      mt > 4 || rows % 16 != 0)
     return hipErrorInvalidValue;
-  const unsigned by = static_cast<unsigned>(p.cap / p.block_m), bz = static_cast<unsigned>(p.splits);
+  const unsigned by = static_cast<unsigned>(p.cap / rows), bz = static_cast<unsigned>(p.splits);
 #define Q16(MT, NT, GW)                                                                                   \
   hipLaunchKernelGGL((gemm2_q16_kernel<MT, NT, GW>), dim3(static_cast<unsigned>(p.H / (64 * NT)), by, bz), \
                      dim3(kThreads), 0, stream, p, qhi, qlo, qscale)
