@@ -130,7 +130,9 @@ def _align_gpu(ids, E, bm):
                                            (4096, 2, 8, 64, True), (512, 6, 64, 16, True), (1, 8, 128, 16, False),
                                            (256, 8, 128, 32, False), (100, 3, 1, 16, False),
                                            (300, 4, 1024, 16, False), (129, 2, 8, 1, False),
-                                           (77, 3, 16, 128, True), (4096, 2, 8, 256, False)])
+                                           (77, 3, 16, 128, True), (4096, 2, 8, 256, False),
+                                           (1000, 3, 40, 16, True), (4096, 2, 96, 16, False),
+                                           (171, 4, 129, 32, True)])
 def test_align(T, k, E, bm, skew):
     log(f"[align] T={T} k={k} E={E} bm={bm} skew={skew}")
     rng = np.random.default_rng(T + E + bm)
@@ -148,6 +150,14 @@ def test_align_drops_out_of_range_ids():
     ids = np.array([[0, 9], [-1, 1], [1, 0], [5, 5]], np.int32)
     s, b, n = _align_gpu(ids, 2, 2)
     sr, br, nr = oracle.align_block(ids, 2, 2)
+    assert n == nr
+    np.testing.assert_array_equal(s, sr)
+    np.testing.assert_array_equal(b, br)
+    # past 512 assignments (every chunk ranked at once): ids below 0 and at or past E in every chunk
+    rng = np.random.default_rng(11)
+    ids = rng.integers(-3, 70, size=(700, 3)).astype(np.int32)
+    s, b, n = _align_gpu(ids, 64, 16)
+    sr, br, nr = oracle.align_block(ids, 64, 16)
     assert n == nr
     np.testing.assert_array_equal(s, sr)
     np.testing.assert_array_equal(b, br)
