@@ -451,7 +451,9 @@ int moe_w4_import(int format, const int32_t* qweight, const int32_t* qzeros, con
  * rewritten in place.
  * moe_wfp8a16_forward / moe_wfp8a16_apply: the layer, as moe_w8a16_forward_ex /
  * moe_w8a16_apply_ex (routing and fused options may be NULL) with the weights
- * above (rows unpadded; w13 and w2 16-byte aligned).  Workspace:
+ * above, w13 [E, 2I, w13_row_stride] and w2 [E, H, w2_row_stride] (row strides
+ * in elements, 0 meaning unpadded; rows a multiple of 512 bytes long read
+ * faster padded by 256 bytes; w13 and w2 16-byte aligned).  Workspace:
  * moe_wfp8a16_workspace_bytes.  Requirements as moe_w8a16_forward.
  * ---------------------------------------------------------------------- */
 int moe_quantize_weights_fp8(const float* w, int64_t E, int64_t N, int64_t K, uint8_t* q, float* scale,
@@ -461,13 +463,15 @@ int moe_fp8_merge_w13_scales(uint8_t* w13, const float* w13_shard_scales, int64_
 size_t moe_wfp8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t block_m,
                                    const moe_fused_opts* opts);
 int moe_wfp8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
-                        const uint8_t* w13, const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                        const uint8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                        const uint8_t* w2, const float* w2_scale, int64_t w2_row_stride,
                         const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* opts,
                         int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 int moe_wfp8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                       const float* router_logits, const moe_routing* routing,
-                      const uint8_t* w13, const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                      const uint8_t* w13, const float* w13_scale, int64_t w13_row_stride,
+                      const uint8_t* w2, const float* w2_scale, int64_t w2_row_stride,
                       const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids, int64_t block_m,
                       void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 

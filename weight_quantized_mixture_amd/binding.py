@@ -63,9 +63,11 @@ SIGNATURES = {
     "moe_fp8_merge_w13_scales": (_c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "moe_wfp8a16_workspace_bytes": (_c_size, [_c_i64] * 6 + [_c_p]),
     "moe_wfp8a16_forward": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64,
-                                     _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+                                     _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p,
+                                     _c_size, _c_p]),
     "moe_wfp8a16_apply": (_c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p,
-                                   _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_size, _c_p]),
+                                   _c_p, _c_p, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_p,
+                                   _c_size, _c_p]),
     "moe_wna16_group_size": (_c_int, [_c_i64, _c_i64, _c_i64, _c_p, _c_p]),
     "moe_w4_import": (_c_int, [_c_int, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "moe_w8a16_workspace_bytes_ex": (_c_size, [_c_i64] * 6 + [_c_p]),
@@ -681,16 +683,16 @@ def _fp8_checked(x, w13, w13_scale, w2, w2_scale, S):
     I = N2 // 2
     if S < 0 or S >= Et:
         raise ValueError(f"num_shared_experts {S} must be in [0, {Et})")
-    _need(w13, torch.uint8, (Et, 2 * I, H), "w13")
+    ld13 = _row_stride(w13, torch.uint8, (Et, 2 * I, H), "w13")
     _need(w13_scale, torch.float32, (Et,), "w13_scale")
-    _need(w2, torch.uint8, (Et, H, I), "w2")
+    ld2 = _row_stride(w2, torch.uint8, (Et, H, I), "w2")
     _need(w2_scale, torch.float32, (Et,), "w2_scale")
-    return T, H, I, Et - S, act
+    return T, H, I, Et - S, act, ld13, ld2
 
 
 def moe_wfp8a16_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, workspace, num_shared_experts=0,
                         apply_router_weight_on_input=False, block_m: int = 0, stream=None):
-    T, H, I, E, act = _fp8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
+    T, H, I, E, act, ld13, ld2 = _fp8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
     k = topk_ids.shape[1]
     _need(topk_w, torch.float32, (T, k), "topk_w")
     _need(topk_ids, torch.int32, (T, k), "topk_ids")
@@ -698,8 +700,8 @@ def moe_wfp8a16_forward(x, w13, w13_scale, w2, w2_scale, topk_w, topk_ids, out, 
     o = fused_opts(num_shared_experts, apply_router_weight_on_input)
     _need_bytes(workspace, moe_wfp8a16_workspace_bytes(T, H, I, E, k, block_m, num_shared_experts,
                                                        apply_router_weight_on_input), "workspace")
-    _check(lib().moe_wfp8a16_forward(_ptr(x), act, T, H, I, E, k, _ptr(w13), _ptr(w13_scale), _ptr(w2),
-                                     _ptr(w2_scale), _ptr(topk_w), _ptr(topk_ids), ctypes.byref(o), block_m, _ptr(out),
+    _check(lib().moe_wfp8a16_forward(_ptr(x), act, T, H, I, E, k, _ptr(w13), _ptr(w13_scale), ld13, _ptr(w2),
+                                     _ptr(w2_scale), ld2, _ptr(topk_w), _ptr(topk_ids), ctypes.byref(o), block_m, _ptr(out),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "moe_wfp8a16_forward")
 
@@ -708,7 +710,7 @@ def moe_wfp8a16_apply(x, router_logits, w13, w13_scale, w2, w2_scale, topk_w, to
                       renormalize=True, scoring="softmax", num_expert_group=0, topk_group=0,
                       e_score_correction_bias=None, routed_scaling_factor=1.0, num_shared_experts=0,
                       apply_router_weight_on_input=False, block_m: int = 0, stream=None):
-    T, H, I, E, act = _fp8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
+    T, H, I, E, act, ld13, ld2 = _fp8_checked(x, w13, w13_scale, w2, w2_scale, num_shared_experts)
     k = topk_ids.shape[1]
     _need(router_logits, torch.float32, (T, E), "router_logits")
     _need(topk_w, torch.float32, (T, k), "topk_w")
@@ -720,7 +722,7 @@ def moe_wfp8a16_apply(x, router_logits, w13, w13_scale, w2, w2_scale, topk_w, to
     _need_bytes(workspace, moe_wfp8a16_workspace_bytes(T, H, I, E, k, block_m, num_shared_experts,
                                                        apply_router_weight_on_input), "workspace")
     _check(lib().moe_wfp8a16_apply(_ptr(x), act, T, H, I, E, k, _ptr(router_logits), ctypes.byref(r), _ptr(w13),
-                                   _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), ctypes.byref(o), _ptr(topk_w),
+                                   _ptr(w13_scale), ld13, _ptr(w2), _ptr(w2_scale), ld2, ctypes.byref(o), _ptr(topk_w),
                                    _ptr(topk_ids), block_m, _ptr(out), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)), "moe_wfp8a16_apply")
 

@@ -1059,10 +1059,15 @@ int moe_w4_import(int format, const int32_t* qweight, const int32_t* qzeros, con
 namespace {
 
 int forward_fp8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
-                const uint8_t* w13, const float* w13_scale, const uint8_t* w2, const float* w2_scale,
-                const float* logits, const moe_routing* routing, float* topk_w_out, int32_t* topk_ids_out,
-                const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* fo, int64_t block_m, void* out,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                const uint8_t* w13, const float* w13_scale, int64_t w13_row_stride, const uint8_t* w2,
+                const float* w2_scale, int64_t w2_row_stride, const float* logits, const moe_routing* routing,
+                float* topk_w_out, int32_t* topk_ids_out, const float* topk_w, const int32_t* topk_ids,
+                const moe_fused_opts* fo, int64_t block_m, void* out, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  const int64_t ld13 = w13_row_stride ? w13_row_stride : H;
+  const int64_t ld2 = w2_row_stride ? w2_row_stride : I;
+  if (ld13 < H || ld13 % 16 || ld2 < I || ld2 % 16)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "row strides must cover the row and be multiples of 16");
   if (T > 0 && (!w13 || !w13_scale || !w2 || !w2_scale || !out)) return fail(MOE_ERR_INVALID_ARGUMENT, "null pointer");
   if (T > 0 && (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(out, 8)))
     return fail(MOE_ERR_INVALID_ARGUMENT, "w13, w2 16-byte and out 8-byte alignment required");
@@ -1072,7 +1077,7 @@ int forward_fp8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, i
   if (st != MOE_OK || F.T == 0) return st;
   moe::Gemm1Args p1{};
   p1.x = F.x; p1.f16 = act_dtype == MOE_FP16; p1.T = F.Tg; p1.H = H; p1.I = I; p1.k = F.kg; p1.Tk = F.Tk;
-  p1.w13 = reinterpret_cast<const int8_t*>(w13); p1.s13 = w13_scale; p1.ldw = H; p1.sorted_ids = F.sorted;
+  p1.w13 = reinterpret_cast<const int8_t*>(w13); p1.s13 = w13_scale; p1.ldw = ld13; p1.sorted_ids = F.sorted;
   p1.block_expert = F.blocks; p1.num_padded = F.npad; p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap;
   p1.a = F.a; p1.fp8 = 1;
   hipError_t e;
@@ -1082,7 +1087,7 @@ int forward_fp8(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, i
   if (e != hipSuccess) return hip_status(e, "gemm1_fp8");
   moe::Gemm2Args p2{};
   p2.a = F.a; p2.H = H; p2.I = I; p2.Tk = F.Tk; p2.w2 = reinterpret_cast<const int8_t*>(w2); p2.s2 = w2_scale;
-  p2.ldw = I; p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
+  p2.ldw = ld2; p2.sorted_ids = F.sorted; p2.block_expert = F.blocks; p2.num_padded = F.npad;
   p2.block_m = static_cast<int>(F.bm); p2.cap = F.cap; p2.splits = static_cast<int>(F.splits); p2.y = F.y; p2.fp8 = 1;
   e = moe::gemm2_planes_fits(H, I, F.bm)       ? moe::launch_gemm2_w8_planes(p2, stream)
       : moe::gemm2_fp8_dma_fits(H, I, F.bm) ? moe::launch_gemm2_fp8_dma(p2, stream)
@@ -1117,21 +1122,24 @@ size_t moe_wfp8a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, i
 }
 
 int moe_wfp8a16_forward(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
-                        const uint8_t* w13, const float* w13_scale, const uint8_t* w2, const float* w2_scale,
-                        const float* topk_w, const int32_t* topk_ids, const moe_fused_opts* opts, int64_t block_m,
-                        void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return forward_fp8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w2, w2_scale, nullptr, nullptr, nullptr, nullptr,
-                     topk_w, topk_ids, opts, block_m, out, workspace, workspace_bytes, stream);
+                        const uint8_t* w13, const float* w13_scale, int64_t w13_row_stride, const uint8_t* w2,
+                        const float* w2_scale, int64_t w2_row_stride, const float* topk_w, const int32_t* topk_ids,
+                        const moe_fused_opts* opts, int64_t block_m, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return forward_fp8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                     nullptr, nullptr, nullptr, nullptr, topk_w, topk_ids, opts, block_m, out, workspace,
+                     workspace_bytes, stream);
 }
 
 int moe_wfp8a16_apply(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
                       const float* router_logits, const moe_routing* routing, const uint8_t* w13,
-                      const float* w13_scale, const uint8_t* w2, const float* w2_scale, const moe_fused_opts* opts,
-                      float* topk_w, int32_t* topk_ids, int64_t block_m, void* out, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      const float* w13_scale, int64_t w13_row_stride, const uint8_t* w2, const float* w2_scale,
+                      int64_t w2_row_stride, const moe_fused_opts* opts, float* topk_w, int32_t* topk_ids,
+                      int64_t block_m, void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (T > 0 && !router_logits) return fail(MOE_ERR_INVALID_ARGUMENT, "null router_logits");
-  return forward_fp8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w2, w2_scale, router_logits, routing, topk_w,
-                     topk_ids, nullptr, nullptr, opts, block_m, out, workspace, workspace_bytes, stream);
+  return forward_fp8(x, act_dtype, T, H, I, E, k, w13, w13_scale, w13_row_stride, w2, w2_scale, w2_row_stride,
+                     router_logits, routing, topk_w, topk_ids, nullptr, nullptr, opts, block_m, out, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -149,18 +149,20 @@ class WFP8A16MoE:
         E, H, I = num_experts, hidden_size, intermediate_size
         self.E, self.H, self.I = E, H, I
         self.params_dtype = params_dtype
-        self.w13_weight = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
-        self.w2_weight = torch.empty(E, H, I, dtype=torch.uint8, device=device)
+        self.w13_weight = padded_rows(E, 2 * I, H, torch.uint8, device)
+        self.w2_weight = padded_rows(E, H, I, torch.uint8, device)
         self.w13_weight_scale = torch.zeros(E, dtype=torch.float32, device=device)
         self.w2_weight_scale = torch.zeros(E, dtype=torch.float32, device=device)
         self._ws = _Workspace()
 
     def load_expert(self, e: int, w13_master: torch.Tensor, w2_master: torch.Tensor):
-        """Quantize one expert's 16/32-bit masters (scaled_fp8_quant: one scale for w13, one for w2)."""
-        B.moe_quantize_weights_fp8(w13_master.reshape(1, 2 * self.I, self.H).float().contiguous(),
-                                   self.w13_weight[e:e + 1], self.w13_weight_scale[e:e + 1])
-        B.moe_quantize_weights_fp8(w2_master.reshape(1, self.H, self.I).float().contiguous(),
-                                   self.w2_weight[e:e + 1], self.w2_weight_scale[e:e + 1])
+        """Quantize one expert's 16/32-bit masters (scaled_fp8_quant: one scale for w13, one for w2),
+        through unpadded codes copied into the (possibly row-padded) weight tensors."""
+        for master, dst, scale, N, K in ((w13_master, self.w13_weight, self.w13_weight_scale, 2 * self.I, self.H),
+                                         (w2_master, self.w2_weight, self.w2_weight_scale, self.H, self.I)):
+            q = torch.empty(1, N, K, dtype=torch.uint8, device=dst.device)
+            B.moe_quantize_weights_fp8(master.reshape(1, N, K).float().contiguous(), q, scale[e:e + 1])
+            dst[e:e + 1].copy_(q)
 
     route = W8A16MoE.route
 
