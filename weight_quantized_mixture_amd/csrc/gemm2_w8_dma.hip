@@ -138,6 +138,17 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_dma_kernel(const Gemm2Args
   }
   constexpr int kLoPlane = 16 * MT * kStep;          // lo plane rows follow the hi rows
 
+  // the epilogue's row ids and column scales, loaded now so that no workgroup
+  // ends with a round trip to memory after its last step
+  int rowf[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rowf[mt][i] = p.sorted_ids[row0 + mt * 16 + kg * 4 + i];
+  float csc[kNT];
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) csc[j] = p.s2[static_cast<int64_t>(e) * H + h0 + 16 * j + col];
+
   f32x4 acc[MT][kNT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -201,12 +212,11 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_dma_kernel(const Gemm2Args
     if (mt < ntiles) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int f = p.sorted_ids[row0 + mt * 16 + kg * 4 + i];
+        const int f = rowf[mt][i];
         if (f < p.Tk) {
           float* yr = p.y + (static_cast<int64_t>(blockIdx.z) * p.Tk + f) * H + h0 + col;
 #pragma unroll
-          for (int j = 0; j < kNT; ++j)
-            yr[16 * j] = acc[mt][j][i] * p.s2[static_cast<int64_t>(e) * H + h0 + 16 * j + col];
+          for (int j = 0; j < kNT; ++j) yr[16 * j] = acc[mt][j][i] * csc[j];
         }
       }
     }
@@ -310,6 +320,15 @@ __global__ __launch_bounds__(kThreads) void gemm2_fp8_dma_kernel(const Gemm2Args
   }
   constexpr int kLoPlane = 16 * MT * R::kARow;
 
+  // the epilogue's row ids, loaded now so that no workgroup ends with a round
+  // trip to memory after its last step
+  int rowf[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rowf[mt][i] = p.sorted_ids[row0 + mt * 16 + kg * 4 + i];
+  const float sw = p.s2[e];
+
   f32x4 acc[MT][kNT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -359,13 +378,12 @@ __global__ __launch_bounds__(kThreads) void gemm2_fp8_dma_kernel(const Gemm2Args
     run(std::integral_constant<int, 1>{});
   }
 
-  const float sw = p.s2[e];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt < ntiles) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int f = p.sorted_ids[row0 + mt * 16 + kg * 4 + i];
+        const int f = rowf[mt][i];
         if (f < p.Tk) {
           float* yr = p.y + (static_cast<int64_t>(blockIdx.z) * p.Tk + f) * H + h0 + col;
 #pragma unroll

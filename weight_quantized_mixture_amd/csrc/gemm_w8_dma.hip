@@ -117,6 +117,19 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) aoff[i] = kWStage + col * R::kARow + 16 * ((2 * kg + 8 * (i >> 1) + (i & 1)) ^ swz_c(col));
 
+  // what the epilogue reads besides the sums (the column's two scales, which
+  // of the lane's rows hold a token) is loaded now, so that no workgroup ends
+  // with a round trip to memory after its last step
+  const int64_t n = n0 + col;
+  const float sg = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + n];
+  const float su = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
+  uint32_t rvalid = 0;                               // bit 4 mt + i: row 16 mt + 4 kg + i holds a token
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (p.sorted_ids[row0 + mt * 16 + kg * 4 + i] < Tk) rvalid |= 1u << (4 * mt + i);
+
   f32x4 accg[MT], accu[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -159,17 +172,13 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p, 
     run(std::integral_constant<int, 1>{});
   }
 
-  const int64_t n = n0 + col;
-  const float sg = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + n];
-  const float su = FP8 ? p.s13[e] : p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
   float v[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = row0 + mt * 16 + kg * 4 + i;
-      v[mt][i] = mt < ntiles && p.sorted_ids[r] < Tk ? silu_mul(accg[mt][i] * sg, accu[mt][i] * su) : 0.0f;
-    }
+    for (int i = 0; i < 4; ++i)
+      v[mt][i] = mt < ntiles && ((rvalid >> (4 * mt + i)) & 1u) ? silu_mul(accg[mt][i] * sg, accu[mt][i] * su)
+                                                                 : 0.0f;
   if (qhi) {
     // row maxima over the wave's 16 columns (the 16 lanes of one kg), then over the 4 waves
     constexpr int kQMax = 32639;                 // 256 * 127 + 127
