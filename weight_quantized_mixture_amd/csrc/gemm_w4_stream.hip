@@ -203,6 +203,12 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
       }
   };
 
+  // GEMM2's row ids (to LDS, read after the steps' barriers), loaded now so
+  // that no workgroup ends with a round trip to memory after its last step
+  __shared__ int rowf[ROLE == 2 ? ROWS : 1];
+  if constexpr (ROLE == 2) {
+    if (tid < ROWS) rowf[tid] = sorted_ids[row0 + tid];
+  }
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
       if (mt < ntiles) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int f = sorted_ids[row0 + mt * 16 + kg * 4 + i];
+          const int f = rowf[mt * 16 + kg * 4 + i];
           if (f < Tk) {
             float* yr = p2.y + (static_cast<int64_t>(blockIdx.z) * Tk + f) * H;
 #pragma unroll
@@ -428,6 +434,14 @@ __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Arg
   const int pg0 = static_cast<int>(((e * N + n0 + col) * G) & 1);
   const int pu0 = static_cast<int>(((e * N + I + n0 + col) * G) & 1);
 
+  // which of the lane's rows hold a token, read now so that no workgroup ends
+  // with a round trip to memory after its last step
+  uint32_t rvalid = 0;                               // bit 4 mt + i: row 16 mt + 4 kg + i
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (p.sorted_ids[row0 + mt * 16 + kg * 4 + i] < Tk) rvalid |= 1u << (4 * mt + i);
   f32x4 accg[MT], accu[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -498,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Arg
       for (int i = 0; i < 4; ++i) {
         const int64_t r = row0 + mt * 16 + kg * 4 + i;
         uint16_t hi, lo;
-        split16(p.sorted_ids[r] < Tk ? silu_mul(accg[mt][i], accu[mt][i]) : 0.0f, F16, hi, lo);
+        split16(((rvalid >> (4 * mt + i)) & 1u) ? silu_mul(accg[mt][i], accu[mt][i]) : 0.0f, F16, hi, lo);
         a_hi[r * I + n] = hi;
         a_lo[r * I + n] = lo;
       }

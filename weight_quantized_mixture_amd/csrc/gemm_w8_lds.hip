@@ -85,6 +85,15 @@ __global__ __launch_bounds__(kThreads) void gemm1_lds_kernel(const Gemm1Args p) 
       if (cvalid[c]) *reinterpret_cast<u32x4*>(&As[buf][dsto[c]]) = regs[c];
   };
 
+  // the epilogue's column scales, loaded now so that no workgroup ends with a
+  // round trip to memory after its last step
+  float sgv[NG], suv[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    sgv[g] = p.s13[static_cast<int64_t>(e) * 2 * I + n0 + 16 * g + col];
+    suv[g] = p.s13[static_cast<int64_t>(e) * 2 * I + I + n0 + 16 * g + col];
+  }
+
   f32x4 accg[MT][NG], accu[MT][NG];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -178,8 +187,7 @@ __global__ __launch_bounds__(kThreads) void gemm1_lds_kernel(const Gemm1Args p) 
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const int64_t n = n0 + 16 * g + col;
-    const float sg = p.s13[static_cast<int64_t>(e) * 2 * I + n];
-    const float su = p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
+    const float sg = sgv[g], su = suv[g];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (mt < ntiles) {

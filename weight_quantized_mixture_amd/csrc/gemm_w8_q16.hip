@@ -193,6 +193,15 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
     }
   };
 
+  // the epilogue's row ids (to LDS, read after the loop's barriers) and
+  // column scales, loaded now so that no workgroup ends with a round trip to
+  // memory after its last step
+  __shared__ int rowf[ROWS];
+  if (tid < ROWS) rowf[tid] = p.sorted_ids[row0 + tid];
+  float csc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) csc[j] = p.s2[static_cast<int64_t>(e) * H + h0 + 16 * j + col];
+
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -273,12 +282,11 @@ __global__ __launch_bounds__(kThreads) void gemm2_q16_kernel(const Gemm2Args p, 
     if (mt < ntiles) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int f = p.sorted_ids[row0 + mt * 16 + kg * 4 + i];
+        const int f = rowf[mt * 16 + kg * 4 + i];
         if (f < p.Tk) {
           float* yr = p.y + (static_cast<int64_t>(blockIdx.z) * p.Tk + f) * H + h0 + col;
 #pragma unroll
-          for (int j = 0; j < NT; ++j)
-            yr[16 * j] = acc[mt][j][i] * p.s2[static_cast<int64_t>(e) * H + h0 + 16 * j + col];
+          for (int j = 0; j < NT; ++j) yr[16 * j] = acc[mt][j][i] * csc[j];
         }
       }
     }

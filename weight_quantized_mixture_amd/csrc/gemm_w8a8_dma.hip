@@ -146,6 +146,23 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a8_dma_kernel(const Gemm1Arg
     aoff[mt][1] = kWStage + r * kStep + 16 * ((4 + kg) ^ swz_a(r));
   }
 
+  // the epilogue's inputs besides the sums (the column's two scales, the
+  // rows' token ids and activation scales), loaded now so that no workgroup
+  // ends with a chain of memory round trips after its last step
+  const int64_t n = n0 + col;
+  const float sg = p.s13[static_cast<int64_t>(e) * 2 * I + n];
+  const float su = p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
+  int rowf[MT][4];
+  float rows_sx[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = mt < ntiles ? p.sorted_ids[row0 + mt * 16 + kg * 4 + i] : static_cast<int>(Tk);
+      rowf[mt][i] = f;
+      rows_sx[mt][i] = f < Tk ? sx[f / p.k] : 0.0f;
+    }
+
   i32x4 accg[MT], accu[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -177,19 +194,16 @@ __global__ __launch_bounds__(kThreads) void gemm1_w8a8_dma_kernel(const Gemm1Arg
     run(std::integral_constant<int, 1>{});
   }
 
-  const int64_t n = n0 + col;
-  const float sg = p.s13[static_cast<int64_t>(e) * 2 * I + n];
-  const float su = p.s13[static_cast<int64_t>(e) * 2 * I + I + n];
   float m[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t r = row0 + mt * 16 + kg * 4 + i;
-      const int f = mt < ntiles ? p.sorted_ids[r] : static_cast<int>(Tk);
+      const int f = rowf[mt][i];
       float v = 0.0f;
       if (f < Tk) {
-        const float st = sx[f / p.k];
+        const float st = rows_sx[mt][i];
         v = silu_mul(static_cast<float>(accg[mt][i]) * st * sg, static_cast<float>(accu[mt][i]) * st * su);
         p.a[r * I + n] = v;
       }
@@ -285,6 +299,22 @@ __global__ __launch_bounds__(kThreads) void gemm2_w8a8_dma_kernel(const Gemm2Arg
     aoff[mt][1] = kWStage + r * kStep + 16 * ((4 + kg) ^ swz_a(r));
   }
 
+  // the epilogue's column scales, row ids and row scales, loaded now so that no
+  // workgroup ends with a chain of memory round trips after its last step
+  const float s0 = p.s2[static_cast<int64_t>(e) * H + h0 + col];
+  const float s1 = p.s2[static_cast<int64_t>(e) * H + h0 + 16 + col];
+  int rowf[MT][4];
+  float rows_sa[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = row0 + mt * 16 + kg * 4 + i;
+      const int f = p.sorted_ids[r];
+      rowf[mt][i] = f;
+      rows_sa[mt][i] = f < p.Tk ? sa[r] : 0.0f;
+    }
+
   i32x4 acc0[MT], acc1[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -316,17 +346,14 @@ __global__ __launch_bounds__(kThreads) void gemm2_w8a8_dma_kernel(const Gemm2Arg
     run(std::integral_constant<int, 1>{});
   }
 
-  const float s0 = p.s2[static_cast<int64_t>(e) * H + h0 + col];
-  const float s1 = p.s2[static_cast<int64_t>(e) * H + h0 + 16 + col];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (mt < ntiles) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t r = row0 + mt * 16 + kg * 4 + i;
-        const int f = p.sorted_ids[r];
+        const int f = rowf[mt][i];
         if (f < p.Tk) {
-          const float sr = sa[r];
+          const float sr = rows_sa[mt][i];
           float* yr = p.y + (static_cast<int64_t>(blockIdx.z) * p.Tk + f) * H + h0 + col;
           yr[0] = static_cast<float>(acc0[mt][i]) * sr * s0;
           yr[16] = static_cast<float>(acc1[mt][i]) * sr * s1;
