@@ -202,6 +202,11 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p, 
     }
     __syncthreads();
     const int64_t G = I / 64;
+    // the codes go through an LDS tile [hi, lo][16 MT rows][64 columns] (ring
+    // memory past slot 0, free by now) and out in 16-byte pieces, 64
+    // contiguous bytes per row and plane: single-byte stores from every lane
+    // cost more than the arithmetic of the whole epilogue
+    int8_t* qt = reinterpret_cast<int8_t*>(smem + R::kStage);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       if (mt < ntiles) {
@@ -213,11 +218,20 @@ __global__ __launch_bounds__(kThreads) void gemm1_dma_kernel(const Gemm1Args p, 
           int q = static_cast<int>(__builtin_rintf(v[mt][i] * inv));
           q = q < -kQMax ? -kQMax : (q > kQMax ? kQMax : q);
           const int h = (q + 128) >> 8;
-          const int64_t r = row0 + rl;
-          qhi[r * I + n] = static_cast<int8_t>(h);
-          qlo[r * I + n] = static_cast<int8_t>(q - 256 * h);
-          if (wave == 0 && col == 0) qscale[r * G + blockIdx.x] = gm / static_cast<float>(kQMax);
+          qt[rl * 64 + wave * 16 + col] = static_cast<int8_t>(h);
+          qt[(16 * MT + rl) * 64 + wave * 16 + col] = static_cast<int8_t>(q - 256 * h);
+          if (wave == 0 && col == 0) qscale[(row0 + rl) * G + blockIdx.x] = gm / static_cast<float>(kQMax);
         }
+      }
+    }
+    __syncthreads();
+    {
+      constexpr int kChunks = 2 * 16 * MT * 4;     // (plane, row, 16-byte piece)
+      const int pl = tid / (16 * MT * 4), rl = (tid / 4) % (16 * MT), c = tid % 4;
+      if (tid < kChunks && rl < 16 * ntiles) {
+        const u32x4 q16 = *reinterpret_cast<const u32x4*>(qt + (pl * 16 * MT + rl) * 64 + c * 16);
+        *reinterpret_cast<u32x4*>((pl ? qlo : qhi) + (row0 + rl) * I + static_cast<int64_t>(blockIdx.x) * 64 + c * 16) =
+            q16;
       }
     }
     return;
