@@ -338,13 +338,16 @@ def test_gemm2_blocks_of_256_splits(splits):
 
 # (T, k, splits, H, act): every register shape of the few-token combine
 # (k <= 2 with 1, 2, 3-4 and 5-16 parts; k <= 8 with 1, 2, 3-4 parts), k = 1,
-# and the general kernel (k = 3 with 5 parts; more than 256 workgroups with
-# one part and with 12 parts)
+# the slots-over-waves kernel for more partials (k = 3 with 5 parts, k = 6 with
+# 8 as fine-grained decode at one token, k = 16 with 16 at its limits, 96
+# groups per token so that a workgroup straddles two tokens), and the general
+# kernel (k = 17; 17 parts; more than 256 workgroups with one part and with 12)
 @pytest.mark.parametrize("T,k,splits,H,act", [
     (1, 2, 1, 4096, "bf16"), (3, 2, 2, 4096, "bf16"), (1, 2, 3, 4096, "fp16"), (1, 2, 16, 4096, "bf16"),
     (5, 2, 9, 512, "bf16"), (1, 1, 16, 512, "fp16"), (2, 6, 1, 2048, "bf16"), (4, 8, 2, 2048, "fp16"),
-    (3, 6, 4, 2048, "bf16"), (2, 3, 5, 512, "bf16"), (40, 2, 12, 4096, "bf16"), (300, 2, 1, 4096, "bf16"),
-    (70, 2, 12, 4096, "fp16")])
+    (3, 6, 4, 2048, "bf16"), (2, 3, 5, 512, "bf16"), (1, 6, 8, 2048, "bf16"), (1, 16, 16, 1024, "fp16"),
+    (3, 12, 9, 384, "bf16"), (2, 17, 2, 512, "bf16"), (2, 4, 17, 256, "fp16"), (40, 2, 12, 4096, "bf16"),
+    (300, 2, 1, 4096, "bf16"), (70, 2, 12, 4096, "fp16")])
 def test_combine_topk(T, k, splits, H, act):
     log(f"[combine] T={T} k={k} splits={splits} H={H} act={act}")
     E = 8

@@ -121,6 +121,82 @@ __global__ __launch_bounds__(256) void combine_few_kernel(const float* __restric
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + t * H + h) = packed;
 }
 
+// Few tokens with more (slot, split) partials than combine_few_kernel holds
+// in registers (k <= 16 slots, splits <= SMAX): a workgroup covers 64
+// consecutive 4-element groups, wave w sums the split partials of slots w,
+// w+4, ... (all loads of a slot in flight together, added in ascending s)
+// into LDS, and wave 0 adds the weighted slots in ascending j.  Same sums, in
+// the same order, as combine_kernel; each slot's partials cost one memory
+// round trip instead of one per split.
+constexpr int kWideMaxK = 16;
+
+template <bool F16, int SMAX>
+__global__ __launch_bounds__(256) void combine_wide_kernel(const float* __restrict__ y, int splits,
+                                                           int64_t T, int k, int64_t H, int E,
+                                                           const float* __restrict__ topk_w,
+                                                           const int32_t* __restrict__ topk_ids,
+                                                           void* __restrict__ out) {
+  __shared__ float4 part[kWideMaxK][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t H4 = H / 4;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kWave + lane;
+  const bool live = g < T * H4;
+  const int64_t t = live ? g / H4 : 0;
+  const int64_t h = live ? (g % H4) * 4 : 0;
+  const int64_t Tk = T * k;
+  // ids and weights of every slot requested before the partials (wave 0
+  // uses them after the barrier); slots past k re-read slot 0
+  int eid[kWideMaxK];
+  float wk[kWideMaxK];
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < kWideMaxK; ++j) {
+      const int64_t f = t * k + (j < k ? j : 0);
+      eid[j] = topk_ids[f];
+      wk[j] = topk_w[f];
+    }
+  }
+  // a workgroup's 64 groups may straddle two tokens: slot data per lane
+  for (int j = wave; j < k; j += 4) {
+    const int64_t f = t * k + j;
+    float4 v[SMAX];
+#pragma unroll
+    for (int sp = 0; sp < SMAX; ++sp) {
+      const int64_t sl = sp < splits ? sp : 0;
+      v[sp] = *reinterpret_cast<const float4*>(y + (sl * Tk + f) * H + h);
+    }
+    float4 ys = v[0];
+#pragma unroll
+    for (int sp = 1; sp < SMAX; ++sp) {
+      if (sp < splits) {
+        ys.x += v[sp].x; ys.y += v[sp].y; ys.z += v[sp].z; ys.w += v[sp].w;
+      }
+    }
+    part[j][lane] = ys;
+  }
+  __syncthreads();
+  if (wave != 0 || !live) return;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kWideMaxK; ++j) {
+    if (j < k && eid[j] >= 0 && eid[j] < E) {
+      const float wj = wk[j];
+      const float4 ys = part[j][lane];
+      acc.x += wj * ys.x; acc.y += wj * ys.y; acc.z += wj * ys.z; acc.w += wj * ys.w;
+    }
+  }
+  uint2 packed;
+  if constexpr (F16) {
+    packed.x = static_cast<uint32_t>(f32_to_f16(acc.x)) | (static_cast<uint32_t>(f32_to_f16(acc.y)) << 16);
+    packed.y = static_cast<uint32_t>(f32_to_f16(acc.z)) | (static_cast<uint32_t>(f32_to_f16(acc.w)) << 16);
+  } else {
+    packed.x = pack_bf16_rne(acc.x, acc.y);
+    packed.y = pack_bf16_rne(acc.z, acc.w);
+  }
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + t * H + h) = packed;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t H, int E,
@@ -148,6 +224,23 @@ hipError_t launch_combine(const float* y, int splits, int64_t T, int k, int64_t 
     FEW(8, 2)
     FEW(8, 4)
 #undef FEW
+    // more partials per slot: the slots spread over the waves
+    if (k <= kWideMaxK && splits <= 16) {
+      const unsigned wblocks = static_cast<unsigned>((n + kWave - 1) / kWave);
+#define WIDE(SM)                                                                                            \
+  if (splits <= SM) {                                                                                      \
+    if (f16)                                                                                                \
+      hipLaunchKernelGGL((combine_wide_kernel<true, SM>), dim3(wblocks), dim3(256), 0, stream, y, splits, T, k, \
+                         H, E, topk_w, topk_ids, out);                                                      \
+    else                                                                                                    \
+      hipLaunchKernelGGL((combine_wide_kernel<false, SM>), dim3(wblocks), dim3(256), 0, stream, y, splits, T, \
+                         k, H, E, topk_w, topk_ids, out);                                                   \
+    return hipGetLastError();                                                                               \
+  }
+      WIDE(8)
+      WIDE(16)
+#undef WIDE
+    }
   }
 #define COMBINE(F, B)                                                                                    \
   hipLaunchKernelGGL((combine_kernel<F, B>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y, splits, \
