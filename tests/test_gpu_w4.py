@@ -82,11 +82,15 @@ def test_w4_apply_from_logits():
 
 @pytest.mark.parametrize("act,bm,T,H,I,g", [("fp16", 32, 45, 256, 384, 128), ("bf16", 32, 45, 256, 384, 128),
                                             ("bf16", 16, 7, 384, 256, 128), ("fp16", 16, 30, 384, 384, 128),
-                                            ("fp16", 32, 61, 512, 512, 256), ("bf16", 16, 1, 512, 512, 256)])
+                                            ("fp16", 32, 61, 512, 512, 256), ("bf16", 16, 1, 512, 512, 256),
+                                            ("fp16", 16, 5, 2560, 256, 128), ("bf16", 32, 40, 4096, 256, 128),
+                                            ("fp16", 16, 3, 4224, 256, 128)])
 def test_w4_blocks_of_16_and_32(act, bm, T, H, I, g):
-    # GEMM1 of 16/32-row blocks streams packed rows, scales and zero words
-    # through the LDS ring: odd group counts per row (H / g = 3) make the
-    # parity of each row's scale element differ, and g = 256 spans two K steps
+    # GEMM1 of 16/32-row blocks copies each wave's scales and zero words of
+    # the whole K into LDS once and streams the packed rows through the ring:
+    # odd group counts per row (H / g = 3) put the scale spans at odd element
+    # offsets, g = 256 spans two K steps, 20 and 32 groups per row take the
+    # larger scale area, and 33 groups the streaming kernel instead
     E, k = 8, 3
     log(f"[w4 dma] act={act} bm={bm} T={T} H={H} I={I} g={g}")
     fn = lambda which, e: synthetic.random_master((2 * I, H) if which == "w13" else (H, I),  # noqa: E731

@@ -944,8 +944,9 @@ int forward_w4(const void* x, int act_dtype, int64_t T, int64_t H, int64_t I, in
   p1.qw = w13_qweight; p1.sc = w13_scales; p1.qz = w13_qzeros; p1.group = static_cast<int>(group_size);
   p1.sorted_ids = F.sorted; p1.block_expert = F.blocks; p1.num_padded = F.npad;
   p1.block_m = static_cast<int>(F.bm); p1.cap = F.cap; p1.a = F.a;
-  // blocks of 16 or 32 rows: the DMA-fed ring (it copies the fp16 scales as dwords)
-  const bool w4_dma = (F.bm == 16 || F.bm == 32) && aligned(w13_scales, 4);
+  // blocks of 16 or 32 rows: the DMA-fed ring (it copies the fp16 scales as
+  // dwords, at most 32 scale groups per row)
+  const bool w4_dma = (F.bm == 16 || F.bm == 32) && aligned(w13_scales, 4) && H / group_size <= 32;
   hipError_t e = w4_dma ? moe::launch_gemm1_w4_dma(p1, stream)
                         : (w4_stream(F.bm) ? moe::launch_gemm1_w4_stream(p1, stream) : moe::launch_gemm1_w4(p1, stream));
   if (e != hipSuccess) return hip_status(e, "gemm1_w4");

@@ -334,33 +334,44 @@ __global__ __launch_bounds__(kThreads) void gemm_w4_stream_kernel(const Gemm1W4A
 // GEMM1 for blocks of 16 or 32 rows fed by direct global -> LDS copies (the
 // ring of the int8 decode GEMM1, with packed uint4 rows).  A workgroup is one
 // align block and 64 output columns; each wave owns 16 gate rows and the
-// matching 16 up rows.  Per 128-K step (one scale group or part of one) every
-// wave copies its 32 packed rows (64 bytes each, 2 KB) and one dword per
-// lane: lanes 0-31 the dword holding their row's fp16 group scale, lanes
-// 32-35 the zero words of the wave's rows (gate n0, n0+8, up I+n0, I+n0+8),
-// the other lanes repeat lane 32's; the workgroup copies the block's
-// activation rows (256 bytes each; rows without a token read token 0's row
-// and their results are replaced by 0).  A 4-deep ring keeps steps s+1..s+3
-// in flight while step s is decoded and multiplied; one barrier per step,
-// after each thread has waited for its own copies of that step.  Lane
-// (col, kg) takes K [32 kg, 32 kg + 32) of its gate and up rows, 8 codes per
-// MFMA, the activation operand read for the same K positions (permuted to
-// the fp16 decode's slot order 0,4,1,5,2,6,3,7 after the LDS read).
+// matching 16 up rows.  Once, before the ring starts, every wave copies as
+// dwords its rows' fp16 scales and zero words of every group of the whole K
+// (the 16 gate rows' scales are one contiguous span, the up rows' another,
+// then 2 rows of zero words each: 20 G dwords per wave, G <= MAXG groups).
+// Per 128-K step (one scale group or part of one) every wave copies its 32
+// packed rows (64 bytes each, 2 KB) and the workgroup the block's activation
+// rows (256 bytes each; rows without a token read token 0's row and their
+// results are replaced by 0).  A 4-deep ring keeps steps s+1..s+3 in flight
+// while step s is decoded and multiplied; one barrier per step, after each
+// thread has waited for its own copies of that step, and the refill of step
+// s-1's slot right after it.  Lane (col, kg) takes K [32 kg, 32 kg + 32) of
+// its gate and up rows, 8 codes per MFMA, the activation operand read for the
+// same K positions (permuted to the fp16 decode's slot order 0,4,1,5,2,6,3,7
+// after the LDS read).
+//
+// The scale area is the tail of the ring's own LDS array: LDS reads from an
+// array of its own, while copies into LDS are in flight, make the compiler
+// wait for all copies before them (the ring drained every step, measured
+// 9-15 us slower at W4A16 T=8..64).  With MAXG = 16 (H = 2048 at groups of
+// 128) the 16-row kernel takes 53 KB and three workgroups fit a CU.
 constexpr int kW4Ring = 4;
 constexpr int kW4WWave = 32 * (kStep / 2);             // 2 KB of packed codes per wave and step
 constexpr int kW4WStage = 4 * kW4WWave;
-constexpr int kW4SZWave = kWave * 4;                   // one dword per lane
-constexpr int kW4SZStage = 4 * kW4SZWave;
 constexpr int kW4WDma = kW4WWave / (kWave * 16);       // 2 copies per lane and step
+constexpr int kW4MaxG = 32;                            // most groups per row of any instantiation
+template <int MAXG>
+constexpr int w4_sz_wave() { return (20 * MAXG + kWave - 1) / kWave * kWave * 4; }   // bytes per wave
 
-template <int MT, bool F16>
+template <int MT, bool F16, int MAXG>
 __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Args p) {
   constexpr int kARow = kStep * 2;                     // bytes per activation row and step
   constexpr int kAStage = 16 * MT * kARow;
   constexpr int kADma = kAStage / (kThreads * 16);     // = MT
-  constexpr int kStage = kW4WStage + kW4SZStage + kAStage;
-  constexpr int kPer = kW4WDma + 1 + kADma;            // copies per thread and step
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kW4Ring * kStage];
+  constexpr int kStage = kW4WStage + kAStage;
+  constexpr int kPer = kW4WDma + kADma;                // copies per thread and step
+  constexpr int kSZWave = w4_sz_wave<MAXG>();
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kW4Ring * kStage + 4 * kSZWave];
+  uint8_t* const szs = smem + kW4Ring * kStage;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -389,13 +400,12 @@ __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Arg
     const int c = (lane & 3) ^ swz_b(r);
     wsrc[i] = qwb + (e * N + wrow(r)) * (H / 2) + c * 16;
   }
-  // scale / zero dword of this lane: element (row, group) of the fp16 scales
-  // is at srow + group; zero word (rows/8, group) at zrow + group
-  const uint8_t* scb = reinterpret_cast<const uint8_t*>(p.sc);
-  const int64_t srow = (e * N + wrow(lane < 32 ? lane : 0)) * G;
-  const int zl = lane >= 32 && lane < 36 ? lane - 32 : 0;
-  const int64_t zn = zl < 2 ? n0 + 8 * zl : I + n0 + 8 * (zl - 2);
-  const int32_t* zsrc = p.qz + (e * (N / 8) + zn / 8) * G;
+  // the wave's scale / zero area, dword d: [0, 8G) the gate rows' scales
+  // (row-major [16][G] fp16), [8G, 16G) the up rows', [16G, 18G) the gate
+  // zero words ([2][G]: rows n0..n0+7, n0+8..n0+15), [18G, 20G) the up ones;
+  // dwords past 20 G repeat dword 0 into the area's tail
+  uint8_t* sza = szs + wave * kSZWave;
+
   // activation copies: row r = 4 (wave MT + q) + lane/16, slot lane%16 holds
   // chunk (lane%16) ^ swz_c(r)
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
@@ -413,14 +423,9 @@ __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Arg
 #pragma unroll
     for (int i = 0; i < kW4WDma; ++i)
       dma16(wsrc[i] + static_cast<int64_t>(s) * (kStep / 2), base + wave * kW4WWave + i * 1024);
-    const int64_t grp = static_cast<int64_t>(s) * kStep / p.group;
-    const void* szp = lane < 32 ? static_cast<const void*>(scb + ((srow + grp) & ~int64_t{1}) * 2)
-                                : static_cast<const void*>(zsrc + grp);
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)const_cast<void*>(szp),
-                                     (lds_ptr_t)(base + kW4WStage + wave * kW4SZWave), 4, 0, 0);
 #pragma unroll
     for (int q = 0; q < kADma; ++q)
-      dma16(asrc[q] + static_cast<int64_t>(s) * kStep, base + kW4WStage + kW4SZStage + (wave * kADma + q) * 1024);
+      dma16(asrc[q] + static_cast<int64_t>(s) * kStep, base + kW4WStage + (wave * kADma + q) * 1024);
   };
 
   // LDS offsets this lane reads
@@ -428,11 +433,11 @@ __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Arg
   const int wou = wave * kW4WWave + (16 + col) * (kStep / 2) + 16 * (kg ^ swz_b(16 + col));
   int aoff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) aoff[i] = kW4WStage + kW4SZStage + col * kARow + 16 * ((4 * kg + i) ^ swz_c(col));
-  // parity of the scale element of group 0 for the gate and up row (the
-  // copied dword holds the even element and the next one)
-  const int pg0 = static_cast<int>(((e * N + n0 + col) * G) & 1);
-  const int pu0 = static_cast<int>(((e * N + I + n0 + col) * G) & 1);
+  for (int i = 0; i < 4; ++i) aoff[i] = kW4WStage + col * kARow + 16 * ((4 * kg + i) ^ swz_c(col));
+  const uint16_t* sgl = reinterpret_cast<const uint16_t*>(sza) + col * G;
+  const uint16_t* sul = reinterpret_cast<const uint16_t*>(sza) + (16 + col) * G;
+  const uint32_t* zgl = reinterpret_cast<const uint32_t*>(sza) + 16 * G + (col >> 3) * G;
+  const uint32_t* zul = reinterpret_cast<const uint32_t*>(sza) + 18 * G + (col >> 3) * G;
 
   // which of the lane's rows hold a token, read now so that no workgroup ends
   // with a round trip to memory after its last step
@@ -442,7 +447,25 @@ __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Arg
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (p.sorted_ids[row0 + mt * 16 + kg * 4 + i] < Tk) rvalid |= 1u << (4 * mt + i);
-  f32x4 accg[MT], accu[MT];
+  // the scale area's copies go out after the reads of sorted_ids above are
+  // consumed, so their waits do not wait for these copies as well
+  {
+    const uint32_t* scg = reinterpret_cast<const uint32_t*>(p.sc + (e * N + n0) * G);
+    const uint32_t* scu = reinterpret_cast<const uint32_t*>(p.sc + (e * N + I + n0) * G);
+    const int32_t* zg = p.qz + (e * (N / 8) + n0 / 8) * G;
+    const int32_t* zu = p.qz + (e * (N / 8) + (I + n0) / 8) * G;
+    const int64_t g8 = 8 * G;
+    for (int j = 0; j * kWave < 20 * G; ++j) {
+      const int64_t d = j * kWave + lane;
+      const void* src = d < g8             ? static_cast<const void*>(scg + d)
+                        : d < 2 * g8       ? static_cast<const void*>(scu + (d - g8))
+                        : d < 2 * g8 + 2 * G ? static_cast<const void*>(zg + (d - 2 * g8))
+                        : d < 20 * G       ? static_cast<const void*>(zu + (d - 2 * g8 - 2 * G))
+                                           : static_cast<const void*>(scg);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)const_cast<void*>(src), (lds_ptr_t)(sza + j * kWave * 4), 4, 0,
+                                       0);
+    }
+  }  f32x4 accg[MT], accu[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     accg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -454,22 +477,21 @@ __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Arg
 #pragma unroll
     for (int q = 0; q < kW4Ring - 1; ++q) issue(q < nst ? q : nst - 1, q);
     for (int s = 0; s < nst; ++s) {
-      // this thread's copies of step s landed (s+1, s+2 may still fly); then
-      // the slot of step s-1 takes step s+3 (past the end the last step
-      // again, into a slot nobody reads: a fixed copy count per step)
+      // this thread's copies of step s (and, at step 0, of the scale area:
+      // those were issued first) landed, s+1, s+2 may still fly; then the
+      // slot of step s-1 takes step s+3 (past the end the last step again,
+      // into a slot nobody reads: a fixed copy count per step)
       wait_vmcnt<(kW4Ring - 2) * kPer>();
       stage_barrier();
       issue(s + 3 < nst ? s + 3 : nst - 1, (s + 3) % kW4Ring);
       const uint8_t* st = smem + (s % kW4Ring) * kStage;
       const u32x4 wg = *reinterpret_cast<const u32x4*>(st + wog);
       const u32x4 wu = *reinterpret_cast<const u32x4*>(st + wou);
-      const uint32_t* sz = reinterpret_cast<const uint32_t*>(st + kW4WStage + wave * kW4SZWave);
       const int grp = static_cast<int>(static_cast<int64_t>(s) * kStep / p.group);
-      const uint32_t sgw = sz[col], suw = sz[16 + col];
-      const float sg = f16_to_f32(static_cast<uint16_t>(((pg0 ^ grp) & 1) ? sgw >> 16 : sgw & 0xffffu));
-      const float su = f16_to_f32(static_cast<uint16_t>(((pu0 ^ grp) & 1) ? suw >> 16 : suw & 0xffffu));
-      const uint32_t zg = (sz[32 + (col >> 3)] >> (4 * (col & 7))) & 0xFu;
-      const uint32_t zu = (sz[34 + (col >> 3)] >> (4 * (col & 7))) & 0xFu;
+      const float sg = f16_to_f32(sgl[grp]);
+      const float su = f16_to_f32(sul[grp]);
+      const uint32_t zg = (zgl[grp] >> (4 * (col & 7))) & 0xFu;
+      const uint32_t zu = (zul[grp] >> (4 * (col & 7))) & 0xFu;
       u32x4 bg[4], bu[4];
       bg[0] = w4_op<F16>(wg.x, zg);
       bg[1] = w4_op<F16>(wg.y, zg);
@@ -522,9 +544,11 @@ __global__ __launch_bounds__(kThreads) void gemm1_w4_dma_kernel(const Gemm1W4Arg
 
 template <int MT, bool F16>
 hipError_t w4d_launch1(const Gemm1W4Args& p, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm1_w4_dma_kernel<MT, F16>),
-                     dim3(static_cast<unsigned>(p.I / 64), static_cast<unsigned>(p.cap / p.block_m)),
-                     dim3(kThreads), 0, stream, p);
+  const dim3 grid(static_cast<unsigned>(p.I / 64), static_cast<unsigned>(p.cap / p.block_m));
+  if (p.H / p.group <= 16)
+    hipLaunchKernelGGL((gemm1_w4_dma_kernel<MT, F16, 16>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm1_w4_dma_kernel<MT, F16, kW4MaxG>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -562,6 +586,7 @@ hipError_t launch_gemm1_w4_stream(const Gemm1W4Args& p, hipStream_t stream) {
 }
 
 hipError_t launch_gemm1_w4_dma(const Gemm1W4Args& p, hipStream_t stream) {
+  if (p.H / p.group > kW4MaxG) return hipErrorInvalidValue;
   if (p.block_m == 32) return p.f16 ? w4d_launch1<2, true>(p, stream) : w4d_launch1<2, false>(p, stream);
   return p.f16 ? w4d_launch1<1, true>(p, stream) : w4d_launch1<1, false>(p, stream);
 }
