@@ -205,7 +205,11 @@ __global__ __launch_bounds__(k1Threads) void gemm1_big_kernel(const Gemm1Args p,
     // row tiles 2 VALU per MFMA beats 1 or 3; partly filled blocks one less
     // than their conversions need per MFMA)
     auto interleave = []() {
-      constexpr int kConv = FP8 ? 4 : 12;   // VALU per conversion of 8 codes
+      // VALU per conversion of 8 codes, as the schedule counts them (e4m3
+      // takes about 4; counting 8 keeps the fp8 loop free of register spills,
+      // whose reloads would wait for every copy in flight each stage: 4 spilt
+      // 10 registers, and the fp8 prefill ran 8% slower)
+      constexpr int kConv = FP8 ? 8 : 12;
       constexpr int per = (kConv * ((8 + MT1 - 1) / MT1) + 7) / 8 - (MT1 < 8 && !FP8 ? 1 : 0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
